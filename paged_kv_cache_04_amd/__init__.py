@@ -1,0 +1,6 @@
+"""paged_kv_cache_04_amd: attention over a paged KV cache on MI355X (gfx950).
+
+The compute lives in libpkv.so (hand-written HIP kernels behind a C ABI,
+declared in include/pkv.h).  This package holds the thin Python binding over
+that library, the seeded workload generators and the work/byte accounting.
+"""
