@@ -1,0 +1,217 @@
+/*
+ * pkv.h -- C ABI of libpkv: attention over a paged KV cache on MI355X (gfx950).
+ *
+ * The operation (page 2, "FlashAttention + PageAttention joint tuning",
+ * section 2.1): out = softmax(Q K^T * scale) V for every query row, reduced
+ * tile by tile with an online softmax (same page, section 2.2).  K and V live
+ * in fixed-size physical pages; each sequence reaches its pages through a
+ * block table whose entry i holds the physical page of logical tokens
+ * [i*P, (i+1)*P) (page 2, section 3.2; page 3, section 3.2: the page of token
+ * t is table[t / P]).  Query heads share KV heads in contiguous groups of
+ * G = H_q / H_kv (page 4, section 2.2, GQA): query head h reads KV head h / G.
+ *
+ * Data layout, shared by every call (one layer per call):
+ *   k_cache, v_cache : [num_pages][H_kv][P][D] of desc->dtype, separate buffers.
+ *                      One (page, head) block is P*D contiguous elements.
+ *   block_table      : int32 [batch][block_table_stride], device memory.
+ *   context_lens     : int32 [batch], device memory.
+ *   slot             : page * P + offset (int32).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named "device" are HIP device pointers; "host" ones are CPU
+ *     memory.  The caller owns every buffer.  The library allocates no device
+ *     memory, keeps no pointer after returning, and never synchronises.
+ *   - stream: a hipStream_t passed as void*; NULL is the null stream.  All
+ *     device work is enqueued on it asynchronously.
+ *   - Base pointers of device buffers must be 16-byte aligned.
+ *   - Return value: PKV_OK (0) or a negative pkv_status.  Argument checks run
+ *     on the host before any HIP call; on error nothing is enqueued and
+ *     pkv_last_error() gives a message (per calling thread).
+ *   - Supported shapes: page_size 16; head_dim 64 or 128; dtype f32, f16,
+ *     bf16; H_q a multiple of H_kv with G in {1, 2, 4, 8}; the prefill call
+ *     needs f16 or bf16 and head_dim 128.
+ *   - Contents of device tables (page ids, lengths, slots) are preconditions
+ *     the host cannot see.  Kernels keep every memory access inside the
+ *     buffers described by the arguments even when a precondition is broken;
+ *     a decode or prefill row whose table entries or length are out of range
+ *     is written as NaN.  pkv_validate_tables() checks host copies.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_VERSION 1
+
+typedef enum pkv_dtype { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_INVALID = -1,     /* bad pointer, size or descriptor field */
+  PKV_ERR_UNSUPPORTED = -2, /* valid but not implemented (dtype, D, P, G) */
+  PKV_ERR_WORKSPACE = -3,   /* workspace missing or too small */
+  PKV_ERR_HIP = -4          /* a HIP launch failed; see pkv_last_error() */
+} pkv_status;
+
+/* Describes one layer's K and V page pools (both have this shape and type). */
+typedef struct pkv_cache_desc {
+  int32_t num_pages;    /* physical pages in each pool */
+  int32_t page_size;    /* tokens per page, P */
+  int32_t num_kv_heads; /* H_kv */
+  int32_t head_dim;     /* D */
+  int32_t dtype;        /* pkv_dtype of K, V, Q and the output */
+} pkv_cache_desc;
+
+/* Library version (PKV_VERSION). */
+int pkv_version(void);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/*
+ * kv_append -- write new tokens' K/V into their page slots (page 2, section
+ * 5.2: pages for the next step are allocated ahead; the new token's K/V is
+ * then stored in place).  For each i < n_tokens with s = slot_mapping[i] >= 0
+ * and every KV head g:
+ *     k_cache[s / P][g][s % P][:] = k_new[i][g][:]   (same for V)
+ * A bitwise copy.  slot < 0 skips the token; a slot >= num_pages * P is also
+ * skipped.  Two tokens with the same slot race (unspecified result).
+ *   k_cache, v_cache : device, updated in place.
+ *   k_new, v_new     : device, [n_tokens][H_kv][D] of desc->dtype.
+ *   slot_mapping     : device int32 [n_tokens].
+ * n_tokens == 0 is a no-op.
+ */
+int pkv_kv_append(const pkv_cache_desc* desc, void* k_cache, void* v_cache,
+                  const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                  int32_t n_tokens, void* stream);
+
+/*
+ * gather_kv -- copy logical tokens [0, len) of one sequence into contiguous
+ * k_out, v_out [len][H_kv][D] (device), following table_row (device int32,
+ * ceil(len/P) entries; page 3, section 3.2 address rule).  Bitwise.  Used to
+ * check the indexing path; a page id out of range yields NaN rows for f16,
+ * bf16 and f32 alike.
+ */
+int pkv_gather_kv(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache,
+                  const int32_t* table_row, int32_t len, void* k_out, void* v_out,
+                  void* stream);
+
+/*
+ * decode_plan -- how the decode call splits each sequence's keys.
+ * split_tokens > 0 (a multiple of P) fixes the keys per split; 0 lets the
+ * library choose from batch, H_kv and max_context_len (a fixed rule aimed at
+ * filling a 256-CU device, so the result does not depend on the device).
+ * Writes *n_split (splits per sequence; 1 means no workspace and no merge
+ * pass) and *workspace_bytes (0 when n_split == 1).  Host-only; no HIP call.
+ */
+int pkv_decode_plan(const pkv_cache_desc* desc, int32_t batch, int32_t num_q_heads,
+                    int32_t max_context_len, int32_t split_tokens, int32_t* n_split,
+                    size_t* workspace_bytes);
+
+/*
+ * paged_attn_decode -- one query token per sequence against its paged K/V
+ * (page 1, chapter 4.3: a batched decode over kv_cache, block_table
+ * [batch, max_blocks] and context_lens [batch]).
+ *   q, out       : device [batch][H_q][D] of desc->dtype.
+ *   lse_out      : device float [batch][H_q], natural-log log-sum-exp of the
+ *                  scaled scores; may be NULL.  Empty context: out row 0,
+ *                  lse -inf.
+ *   block_table  : device int32 [batch][block_table_stride].
+ *   context_lens : device int32 [batch]; keys 0 .. len-1 are attended.
+ *   max_context_len : host bound, >= every context_lens[b] and
+ *                  <= block_table_stride * P; sizes the grid.
+ *   scale        : multiplies Q.K (normally 1/sqrt(D)).
+ *   split_tokens : as in pkv_decode_plan.
+ *   workspace    : device, >= the workspace_bytes pkv_decode_plan reports for
+ *                  the same arguments (may be NULL when that is 0).
+ * With n_split > 1 the keys of a sequence are cut into splits of
+ * split_tokens; each split yields a partial (o_k, lse_k) and a merge pass
+ * combines them by their log-sum-exp (the online-softmax recursion of page 2,
+ * section 2.2, applied across splits).
+ */
+int pkv_paged_attn_decode(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache,
+                          const void* q, int32_t batch, int32_t num_q_heads,
+                          const int32_t* block_table, int32_t block_table_stride,
+                          const int32_t* context_lens, int32_t max_context_len, float scale,
+                          int32_t split_tokens, void* out, float* lse_out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * paged_attn_decode_partials -- the first pass of paged_attn_decode alone:
+ * writes, for every (b, h, split k), o_k = (sum_t w_t V_t) / (sum_t w_t) and
+ * lse_k into the workspace, laid out as
+ *     o_parts   float [batch * H_q][n_split][D]      at workspace
+ *     lse_parts float [batch * H_q][n_split]         at workspace + o_bytes,
+ * o_bytes = batch * H_q * n_split * D * 4 rounded up to 256.  An empty split
+ * has o_k = 0 and lse_k = -inf.  Follow with pkv_merge_states() to finish.
+ * Arguments as in paged_attn_decode; the workspace is required even when
+ * n_split == 1 (size: pkv_decode_plan with that split, or the formula above).
+ */
+int pkv_paged_attn_decode_partials(const pkv_cache_desc* desc, const void* k_cache,
+                                   const void* v_cache, const void* q, int32_t batch,
+                                   int32_t num_q_heads, const int32_t* block_table,
+                                   int32_t block_table_stride, const int32_t* context_lens,
+                                   int32_t max_context_len, float scale, int32_t split_tokens,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * merge_states -- combine n_parts partial attention states per row:
+ *     M = max_k lse_k,  w_k = exp(lse_k - M),
+ *     out = sum_k w_k o_k / sum_k w_k,  lse = M + log(sum_k w_k),
+ * in ascending k order.  Parts with lse_k = -inf are skipped; all skipped
+ * gives out 0 and lse -inf.
+ *   o_parts   : device float [rows][n_parts][head_dim]
+ *   lse_parts : device float [rows][n_parts]
+ *   out       : device [rows][head_dim] of out_dtype (pkv_dtype)
+ *   lse_out   : device float [rows] or NULL
+ */
+int pkv_merge_states(const float* o_parts, const float* lse_parts, int32_t rows,
+                     int32_t n_parts, int32_t head_dim, int32_t out_dtype, void* out,
+                     float* lse_out, void* stream);
+
+/*
+ * paged_attn_prefill_chunk -- a causal chunk of query rows against the paged
+ * history plus the chunk itself (page 4, section 3.1: chunked prefill splits
+ * a prompt into chunks that reuse the KV cache).  The caller appends the
+ * chunk's K/V with pkv_kv_append first; kv_lens[b] counts history plus chunk.
+ * Chunk row i of sequence b (C_b rows) sits at position kv_lens[b] - C_b + i
+ * and attends to keys 0 .. that position (bottom-right aligned causal mask).
+ *   q, out       : device, packed [sum_b C_b][H_q][D] of desc->dtype.
+ *   q_indptr     : device int32 [batch + 1]; rows of sequence b are
+ *                  q_indptr[b] .. q_indptr[b+1]-1; q_indptr[0] = 0.
+ *   max_q_len    : host bound >= every C_b; sizes the grid.
+ *   block_table, block_table_stride : as for decode.
+ *   kv_lens      : device int32 [batch]; C_b <= kv_lens[b] <= stride * P.
+ *   max_kv_len   : host bound >= every kv_lens[b], <= stride * P.
+ *   lse_out      : device float [sum C_b][H_q] or NULL.
+ * QK^T and PV run on the matrix cores; needs f16 or bf16, head_dim 128.
+ */
+int pkv_paged_attn_prefill_chunk(const pkv_cache_desc* desc, const void* k_cache,
+                                 const void* v_cache, const void* q, const int32_t* q_indptr,
+                                 int32_t batch, int32_t num_q_heads, int32_t max_q_len,
+                                 const int32_t* block_table, int32_t block_table_stride,
+                                 const int32_t* kv_lens, int32_t max_kv_len, float scale,
+                                 void* out, float* lse_out, void* stream);
+
+/*
+ * validate_tables -- host-side check of host copies of the tables (no HIP
+ * call): every entry a sequence uses (the first ceil(lens[b]/P) of its row)
+ * is in [0, num_pages); 0 <= lens[b] <= stride * P; every slot is < 0 or in
+ * [0, num_pages * P) and no slot >= 0 repeats.  slots may be NULL (n = 0).
+ * Returns PKV_OK or PKV_ERR_INVALID with the first offence in
+ * pkv_last_error().
+ */
+int pkv_validate_tables(const pkv_cache_desc* desc, const int32_t* block_table_host,
+                        int32_t block_table_stride, const int32_t* lens_host, int32_t batch,
+                        const int32_t* slots_host, int32_t n_slots);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -4,3 +4,16 @@ The compute lives in libpkv.so (hand-written HIP kernels behind a C ABI,
 declared in include/pkv.h).  This package holds the thin Python binding over
 that library, the seeded workload generators and the work/byte accounting.
 """
+from .binding import (  # noqa: F401
+    CacheDesc,
+    PkvError,
+    cache_desc,
+    decode_plan,
+    gather_kv,
+    kv_append,
+    merge_states,
+    paged_attn_decode,
+    paged_attn_decode_partials,
+    paged_attn_prefill_chunk,
+    validate_tables,
+)

@@ -1,0 +1,267 @@
+"""Thin ctypes binding over libpkv.so (include/pkv.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream; every step of the computation runs in the library's kernels.  If the
+library is not built the first call raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkv.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "pkv.h")
+
+PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+_TORCH_TO_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
+_CODE_TO_TORCH = {v: k for k, v in _TORCH_TO_CODE.items()}
+STATUS = {0: "PKV_OK", -1: "PKV_ERR_INVALID", -2: "PKV_ERR_UNSUPPORTED",
+          -3: "PKV_ERR_WORKSPACE", -4: "PKV_ERR_HIP"}
+
+
+class PkvError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class CacheDesc(C.Structure):
+    _fields_ = [("num_pages", C.c_int32), ("page_size", C.c_int32),
+                ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("dtype", C.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libpkv.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               f"`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, f32, sz = C.c_void_p, C.c_int32, C.c_float, C.c_size_t
+        dp = C.POINTER(CacheDesc)
+        L.pkv_version.restype = C.c_int
+        L.pkv_last_error.restype = C.c_char_p
+        L.pkv_kv_append.argtypes = [dp, vp, vp, vp, vp, vp, i32, vp]
+        L.pkv_gather_kv.argtypes = [dp, vp, vp, vp, i32, vp, vp, vp]
+        L.pkv_decode_plan.argtypes = [dp, i32, i32, i32, i32, C.POINTER(i32), C.POINTER(sz)]
+        L.pkv_paged_attn_decode.argtypes = [dp, vp, vp, vp, i32, i32, vp, i32, vp, i32, f32, i32,
+                                            vp, vp, vp, sz, vp]
+        L.pkv_paged_attn_decode_partials.argtypes = [dp, vp, vp, vp, i32, i32, vp, i32, vp, i32,
+                                                     f32, i32, vp, sz, vp]
+        L.pkv_merge_states.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
+        L.pkv_paged_attn_prefill_chunk.argtypes = [dp, vp, vp, vp, vp, i32, i32, i32, vp, i32, vp,
+                                                   i32, f32, vp, vp, vp]
+        L.pkv_validate_tables.argtypes = [dp, vp, i32, vp, i32, vp, i32]
+        for name in ("pkv_kv_append", "pkv_gather_kv", "pkv_decode_plan", "pkv_paged_attn_decode",
+                     "pkv_paged_attn_decode_partials", "pkv_merge_states",
+                     "pkv_paged_attn_prefill_chunk", "pkv_validate_tables"):
+            getattr(L, name).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def declared_symbols():
+    """Names of the functions include/pkv.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_0-9]+)\s*\(", text)))
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise PkvError(rc, lib().pkv_last_error().decode())
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def cache_desc(k_cache: torch.Tensor) -> CacheDesc:
+    """Descriptor of a [num_pages][H_kv][P][D] pool."""
+    if k_cache.dim() != 4:
+        raise ValueError("cache must be [num_pages][num_kv_heads][page_size][head_dim]")
+    if k_cache.dtype not in _TORCH_TO_CODE:
+        raise TypeError(f"unsupported cache dtype {k_cache.dtype}")
+    n, h, p, d = k_cache.shape
+    return CacheDesc(n, p, h, d, _TORCH_TO_CODE[k_cache.dtype])
+
+
+def _check_pools(k_cache, v_cache):
+    _dev(k_cache, "k_cache")
+    _dev(v_cache, "v_cache", k_cache.dtype)
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    return cache_desc(k_cache)
+
+
+def kv_append(k_cache, v_cache, k_new, v_new, slots) -> None:
+    """pkv_kv_append: store new tokens' K/V rows [n][H_kv][D] at their slots."""
+    desc = _check_pools(k_cache, v_cache)
+    _dev(k_new, "k_new", k_cache.dtype)
+    _dev(v_new, "v_new", k_cache.dtype)
+    _dev(slots, "slots", torch.int32)
+    n = int(slots.shape[0])
+    if k_new.shape != (n, desc.num_kv_heads, desc.head_dim) or v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new must be [n][H_kv][D]")
+    _check(lib().pkv_kv_append(C.byref(desc), _p(k_cache), _p(v_cache), _p(k_new), _p(v_new),
+                               _p(slots), n, _stream()))
+
+
+def gather_kv(k_cache, v_cache, table_row, length: int) -> Tuple[torch.Tensor, torch.Tensor]:
+    """pkv_gather_kv: logical tokens [0, length) as contiguous [L][H_kv][D]."""
+    desc = _check_pools(k_cache, v_cache)
+    _dev(table_row, "table_row", torch.int32)
+    k_out = torch.empty((length, desc.num_kv_heads, desc.head_dim), dtype=k_cache.dtype,
+                        device=k_cache.device)
+    v_out = torch.empty_like(k_out)
+    _check(lib().pkv_gather_kv(C.byref(desc), _p(k_cache), _p(v_cache), _p(table_row),
+                               int(length), _p(k_out), _p(v_out), _stream()))
+    return k_out, v_out
+
+
+def decode_plan(desc: CacheDesc, batch: int, num_q_heads: int, max_context_len: int,
+                split_tokens: int = 0) -> Tuple[int, int]:
+    """pkv_decode_plan: (n_split, workspace_bytes)."""
+    n = C.c_int32(0)
+    ws = C.c_size_t(0)
+    _check(lib().pkv_decode_plan(C.byref(desc), int(batch), int(num_q_heads),
+                                 int(max_context_len), int(split_tokens), C.byref(n),
+                                 C.byref(ws)))
+    return int(n.value), int(ws.value)
+
+
+def partials_bytes(batch: int, num_q_heads: int, n_split: int, head_dim: int) -> Tuple[int, int]:
+    """(o_bytes rounded to 256, total) of the partials layout in include/pkv.h."""
+    rows = batch * num_q_heads
+    ob = rows * n_split * head_dim * 4
+    ob = (ob + 255) & ~255
+    return ob, ob + rows * n_split * 4
+
+
+def _decode_common(q, k_cache, v_cache, block_table, context_lens, max_context_len):
+    desc = _check_pools(k_cache, v_cache)
+    _dev(q, "q", k_cache.dtype)
+    _dev(block_table, "block_table", torch.int32)
+    _dev(context_lens, "context_lens", torch.int32)
+    if q.dim() != 3 or q.shape[2] != desc.head_dim:
+        raise ValueError("q must be [B][H_q][D]")
+    batch, hq = int(q.shape[0]), int(q.shape[1])
+    if block_table.dim() != 2 or block_table.shape[0] != batch or context_lens.shape != (batch,):
+        raise ValueError("block_table must be [B][stride] and context_lens [B]")
+    return desc, batch, hq
+
+
+def paged_attn_decode(q, k_cache, v_cache, block_table, context_lens, max_context_len: int,
+                      scale: float, split_tokens: int = 0, out=None, lse_out=None,
+                      workspace=None, return_lse: bool = False):
+    """pkv_paged_attn_decode.  Returns out [B][H_q][D] (and lse [B][H_q])."""
+    desc, batch, hq = _decode_common(q, k_cache, v_cache, block_table, context_lens,
+                                     max_context_len)
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse_out is None:
+        lse_out = torch.empty((batch, hq), dtype=torch.float32, device=q.device)
+    n_split, ws_bytes = decode_plan(desc, batch, hq, max_context_len, split_tokens)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pkv_paged_attn_decode(
+        C.byref(desc), _p(k_cache), _p(v_cache), _p(q), batch, hq, _p(block_table),
+        int(block_table.shape[1]), _p(context_lens), int(max_context_len), float(scale),
+        int(split_tokens), _p(out), _p(lse_out), _p(workspace), ws_len, _stream()))
+    return (out, lse_out) if return_lse else out
+
+
+def paged_attn_decode_partials(q, k_cache, v_cache, block_table, context_lens,
+                               max_context_len: int, scale: float, split_tokens: int = 0,
+                               workspace=None):
+    """pkv_paged_attn_decode_partials.  Returns (o_parts [B*H_q][n][D],
+    lse_parts [B*H_q][n], workspace) as views of the workspace."""
+    desc, batch, hq = _decode_common(q, k_cache, v_cache, block_table, context_lens,
+                                     max_context_len)
+    n_split, _ = decode_plan(desc, batch, hq, max_context_len, split_tokens)
+    ob, total = partials_bytes(batch, hq, n_split, desc.head_dim)
+    if workspace is None:
+        workspace = torch.empty(total, dtype=torch.uint8, device=q.device)
+    ws_len = workspace.numel() * workspace.element_size()
+    _check(lib().pkv_paged_attn_decode_partials(
+        C.byref(desc), _p(k_cache), _p(v_cache), _p(q), batch, hq, _p(block_table),
+        int(block_table.shape[1]), _p(context_lens), int(max_context_len), float(scale),
+        int(split_tokens), _p(workspace), ws_len, _stream()))
+    rows = batch * hq
+    o_parts = workspace[:rows * n_split * desc.head_dim * 4].view(torch.float32).view(
+        rows, n_split, desc.head_dim)
+    lse_parts = workspace[ob:ob + rows * n_split * 4].view(torch.float32).view(rows, n_split)
+    return o_parts, lse_parts, workspace
+
+
+def merge_states(o_parts, lse_parts, out_dtype=torch.float32, out=None, lse_out=None,
+                 return_lse: bool = False):
+    """pkv_merge_states.  o_parts [rows][n][D] float32, lse_parts [rows][n]."""
+    _dev(o_parts, "o_parts", torch.float32)
+    _dev(lse_parts, "lse_parts", torch.float32)
+    rows, n, d = (int(x) for x in o_parts.shape)
+    if lse_parts.shape != (rows, n):
+        raise ValueError("lse_parts must be [rows][n_parts]")
+    if out is None:
+        out = torch.empty((rows, d), dtype=out_dtype, device=o_parts.device)
+    if return_lse and lse_out is None:
+        lse_out = torch.empty((rows,), dtype=torch.float32, device=o_parts.device)
+    _check(lib().pkv_merge_states(_p(o_parts), _p(lse_parts), rows, n, d,
+                                  _TORCH_TO_CODE[out.dtype], _p(out), _p(lse_out), _stream()))
+    return (out, lse_out) if return_lse else out
+
+
+def paged_attn_prefill_chunk(q, k_cache, v_cache, q_indptr, block_table, kv_lens,
+                             max_q_len: int, max_kv_len: int, scale: float, out=None,
+                             lse_out=None, return_lse: bool = False):
+    """pkv_paged_attn_prefill_chunk.  q packed [sum C][H_q][D]."""
+    desc = _check_pools(k_cache, v_cache)
+    _dev(q, "q", k_cache.dtype)
+    _dev(q_indptr, "q_indptr", torch.int32)
+    _dev(block_table, "block_table", torch.int32)
+    _dev(kv_lens, "kv_lens", torch.int32)
+    batch = int(q_indptr.shape[0]) - 1
+    hq = int(q.shape[1])
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse_out is None:
+        lse_out = torch.empty((q.shape[0], hq), dtype=torch.float32, device=q.device)
+    _check(lib().pkv_paged_attn_prefill_chunk(
+        C.byref(desc), _p(k_cache), _p(v_cache), _p(q), _p(q_indptr), batch, hq,
+        int(max_q_len), _p(block_table), int(block_table.shape[1]), _p(kv_lens),
+        int(max_kv_len), float(scale), _p(out), _p(lse_out), _stream()))
+    return (out, lse_out) if return_lse else out
+
+
+def validate_tables(desc: CacheDesc, block_table, lens, slots=None) -> None:
+    """pkv_validate_tables on host copies (CPU int32 tensors)."""
+    bt = block_table.to(torch.int32).contiguous().cpu()
+    ln = lens.to(torch.int32).contiguous().cpu()
+    sl = None if slots is None else slots.to(torch.int32).contiguous().cpu()
+    _check(lib().pkv_validate_tables(C.byref(desc), _p(bt), int(bt.shape[1]) if bt.dim() == 2 else 0,
+                                     _p(ln), int(ln.shape[0]), _p(sl),
+                                     0 if sl is None else int(sl.shape[0])))

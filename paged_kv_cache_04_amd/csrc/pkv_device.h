@@ -1,0 +1,133 @@
+// Device-side helpers shared by the HIP kernels: element types, 16-byte
+// vector loads, conversions, packed dot products and cross-lane reductions
+// for 64-wide CDNA wavefronts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+
+struct u32x4 {
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  u32x4 r;
+  r.w[0] = v.x;
+  r.w[1] = v.y;
+  r.w[2] = v.z;
+  r.w[3] = v.w;
+  return r;
+}
+
+__device__ __forceinline__ void store16(void* p, const u32x4& r) {
+  uint4 v;
+  v.x = r.w[0];
+  v.y = r.w[1];
+  v.z = r.w[2];
+  v.w = r.w[3];
+  *reinterpret_cast<uint4*>(p) = v;
+}
+
+__device__ __forceinline__ float u2f(uint32_t u) { return __uint_as_float(u); }
+
+// Element types.  `bytes` is the element size; a 32-bit word holds
+// 4 / bytes elements; lo()/hi() widen the elements of one word to float.
+struct TF32 {
+  static constexpr int bytes = 4;
+  static __device__ __forceinline__ float lo(uint32_t u) { return u2f(u); }
+  static __device__ __forceinline__ float store_cvt(float x) { return x; }
+};
+
+struct TF16 {
+  static constexpr int bytes = 2;
+  static __device__ __forceinline__ float lo(uint32_t u) {
+    return (float)__builtin_bit_cast(half2_t, u).x;
+  }
+  static __device__ __forceinline__ float hi(uint32_t u) {
+    return (float)__builtin_bit_cast(half2_t, u).y;
+  }
+  // sum += a.x*b.x + a.y*b.y with the products and sum in fp32
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a),
+                                  __builtin_bit_cast(half2_t, b), acc, false);
+  }
+  static __device__ __forceinline__ uint16_t from_float(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);  // round to nearest even
+  }
+};
+
+struct TBF16 {
+  static constexpr int bytes = 2;
+  static __device__ __forceinline__ float lo(uint32_t u) { return u2f(u << 16); }
+  static __device__ __forceinline__ float hi(uint32_t u) { return u2f(u & 0xffff0000u); }
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, a),
+                                           __builtin_bit_cast(bf162_t, b), acc, false);
+  }
+  static __device__ __forceinline__ uint16_t from_float(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);    // round to nearest even
+  }
+};
+
+// Store one float as element type TT at p[idx].
+template <typename TT>
+__device__ __forceinline__ void store_elem(void* p, int64_t idx, float x);
+
+template <>
+__device__ __forceinline__ void store_elem<TF32>(void* p, int64_t idx, float x) {
+  reinterpret_cast<float*>(p)[idx] = x;
+}
+template <>
+__device__ __forceinline__ void store_elem<TF16>(void* p, int64_t idx, float x) {
+  reinterpret_cast<uint16_t*>(p)[idx] = TF16::from_float(x);
+}
+template <>
+__device__ __forceinline__ void store_elem<TBF16>(void* p, int64_t idx, float x) {
+  reinterpret_cast<uint16_t*>(p)[idx] = TBF16::from_float(x);
+}
+
+// ---- cross-lane data movement inside a 64-lane wavefront ------------------
+
+// DPP controls (GCN/CDNA encoding).
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i within each 8 lanes
+constexpr int kDppRowRor8 = 0x128;     // rotate right by 8 within 16 lanes (= xor 8)
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float xor_f(float x, int mask) { return __shfl_xor(x, mask, 64); }
+
+// Sum over the 8 lanes {8j .. 8j+7}; every lane of the group gets the sum.
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp_f<kDppQuadXor1>(x);
+  x += dpp_f<kDppQuadXor2>(x);
+  x += dpp_f<kDppHalfMirror>(x);
+  return x;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Order LDS accesses of one wavefront across lanes (writes before reads by
+// other lanes of the same wave).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+}  // namespace pkv

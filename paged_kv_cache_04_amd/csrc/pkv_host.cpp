@@ -1,0 +1,357 @@
+// C-ABI host layer of libpkv: argument checks, the decode split plan and
+// kernel launches on the caller's stream.  See include/pkv.h for the contract.
+#include "pkv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <unordered_set>
+
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return PKV_OK;
+}
+
+int elem_bytes(int dtype) { return dtype == PKV_F32 ? 4 : 2; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_dtype(int dtype) {
+  if (dtype != PKV_F32 && dtype != PKV_F16 && dtype != PKV_BF16)
+    return fail(PKV_ERR_INVALID, "dtype %d is not a pkv_dtype", dtype);
+  return PKV_OK;
+}
+
+int check_desc(const pkv_cache_desc* d) {
+  if (!d) return fail(PKV_ERR_INVALID, "desc is NULL");
+  if (d->num_pages <= 0) return fail(PKV_ERR_INVALID, "num_pages %d <= 0", d->num_pages);
+  if (d->page_size <= 0) return fail(PKV_ERR_INVALID, "page_size %d <= 0", d->page_size);
+  if (d->num_kv_heads <= 0) return fail(PKV_ERR_INVALID, "num_kv_heads %d <= 0", d->num_kv_heads);
+  if (d->head_dim <= 0) return fail(PKV_ERR_INVALID, "head_dim %d <= 0", d->head_dim);
+  if (int rc = check_dtype(d->dtype)) return rc;
+  if (d->page_size != pkv::kPageSize)
+    return fail(PKV_ERR_UNSUPPORTED, "page_size %d: only %d is built", d->page_size,
+                pkv::kPageSize);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d: only 64 and 128 are built", d->head_dim);
+  return PKV_OK;
+}
+
+int check_heads(const pkv_cache_desc* d, int32_t num_q_heads, int* group) {
+  if (num_q_heads <= 0) return fail(PKV_ERR_INVALID, "num_q_heads %d <= 0", num_q_heads);
+  if (num_q_heads % d->num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                num_q_heads, d->num_kv_heads);
+  const int g = num_q_heads / d->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(PKV_ERR_UNSUPPORTED, "query heads per KV head %d: only 1, 2, 4, 8 are built",
+                g);
+  *group = g;
+  return PKV_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// Decode split plan.  Auto rule: aim for about 1024 workgroups (four per CU
+// on a 256-CU device) and never less than 16 pages (256 keys) per split.
+struct Plan {
+  int32_t n_split;
+  int32_t pages_per_split;
+  size_t o_bytes;      // partial outputs, rounded up to 256
+  size_t ws_bytes;     // o_bytes + lse bytes
+};
+
+constexpr int64_t kTargetWorkgroups = 1024;
+constexpr int32_t kMinSplitPages = 16;
+
+int make_plan(const pkv_cache_desc* d, int32_t batch, int32_t num_q_heads,
+              int32_t max_context_len, int32_t split_tokens, Plan* plan) {
+  const int P = d->page_size;
+  const int64_t max_pages = ((int64_t)max_context_len + P - 1) / P;
+  int64_t pps;
+  if (split_tokens > 0) {
+    if (split_tokens % P != 0)
+      return fail(PKV_ERR_INVALID, "split_tokens %d is not a multiple of page_size %d",
+                  split_tokens, P);
+    pps = split_tokens / P;
+  } else if (split_tokens == 0) {
+    const int64_t units = (int64_t)batch * d->num_kv_heads;
+    int64_t want = units > 0 ? (kTargetWorkgroups + units - 1) / units : 1;
+    const int64_t cap = (max_pages + kMinSplitPages - 1) / kMinSplitPages;
+    if (want > cap) want = cap;
+    if (want < 1) want = 1;
+    pps = (max_pages + want - 1) / want;
+    if (pps < 1) pps = 1;
+  } else {
+    return fail(PKV_ERR_INVALID, "split_tokens %d < 0", split_tokens);
+  }
+  int64_t n = max_pages > 0 ? (max_pages + pps - 1) / pps : 1;
+  if (n < 1) n = 1;
+  if (n > (1 << 20) || pps > (1 << 30)) return fail(PKV_ERR_INVALID, "split plan out of range");
+  plan->n_split = (int32_t)n;
+  plan->pages_per_split = (int32_t)pps;
+  const size_t rows = (size_t)batch * num_q_heads;
+  const size_t ob = rows * (size_t)n * d->head_dim * sizeof(float);
+  plan->o_bytes = (ob + 255) & ~(size_t)255;
+  plan->ws_bytes = plan->o_bytes + rows * (size_t)n * sizeof(float);
+  return PKV_OK;
+}
+
+struct DecodeCommon {
+  int group;
+  Plan plan;
+};
+
+int check_decode(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache,
+                 const void* q, int32_t batch, int32_t num_q_heads, const int32_t* block_table,
+                 int32_t stride, const int32_t* context_lens, int32_t max_context_len,
+                 float scale, int32_t split_tokens, DecodeCommon* dc) {
+  if (int rc = check_desc(desc)) return rc;
+  if (int rc = check_heads(desc, num_q_heads, &dc->group)) return rc;
+  if (batch < 0) return fail(PKV_ERR_INVALID, "batch %d < 0", batch);
+  if (stride <= 0) return fail(PKV_ERR_INVALID, "block_table_stride %d <= 0", stride);
+  if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)stride * desc->page_size)
+    return fail(PKV_ERR_INVALID, "max_context_len %d outside [0, stride * page_size = %lld]",
+                max_context_len, (long long)stride * desc->page_size);
+  if (!(scale == scale)) return fail(PKV_ERR_INVALID, "scale is NaN");
+  if (batch > 0) {
+    if (!k_cache || !v_cache || !q || !block_table || !context_lens)
+      return fail(PKV_ERR_INVALID, "NULL input pointer");
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q))
+      return fail(PKV_ERR_INVALID, "k_cache, v_cache and q must be 16-byte aligned");
+  }
+  if (int rc = make_plan(desc, batch, num_q_heads, max_context_len, split_tokens, &dc->plan))
+    return rc;
+  const int64_t blocks = (int64_t)batch * desc->num_kv_heads * dc->plan.n_split;
+  if (blocks > 0x7fffffff) return fail(PKV_ERR_INVALID, "grid too large (%lld)", (long long)blocks);
+  return PKV_OK;
+}
+
+pkv::DecodeArgs decode_args(const pkv_cache_desc* desc, const void* k_cache,
+                            const void* v_cache, const void* q, int32_t num_q_heads,
+                            const int32_t* block_table, int32_t stride,
+                            const int32_t* context_lens, float scale, const Plan& plan) {
+  pkv::DecodeArgs a{};
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.q = q;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.num_pages = desc->num_pages;
+  a.stride = stride;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.num_q_heads = num_q_heads;
+  a.pages_per_split = plan.pages_per_split;
+  a.n_split = plan.n_split;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_version(void) { return PKV_VERSION; }
+
+const char* pkv_last_error(void) { return g_err.c_str(); }
+
+int pkv_kv_append(const pkv_cache_desc* desc, void* k_cache, void* v_cache, const void* k_new,
+                  const void* v_new, const int32_t* slot_mapping, int32_t n_tokens,
+                  void* stream) {
+  if (int rc = check_desc(desc)) return rc;
+  if (n_tokens < 0) return fail(PKV_ERR_INVALID, "n_tokens %d < 0", n_tokens);
+  if (n_tokens == 0) return ok();
+  if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping)
+    return fail(PKV_ERR_INVALID, "NULL pointer");
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
+    return fail(PKV_ERR_INVALID, "cache and new-token buffers must be 16-byte aligned");
+  return hip_status(pkv::launch_kv_append(desc->dtype, desc->head_dim, desc->num_kv_heads,
+                                          desc->num_pages, k_cache, v_cache, k_new, v_new,
+                                          slot_mapping, n_tokens, (hipStream_t)stream),
+                    "kv_append launch");
+}
+
+int pkv_gather_kv(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache,
+                  const int32_t* table_row, int32_t len, void* k_out, void* v_out,
+                  void* stream) {
+  if (int rc = check_desc(desc)) return rc;
+  if (len < 0) return fail(PKV_ERR_INVALID, "len %d < 0", len);
+  if (len == 0) return ok();
+  if (!k_cache || !v_cache || !table_row || !k_out || !v_out)
+    return fail(PKV_ERR_INVALID, "NULL pointer");
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_out) || !aligned16(v_out))
+    return fail(PKV_ERR_INVALID, "buffers must be 16-byte aligned");
+  return hip_status(pkv::launch_gather(desc->dtype, desc->head_dim, desc->num_kv_heads,
+                                       desc->num_pages, k_cache, v_cache, table_row, len, k_out,
+                                       v_out, (hipStream_t)stream),
+                    "gather launch");
+}
+
+int pkv_decode_plan(const pkv_cache_desc* desc, int32_t batch, int32_t num_q_heads,
+                    int32_t max_context_len, int32_t split_tokens, int32_t* n_split,
+                    size_t* workspace_bytes) {
+  if (int rc = check_desc(desc)) return rc;
+  int group = 0;
+  if (int rc = check_heads(desc, num_q_heads, &group)) return rc;
+  if (batch < 0) return fail(PKV_ERR_INVALID, "batch %d < 0", batch);
+  if (max_context_len < 0) return fail(PKV_ERR_INVALID, "max_context_len %d < 0", max_context_len);
+  if (!n_split || !workspace_bytes) return fail(PKV_ERR_INVALID, "NULL output pointer");
+  Plan plan;
+  if (int rc = make_plan(desc, batch, num_q_heads, max_context_len, split_tokens, &plan))
+    return rc;
+  *n_split = plan.n_split;
+  *workspace_bytes = plan.n_split > 1 ? plan.ws_bytes : 0;
+  return ok();
+}
+
+int pkv_paged_attn_decode(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache,
+                          const void* q, int32_t batch, int32_t num_q_heads,
+                          const int32_t* block_table, int32_t block_table_stride,
+                          const int32_t* context_lens, int32_t max_context_len, float scale,
+                          int32_t split_tokens, void* out, float* lse_out, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  DecodeCommon dc;
+  if (int rc = check_decode(desc, k_cache, v_cache, q, batch, num_q_heads, block_table,
+                            block_table_stride, context_lens, max_context_len, scale,
+                            split_tokens, &dc))
+    return rc;
+  if (batch == 0) return ok();
+  if (!out) return fail(PKV_ERR_INVALID, "out is NULL");
+  pkv::DecodeArgs a = decode_args(desc, k_cache, v_cache, q, num_q_heads, block_table,
+                                  block_table_stride, context_lens, scale, dc.plan);
+  hipStream_t s = (hipStream_t)stream;
+  if (dc.plan.n_split == 1) {
+    a.direct = 1;
+    a.out = out;
+    a.lse_out = lse_out;
+    return hip_status(pkv::launch_decode(desc->dtype, desc->head_dim, dc.group, batch, a, s),
+                      "decode launch");
+  }
+  if (!workspace || workspace_bytes < dc.plan.ws_bytes)
+    return fail(PKV_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes,
+                dc.plan.ws_bytes);
+  if (!aligned16(workspace)) return fail(PKV_ERR_INVALID, "workspace must be 16-byte aligned");
+  a.direct = 0;
+  a.o_part = (float*)workspace;
+  a.lse_part = (float*)((char*)workspace + dc.plan.o_bytes);
+  if (int rc = hip_status(pkv::launch_decode(desc->dtype, desc->head_dim, dc.group, batch, a, s),
+                          "decode launch"))
+    return rc;
+  return hip_status(pkv::launch_merge(desc->dtype, desc->head_dim, a.o_part, a.lse_part,
+                                      batch * num_q_heads, dc.plan.n_split, out, lse_out, s),
+                    "merge launch");
+}
+
+int pkv_paged_attn_decode_partials(const pkv_cache_desc* desc, const void* k_cache,
+                                   const void* v_cache, const void* q, int32_t batch,
+                                   int32_t num_q_heads, const int32_t* block_table,
+                                   int32_t block_table_stride, const int32_t* context_lens,
+                                   int32_t max_context_len, float scale, int32_t split_tokens,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  DecodeCommon dc;
+  if (int rc = check_decode(desc, k_cache, v_cache, q, batch, num_q_heads, block_table,
+                            block_table_stride, context_lens, max_context_len, scale,
+                            split_tokens, &dc))
+    return rc;
+  if (batch == 0) return ok();
+  if (!workspace || workspace_bytes < dc.plan.ws_bytes)
+    return fail(PKV_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes,
+                dc.plan.ws_bytes);
+  if (!aligned16(workspace)) return fail(PKV_ERR_INVALID, "workspace must be 16-byte aligned");
+  pkv::DecodeArgs a = decode_args(desc, k_cache, v_cache, q, num_q_heads, block_table,
+                                  block_table_stride, context_lens, scale, dc.plan);
+  a.direct = 0;
+  a.o_part = (float*)workspace;
+  a.lse_part = (float*)((char*)workspace + dc.plan.o_bytes);
+  return hip_status(pkv::launch_decode(desc->dtype, desc->head_dim, dc.group, batch, a,
+                                       (hipStream_t)stream),
+                    "decode launch");
+}
+
+int pkv_merge_states(const float* o_parts, const float* lse_parts, int32_t rows,
+                     int32_t n_parts, int32_t head_dim, int32_t out_dtype, void* out,
+                     float* lse_out, void* stream) {
+  if (rows < 0) return fail(PKV_ERR_INVALID, "rows %d < 0", rows);
+  if (n_parts <= 0) return fail(PKV_ERR_INVALID, "n_parts %d <= 0", n_parts);
+  if (head_dim <= 0) return fail(PKV_ERR_INVALID, "head_dim %d <= 0", head_dim);
+  if (int rc = check_dtype(out_dtype)) return rc;
+  if (rows == 0) return ok();
+  if (!o_parts || !lse_parts || !out) return fail(PKV_ERR_INVALID, "NULL pointer");
+  return hip_status(pkv::launch_merge(out_dtype, head_dim, o_parts, lse_parts, rows, n_parts,
+                                      out, lse_out, (hipStream_t)stream),
+                    "merge launch");
+}
+
+int pkv_paged_attn_prefill_chunk(const pkv_cache_desc* desc, const void* k_cache,
+                                 const void* v_cache, const void* q, const int32_t* q_indptr,
+                                 int32_t batch, int32_t num_q_heads, int32_t max_q_len,
+                                 const int32_t* block_table, int32_t block_table_stride,
+                                 const int32_t* kv_lens, int32_t max_kv_len, float scale,
+                                 void* out, float* lse_out, void* stream) {
+  (void)k_cache; (void)v_cache; (void)q; (void)q_indptr; (void)batch; (void)num_q_heads;
+  (void)max_q_len; (void)block_table; (void)block_table_stride; (void)kv_lens;
+  (void)max_kv_len; (void)scale; (void)out; (void)lse_out; (void)stream;
+  if (int rc = check_desc(desc)) return rc;
+  return fail(PKV_ERR_UNSUPPORTED, "prefill chunk not built yet");
+}
+
+int pkv_validate_tables(const pkv_cache_desc* desc, const int32_t* block_table_host,
+                        int32_t stride, const int32_t* lens_host, int32_t batch,
+                        const int32_t* slots_host, int32_t n_slots) {
+  if (int rc = check_desc(desc)) return rc;
+  if (batch < 0 || n_slots < 0) return fail(PKV_ERR_INVALID, "negative batch or n_slots");
+  if (batch > 0 && (!block_table_host || !lens_host || stride <= 0))
+    return fail(PKV_ERR_INVALID, "NULL table or stride <= 0");
+  const int P = desc->page_size;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t L = lens_host[b];
+    if (L < 0 || L > (int64_t)stride * P)
+      return fail(PKV_ERR_INVALID, "lens[%d] = %lld outside [0, %lld]", b, (long long)L,
+                  (long long)stride * P);
+    const int64_t np = (L + P - 1) / P;
+    for (int64_t i = 0; i < np; ++i) {
+      const int32_t pg = block_table_host[(int64_t)b * stride + i];
+      if (pg < 0 || pg >= desc->num_pages)
+        return fail(PKV_ERR_INVALID, "block_table[%d][%lld] = %d outside [0, %d)", b,
+                    (long long)i, pg, desc->num_pages);
+    }
+  }
+  if (n_slots > 0) {
+    if (!slots_host) return fail(PKV_ERR_INVALID, "slots is NULL");
+    const int64_t total = (int64_t)desc->num_pages * P;
+    std::unordered_set<int32_t> seen;
+    seen.reserve((size_t)n_slots * 2);
+    for (int32_t i = 0; i < n_slots; ++i) {
+      const int32_t s = slots_host[i];
+      if (s < 0) continue;
+      if (s >= total)
+        return fail(PKV_ERR_INVALID, "slot[%d] = %d >= num_pages * page_size = %lld", i, s,
+                    (long long)total);
+      if (!seen.insert(s).second) return fail(PKV_ERR_INVALID, "slot %d repeats (index %d)", s, i);
+    }
+  }
+  return ok();
+}
+
+}  // extern "C"

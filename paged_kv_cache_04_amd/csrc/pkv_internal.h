@@ -1,0 +1,75 @@
+// Internal interface between the C-ABI host layer (pkv_host.cpp) and the
+// kernel launchers (*.hip).  Not installed; the public ABI is include/pkv.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kPageSize = 16;          // tokens per page (the only size built)
+constexpr int kDecodeWaves = 4;        // waves per decode workgroup
+
+struct DecodeArgs {
+  const void* k_cache;
+  const void* v_cache;
+  const void* q;                // [B][H_q][D]
+  const int32_t* block_table;   // [B][stride]
+  const int32_t* context_lens;  // [B]
+  int64_t num_pages;
+  int32_t stride;
+  int32_t num_kv_heads;
+  int32_t num_q_heads;
+  int32_t pages_per_split;
+  int32_t n_split;
+  float scale_log2;             // scale * log2(e)
+  int32_t direct;               // 1: final output to out/lse_out; 0: partials
+  void* out;                    // [B][H_q][D] (direct)
+  float* lse_out;               // [B][H_q] or null (direct)
+  float* o_part;                // [B*H_q][n_split][D] (partials)
+  float* lse_part;              // [B*H_q][n_split]  (partials)
+};
+
+struct PrefillArgs {
+  const void* k_cache;
+  const void* v_cache;
+  const void* q;                // packed [sum C][H_q][D]
+  const int32_t* q_indptr;      // [B+1]
+  const int32_t* block_table;
+  const int32_t* kv_lens;
+  int64_t num_pages;
+  int32_t stride;
+  int32_t num_kv_heads;
+  int32_t num_q_heads;
+  int32_t batch;
+  int32_t max_q_len;
+  int32_t m_tiles;              // query-row tiles per (b, kv head)
+  float scale_log2;
+  void* out;
+  float* lse_out;
+};
+
+// Each launcher validates nothing: the host layer has done it.
+hipError_t launch_kv_append(int dtype, int head_dim, int num_kv_heads, int64_t num_pages,
+                            void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                            const int32_t* slots, int32_t n_tokens, hipStream_t stream);
+
+hipError_t launch_gather(int dtype, int head_dim, int num_kv_heads, int64_t num_pages,
+                         const void* k_cache, const void* v_cache, const int32_t* table_row,
+                         int32_t len, void* k_out, void* v_out, hipStream_t stream);
+
+hipError_t launch_decode(int dtype, int head_dim, int group, int batch, const DecodeArgs& a,
+                         hipStream_t stream);
+
+hipError_t launch_merge(int out_dtype, int head_dim, const float* o_parts,
+                        const float* lse_parts, int32_t rows, int32_t n_parts, void* out,
+                        float* lse_out, hipStream_t stream);
+
+hipError_t launch_prefill(int dtype, int head_dim, int group, const PrefillArgs& a,
+                          hipStream_t stream);
+
+// Rows of query positions one prefill workgroup covers (per KV head group).
+int prefill_rows_per_tile(int group);
+
+}  // namespace pkv

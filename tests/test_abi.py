@@ -1,0 +1,133 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and every invalid-argument path returns its status before
+any HIP call (fake, aligned device addresses are never dereferenced)."""
+import ctypes as C
+
+import pytest
+import torch
+
+from paged_kv_cache_04_amd import binding
+from paged_kv_cache_04_amd.binding import CacheDesc
+
+
+@pytest.fixture(scope="module")
+def L():
+    return binding.lib()
+
+
+FAKE = C.c_void_p(1 << 20)        # aligned, never dereferenced on these paths
+
+
+def desc(num_pages=64, page_size=16, hkv=2, d=128, dtype=2):
+    return CacheDesc(num_pages, page_size, hkv, d, dtype)
+
+
+def test_exports_every_declared_symbol(L):
+    names = binding.declared_symbols()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.pkv_version() == 1
+
+
+def err(L):
+    return L.pkv_last_error().decode()
+
+
+def test_desc_checks(L):
+    assert L.pkv_kv_append(None, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None) == -1
+    for d, code, words in [(desc(page_size=32), -2, "page_size"), (desc(d=96), -2, "head_dim"),
+                           (desc(dtype=7), -1, "dtype"), (desc(num_pages=0), -1, "num_pages"),
+                           (desc(hkv=0), -1, "num_kv_heads"), (desc(page_size=0), -1, "page_size")]:
+        rc = L.pkv_kv_append(C.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 1, None)
+        assert rc == code and words in err(L)
+
+
+def test_append_args(L):
+    d = desc()
+    assert L.pkv_kv_append(C.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, -1, None) == -1
+    assert L.pkv_kv_append(C.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == 0
+    assert L.pkv_kv_append(C.byref(d), FAKE, None, FAKE, FAKE, FAKE, 4, None) == -1
+    assert L.pkv_kv_append(C.byref(d), C.c_void_p((1 << 20) + 4), FAKE, FAKE, FAKE, FAKE, 4,
+                           None) == -1
+    assert "aligned" in err(L)
+
+
+def _decode(L, d, *, batch=2, hq=4, stride=8, max_len=100, split=0, ws=None, ws_bytes=0,
+            out=FAKE, q=FAKE):
+    return L.pkv_paged_attn_decode(C.byref(d), FAKE, FAKE, q, batch, hq, FAKE, stride, FAKE,
+                                   max_len, 0.125, split, out, None, ws, ws_bytes, None)
+
+
+def test_decode_args(L):
+    d = desc()
+    assert _decode(L, d, hq=3) == -1                       # not a multiple of H_kv
+    assert _decode(L, d, hq=32) == -2                      # G = 16 not built
+    assert _decode(L, d, max_len=8 * 16 + 1) == -1         # beyond stride * P
+    assert _decode(L, d, batch=-1) == -1
+    assert _decode(L, d, split=24) == -1                   # not a multiple of P
+    assert _decode(L, d, out=None) == -1
+    assert _decode(L, d, q=None) == -1
+    assert _decode(L, d, batch=0) == 0                     # empty batch: no-op
+
+
+def test_decode_workspace_required_when_split(L):
+    d = desc()
+    n = C.c_int32()
+    ws = C.c_size_t()
+    assert L.pkv_decode_plan(C.byref(d), 2, 4, 128, 32, C.byref(n), C.byref(ws)) == 0
+    assert n.value == 4
+    rows = 2 * 4
+    o_bytes = (rows * 4 * 128 * 4 + 255) // 256 * 256
+    assert ws.value == o_bytes + rows * 4 * 4
+    assert _decode(L, d, max_len=128, split=32, ws=FAKE, ws_bytes=ws.value - 1) == -3
+    assert "workspace" in err(L)
+    assert _decode(L, d, max_len=128, split=32, ws=None, ws_bytes=0) == -3
+
+
+@pytest.mark.parametrize("name,batch,hq,hkv,max_len,want_split", [
+    ("llama70b_128k", 8, 16, 2, 131072, 64),
+    ("tiny", 4, 8, 8, 511, 2),
+    ("prefix", 256, 32, 8, 2560, 1),
+])
+def test_auto_plan(L, name, batch, hq, hkv, max_len, want_split):
+    d = desc(hkv=hkv)
+    n = C.c_int32()
+    ws = C.c_size_t()
+    assert L.pkv_decode_plan(C.byref(d), batch, hq, max_len, 0, C.byref(n), C.byref(ws)) == 0
+    assert n.value == want_split
+    assert (ws.value == 0) == (n.value == 1)
+
+
+def test_merge_args(L):
+    assert L.pkv_merge_states(FAKE, FAKE, -1, 2, 128, 0, FAKE, None, None) == -1
+    assert L.pkv_merge_states(FAKE, FAKE, 4, 0, 128, 0, FAKE, None, None) == -1
+    assert L.pkv_merge_states(FAKE, FAKE, 4, 2, 128, 9, FAKE, None, None) == -1
+    assert L.pkv_merge_states(FAKE, FAKE, 0, 2, 128, 0, FAKE, None, None) == 0
+
+
+def test_validate_tables():
+    d = desc(num_pages=10)
+    bt = torch.tensor([[3, 4, 0], [9, 1, 1]], dtype=torch.int32)
+    binding.validate_tables(d, bt, torch.tensor([40, 17], dtype=torch.int32),
+                            torch.tensor([5, -1, 159], dtype=torch.int32))
+    with pytest.raises(binding.PkvError, match="block_table"):
+        binding.validate_tables(d, torch.tensor([[3, 10, 0]], dtype=torch.int32),
+                                torch.tensor([17], dtype=torch.int32))
+    with pytest.raises(binding.PkvError, match="lens"):
+        binding.validate_tables(d, bt, torch.tensor([49, 1], dtype=torch.int32))
+    with pytest.raises(binding.PkvError, match="repeats"):
+        binding.validate_tables(d, bt, torch.tensor([40, 17], dtype=torch.int32),
+                                torch.tensor([5, 5], dtype=torch.int32))
+    with pytest.raises(binding.PkvError, match="slot"):
+        binding.validate_tables(d, bt, torch.tensor([40, 17], dtype=torch.int32),
+                                torch.tensor([160], dtype=torch.int32))
+    # entries past ceil(len / P) are not checked (they may point anywhere)
+    binding.validate_tables(d, torch.tensor([[3, -7, 99]], dtype=torch.int32),
+                            torch.tensor([16], dtype=torch.int32))
+
+
+def test_binding_rejects_cpu_tensors():
+    x = torch.zeros(4, 2, 16, 128, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        binding.kv_append(x, x, x[0], x[0], torch.zeros(4, dtype=torch.int32))
