@@ -165,7 +165,8 @@ int pkv_paged_attn_decode_partials(const pkv_cache_desc* desc, const void* k_cac
  *     out = sum_k w_k o_k / sum_k w_k,  lse = M + log(sum_k w_k),
  * in ascending k order.  Parts with lse_k = -inf are skipped; all skipped
  * gives out 0 and lse -inf.
- *   o_parts   : device float [rows][n_parts][head_dim]
+ *   o_parts   : device float [rows][n_parts][head_dim], 16-byte aligned;
+ *               head_dim 64 or 128
  *   lse_parts : device float [rows][n_parts]
  *   out       : device [rows][head_dim] of out_dtype (pkv_dtype)
  *   lse_out   : device float [rows] or NULL

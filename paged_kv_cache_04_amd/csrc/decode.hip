@@ -14,22 +14,32 @@
 // K/V page block is read from HBM once per KV head, never once per query head
 // (page 4, section 2.2: GQA shares KV heads).  A split is a run of
 // pages_per_split logical pages; wave w of the workgroup takes pages
-// w, w+4, w+8, ... of the split, keeping four independent page streams in
-// flight per workgroup.  Each wave keeps its own (m, l, acc) state; the four
-// are combined through LDS at the end.
+// w, w+4, w+8, ... of the split.  Each wave keeps its own (m, l, acc) state;
+// the four are combined through LDS at the end.  Every wave keeps the loads
+// of its next two pages in flight while it computes the current one (three
+// register buffers).
 //
 // Per page (16 tokens x D elements, one contiguous 2-8 KiB block per head):
 //   K, "row layout": 8 lanes per token, 8 tokens per pass, 2 passes; lane c of
 //      a token reads 16-byte vectors c, c+8, ... so each load instruction
 //      reads whole 128-byte lines.  q for the G heads sits in registers in the
-//      same layout.  Partial dot products (packed dot2 for f16/bf16, fp32 FMA
-//      for f32) are summed over the 8 lanes with three DPP adds.
-//   softmax: the running max is updated only when some score exceeds it
-//      (a wave vote); otherwise the page costs one exp2 per score.
-//   V, "column layout": DG = D / vec lanes cover one token row, 64 / DG token
-//      groups; each lane accumulates G x vec outputs over its tokens.  The
-//      probabilities cross from the row layout to the column layout through
-//      a small per-wave LDS buffer.
+//      same layout.  Each lane forms G partial dot products (packed dot2 for
+//      f16/bf16, fp32 FMA for f32).  A transposed butterfly over the 8 lanes
+//      (three DPP exchanges, each halving the values a lane keeps) leaves lane
+//      c holding the complete score of head c >> (3 - log2 G), so the softmax
+//      work of a page (max vote, exp2, running sum) is done once per
+//      (token, head), not once per lane.
+//   running max: updated only when some score exceeds it (a wave vote), then
+//      reduced over the tokens and broadcast per head with v_readlane.
+//   V, "column layout": each lane holds 4 consecutive elements of a token row
+//      (8-byte loads for f16/bf16, 16-byte for f32), D / 4 lanes per row and
+//      64 / (D / 4) token groups; each lane accumulates G x 4 fp32 outputs.
+//      For f16/bf16 the probabilities are rounded to the value type and stored
+//      as pairs of tokens in LDS; V elements of the same two tokens are paired
+//      with v_perm, and one packed dot2 adds both tokens' contributions.  f16
+//      probabilities are carried as p * 2^15 (exact power-of-two scaling; the
+//      largest is 2^15 < 65504) so that small weights keep their precision.
+//      For f32 the probabilities stay fp32 and PV is plain FMA.
 // Tokens past the end of the sequence (the tail of the last page) are
 // selected out, never multiplied by zero, so stale or NaN slots never leak.
 #include "pkv_device.h"
@@ -42,19 +52,31 @@ namespace {
 constexpr int P = kPageSize;
 constexpr int NW = kDecodeWaves;
 
+constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+
 template <typename TT, int D, int G>
 struct DecodeCfg {
   static constexpr int ES = TT::bytes;
-  static constexpr int VEC = 16 / ES;        // elements per 16-byte vector
+  static constexpr int VEC = 16 / ES;        // elements per 16-byte K vector
   static constexpr int KL = 8;               // lanes per K row
   static constexpr int KT = 64 / KL;         // tokens per K pass
   static constexpr int KP = P / KT;          // K passes per page
   static constexpr int KV = D / (KL * VEC);  // 16-byte vectors per lane per K row
-  static constexpr int DG = D / VEC;         // lanes per V row
+  static constexpr int VE = 4;               // V elements per lane per token
+  static constexpr int VW = VE * ES / 4;     // 32-bit words of one V load (2 or 4)
+  static constexpr int DG = D / VE;          // lanes per V row
   static constexpr int TG = 64 / DG;         // V token groups
   static constexpr int VT = P / TG;          // V tokens per lane per page
+  static constexpr int HSHIFT = 3 - ilog2(G);  // lane c owns head c >> HSHIFT
+  static constexpr bool PACKED = (ES == 2);  // packed-pair PV for 16-bit types
+  // f16 probabilities are stored as p * 2^15
+  static constexpr float POFF = TT::is_f16 ? 15.f : 0.f;
+  // pages in flight per wave: the one being computed plus NB - 1 ahead
+  static constexpr int NB = (ES == 4) ? 2 : 3;
   static_assert(KV >= 1 && KV * KL * VEC == D, "head_dim / vector mismatch");
   static_assert(TG >= 1 && VT * TG == P, "V layout mismatch");
+  static_assert(!PACKED || VT % 2 == 0, "packed PV pairs tokens");
+  static_assert(G >= 1 && G <= 8 && (G & (G - 1)) == 0, "group size");
 };
 
 // Partial dot product of one lane's slice of q and of a K row.
@@ -75,30 +97,64 @@ __device__ __forceinline__ float dot_slice(const u32x4 (&q)[KV], const u32x4 (&k
   return acc;
 }
 
-// Widen one 16-byte vector of V to floats.
-template <typename TT, int VEC>
-__device__ __forceinline__ void widen(const u32x4& x, float (&f)[VEC]) {
-  if constexpr (TT::bytes == 4) {
+// One transposed butterfly step over a lane bit: the lane keeps half of its N
+// values (the upper half if `hi`), sends the other half to its partner and adds
+// what the partner sends.  Afterwards v[0 .. N/2) hold the kept half.
+template <int N, int CTRL>
+__device__ __forceinline__ void tstep(float (&v)[8], bool hi) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f[i] = u2f(x.w[i]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = TT::lo(x.w[i]);
-      f[2 * i + 1] = TT::hi(x.w[i]);
-    }
+  for (int i = 0; i < N / 2; ++i) {
+    const float a = v[i], b = v[i + N / 2];
+    const float send = hi ? a : b;
+    const float keep = hi ? b : a;
+    v[i] = keep + dpp_f<CTRL>(send);
   }
 }
 
+// Sum G per-lane partials over the 8 lanes of a token; lane c returns the
+// full sum for head c >> (3 - log2 G).
+template <int G>
+__device__ __forceinline__ float reduce_heads(float (&v)[8], int c) {
+  if constexpr (G >= 2) tstep<G, kDppHalfMirror>(v, (c & 4) != 0);
+  else v[0] += dpp_f<kDppHalfMirror>(v[0]);
+  if constexpr (G >= 4) tstep<G / 2, kDppQuadXor2>(v, (c & 2) != 0);
+  else v[0] += dpp_f<kDppQuadXor2>(v[0]);
+  if constexpr (G >= 8) tstep<G / 4, kDppQuadXor1>(v, (c & 1) != 0);
+  else v[0] += dpp_f<kDppQuadXor1>(v[0]);
+  return v[0];
+}
+
+// Max / sum over the 8 token groups of the row layout (lane bits 3..5).
+__device__ __forceinline__ float max_tokens(float x) {
+  x = fmaxf(x, dpp_f<kDppRowRor8>(x));
+  x = fmaxf(x, xor_f(x, 16));
+  return fmaxf(x, xor_f(x, 32));
+}
+__device__ __forceinline__ float sum_tokens(float x) {
+  x += dpp_f<kDppRowRor8>(x);
+  x += xor_f(x, 16);
+  return x + xor_f(x, 32);
+}
+
 template <typename TT, int D, int G>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
+struct PageRegs {
+  using C = DecodeCfg<TT, D, G>;
+  u32x4 k[C::KP][C::KV];
+  uint32_t v[C::VT][C::VW];
+};
+
+template <typename TT, int D, int G>
+__global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeArgs a) {
   using C = DecodeCfg<TT, D, G>;
   constexpr int ES = C::ES, VEC = C::VEC;
-  __shared__ float p_lds[NW][P][G];
+  // probabilities of the current page: packed pairs (16-bit) or floats [t][h]
+  constexpr int PWORDS = C::PACKED ? (P / 2) * G : P * G;
+  __shared__ uint32_t p_lds[NW][PWORDS];
   __shared__ float red_m[NW][G];
   __shared__ float red_l[NW][G];
   __shared__ float red_acc[NW][G][D];
   __shared__ int bad_flag;
+  __shared__ int pid_lds[NW][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -138,9 +194,15 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
   }
   if (tid == 0) bad_flag = 0;
 
-  // q slices for the G heads, row layout.
+  // row layout: lane = tk * 8 + c
   const int c = lane & (C::KL - 1);
   const int tk = lane / C::KL;
+  const int h_own = c >> C::HSHIFT;
+  const bool p_writer = (c & ((1 << C::HSHIFT) - 1)) == 0;
+  // column layout: lane = tg * DG + dg
+  const int dg = lane % C::DG;
+  const int tg = lane / C::DG;
+
   u32x4 qv[G][C::KV];
 #pragma unroll
   for (int h = 0; h < G; ++h)
@@ -150,155 +212,194 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeArgs a) {
                         (((int64_t)b * a.num_q_heads + hq0 + h) * D + v * C::KL * VEC + c * VEC) *
                             ES);
 
-  const int dg = lane % C::DG;
-  const int tg = lane / C::DG;
-
-  float m[G], l_lane[G], acc[G][VEC];
+  float m_own = -INFINITY, l_own = 0.f;
+  float acc[G][C::VE];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    l_lane[h] = 0.f;
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[h][e] = 0.f;
-  }
+    for (int e = 0; e < C::VE; ++e) acc[h][e] = 0.f;
 
   const int32_t* bt_row = a.block_table + (int64_t)b * a.stride;
   const int my_pages = (p1 - p0 > w) ? (p1 - p0 - w + NW - 1) / NW : 0;
   const int64_t head_block = (int64_t)P * D * ES;  // bytes of one (page, head) block
   bool wave_bad = false;
-  int pid_vec = 0;
+  uint32_t* pw = p_lds[w];
   __syncthreads();
 
-  for (int i = 0; i < my_pages; ++i) {
-    if ((i & 63) == 0) {  // page ids of the next 64 pages of this wave, one per lane
+  // Issue the loads of this wave's i-th page into r.  The wave's page ids are
+  // staged in LDS 64 at a time, so a lookup waits only on LDS, never on the
+  // K/V loads in flight (those drain only at a refill, once per 64 pages).
+  auto issue = [&](PageRegs<TT, D, G>& r, int i) {
+    if ((i & 63) == 0) {
       const int idx = i + lane;
-      pid_vec = idx < my_pages ? bt_row[p0 + w + NW * idx] : 0;
+      const int v = idx < my_pages ? bt_row[p0 + w + NW * idx] : 0;
+      wave_lds_sync();
+      pid_lds[w][lane] = v;
+      wave_lds_sync();
     }
-    int pid = __builtin_amdgcn_readlane(pid_vec, i & 63);
+    int pid = __builtin_amdgcn_readfirstlane(pid_lds[w][i & 63]);
     if (pid < 0 || pid >= a.num_pages) {
       wave_bad = true;
       pid = 0;
     }
-    const int pi = p0 + w + NW * i;  // logical page index
     const int64_t blk = ((int64_t)pid * a.num_kv_heads + g) * head_block;
     const char* kb = (const char*)a.k_cache + blk;
     const char* vb = (const char*)a.v_cache + blk;
-
-    u32x4 kr[C::KP][C::KV];
 #pragma unroll
-    for (int r = 0; r < C::KP; ++r)
+    for (int rr = 0; rr < C::KP; ++rr)
 #pragma unroll
       for (int v = 0; v < C::KV; ++v)
-        kr[r][v] = load16(kb + ((tk + C::KT * r) * D + v * C::KL * VEC + c * VEC) * ES);
-    u32x4 vr[C::VT];
-#pragma unroll
-    for (int j = 0; j < C::VT; ++j) vr[j] = load16(vb + ((tg + C::TG * j) * D + dg * VEC) * ES);
-
-    const bool partial = (pi + 1) * P > L;
-
-    // scores (log2 units)
-    float s[C::KP][G];
-#pragma unroll
-    for (int r = 0; r < C::KP; ++r) {
-      const bool valid = !partial || (pi * P + tk + C::KT * r < L);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float d = sum8(dot_slice<TT, C::KV>(qv[h], kr[r]));
-        s[r][h] = valid ? d * a.scale_log2 : -INFINITY;
-      }
-    }
-
-    // running max: reduce and rescale only when some score exceeds it
-    bool need = false;
-#pragma unroll
-    for (int r = 0; r < C::KP; ++r)
-#pragma unroll
-      for (int h = 0; h < G; ++h) need |= s[r][h] > m[h];
-    if (__ballot(need) != 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float mx = s[0][h];
-#pragma unroll
-        for (int r = 1; r < C::KP; ++r) mx = fmaxf(mx, s[r][h]);
-        mx = fmaxf(mx, dpp_f<kDppRowRor8>(mx));
-        mx = fmaxf(mx, xor_f(mx, 16));
-        mx = fmaxf(mx, xor_f(mx, 32));
-        const float mn = fmaxf(m[h], mx);
-        const float alpha = exp2_fast(m[h] - mn);
-        m[h] = mn;
-        l_lane[h] *= alpha;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[h][e] *= alpha;
-      }
-    }
-
-    float p[C::KP][G];
-#pragma unroll
-    for (int r = 0; r < C::KP; ++r)
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        p[r][h] = exp2_fast(s[r][h] - m[h]);
-        l_lane[h] += p[r][h];
-      }
-
-    // probabilities: row layout -> column layout through LDS
-    wave_lds_sync();
-    if (c == 0) {
-#pragma unroll
-      for (int r = 0; r < C::KP; ++r)
-#pragma unroll
-        for (int h = 0; h < G; ++h) p_lds[w][tk + C::KT * r][h] = p[r][h];
-    }
-    wave_lds_sync();
-
+        r.k[rr][v] = load16(kb + ((tk + C::KT * rr) * D + v * C::KL * VEC + c * VEC) * ES);
 #pragma unroll
     for (int j = 0; j < C::VT; ++j) {
-      const int t = tg + C::TG * j;
-      float pv[G];
+      const char* src = vb + ((tg + C::TG * j) * D + dg * C::VE) * ES;
+      if constexpr (C::VW == 2) {
+        const u32x2 x = load8(src);
+        r.v[j][0] = x.w[0];
+        r.v[j][1] = x.w[1];
+      } else {
+        const u32x4 x = load16(src);
 #pragma unroll
-      for (int h = 0; h < G; ++h) pv[h] = p_lds[w][t][h];
-      float vf[VEC];
-      widen<TT, VEC>(vr[j], vf);
-      if (partial && pi * P + t >= L) {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) vf[e] = 0.f;
+        for (int e = 0; e < 4; ++e) r.v[j][e] = x.w[e];
       }
+    }
+  };
+
+  // Online-softmax update with the wave's i-th page held in r.
+  auto compute = [&](const PageRegs<TT, D, G>& r, int i) {
+    const int pi = p0 + w + NW * i;  // logical page index
+    const int t0 = pi * P;
+    const bool partial = t0 + P > L;
+
+    float s[C::KP];
 #pragma unroll
-      for (int h = 0; h < G; ++h)
+    for (int rr = 0; rr < C::KP; ++rr) {
+      float part[8];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(pv[h], vf[e], acc[h][e]);
+      for (int h = 0; h < G; ++h) part[h] = dot_slice<TT, C::KV>(qv[h], r.k[rr]);
+      const float sc = reduce_heads<G>(part, c) * a.scale_log2;
+      const bool valid = !partial || (t0 + tk + C::KT * rr < L);
+      s[rr] = valid ? sc : -INFINITY;
+    }
+
+    bool need = false;
+#pragma unroll
+    for (int rr = 0; rr < C::KP; ++rr) need |= s[rr] > m_own;
+    if (__ballot(need) != 0) {
+      float mx = s[0];
+#pragma unroll
+      for (int rr = 1; rr < C::KP; ++rr) mx = fmaxf(mx, s[rr]);
+      const float mn = fmaxf(m_own, max_tokens(mx));
+      const float alpha = exp2_fast(m_own - mn);
+      m_own = mn;
+      l_own *= alpha;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float ah = __int_as_float(
+            __builtin_amdgcn_readlane(__float_as_int(alpha), h << C::HSHIFT));
+#pragma unroll
+        for (int e = 0; e < C::VE; ++e) acc[h][e] *= ah;
+      }
+    }
+
+    wave_lds_sync();  // the previous page's probabilities have been read
+#pragma unroll
+    for (int rr = 0; rr < C::KP; ++rr) {
+      const float pf = exp2_fast(s[rr] - m_own + C::POFF);
+      l_own += (C::POFF != 0.f) ? pf * (1.f / 32768.f) : pf;
+      if (p_writer) {
+        const int t = tk + C::KT * rr;
+        if constexpr (C::PACKED) {
+          const int word = ((t % C::TG) + C::TG * ((t / C::TG) >> 1)) * G + h_own;
+          const int half = (t / C::TG) & 1;
+          reinterpret_cast<uint16_t*>(pw)[word * 2 + half] = TT::from_float(pf);
+        } else {
+          reinterpret_cast<float*>(pw)[t * G + h_own] = pf;
+        }
+      }
+    }
+    wave_lds_sync();
+
+    if constexpr (C::PACKED) {
+#pragma unroll
+      for (int pp = 0; pp < C::VT / 2; ++pp) {
+        const int ta = tg + C::TG * 2 * pp, tb = ta + C::TG;
+        uint32_t wa[C::VW], wb[C::VW];
+        const bool va = !partial || (t0 + ta < L), vb_ok = !partial || (t0 + tb < L);
+#pragma unroll
+        for (int e = 0; e < C::VW; ++e) {
+          wa[e] = va ? r.v[2 * pp][e] : 0u;
+          wb[e] = vb_ok ? r.v[2 * pp + 1][e] : 0u;
+        }
+        uint32_t pr[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) pr[h] = pw[(tg + C::TG * pp) * G + h];
+#pragma unroll
+        for (int i2 = 0; i2 < C::VW; ++i2) {
+          const uint32_t lo = __builtin_amdgcn_perm(wb[i2], wa[i2], 0x05040100u);
+          const uint32_t hi = __builtin_amdgcn_perm(wb[i2], wa[i2], 0x07060302u);
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            acc[h][2 * i2] = TT::dot2(pr[h], lo, acc[h][2 * i2]);
+            acc[h][2 * i2 + 1] = TT::dot2(pr[h], hi, acc[h][2 * i2 + 1]);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < C::VT; ++j) {
+        const int t = tg + C::TG * j;
+        const bool valid = !partial || (t0 + t < L);
+        const float* pf = reinterpret_cast<const float*>(pw) + t * G;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float ph = pf[h];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[h][e] = fmaf(ph, valid ? u2f(r.v[j][e]) : 0.f, acc[h][e]);
+        }
+      }
+    }
+  };
+
+  {
+    // software pipeline: NB register buffers, loads issued NB - 1 pages ahead
+    PageRegs<TT, D, G> rb[C::NB];
+#pragma unroll
+    for (int j = 0; j < C::NB - 1; ++j)
+      if (j < my_pages) issue(rb[j], j);
+    for (int i = 0; i < my_pages; i += C::NB) {
+#pragma unroll
+      for (int u = 0; u < C::NB; ++u) {
+        const int ii = i + u;
+        if (ii < my_pages) {
+          if (ii + C::NB - 1 < my_pages) issue(rb[(u + C::NB - 1) % C::NB], ii + C::NB - 1);
+          compute(rb[u], ii);
+        }
+      }
     }
   }
 
-  // l: sum over the 8 token groups of the row layout
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float x = l_lane[h];
-    x += dpp_f<kDppRowRor8>(x);
-    x += xor_f(x, 16);
-    x += xor_f(x, 32);
-    l_lane[h] = x;
-  }
+  // l: the owners of each head sum over the 8 token groups
+  l_own = sum_tokens(l_own);
   // acc: sum over the token groups of the column layout
 #pragma unroll
   for (int msk = C::DG; msk < 64; msk <<= 1)
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[h][e] += xor_f(acc[h][e], msk);
+      for (int e = 0; e < C::VE; ++e) acc[h][e] += xor_f(acc[h][e], msk);
 
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      red_m[w][h] = m[h];
-      red_l[w][h] = l_lane[h];
-    }
+  if (tk == 0 && p_writer) {
+    red_m[w][h_own] = m_own;
+    red_l[w][h_own] = l_own;
   }
   if (tg == 0) {
+    constexpr float unscale = C::POFF != 0.f ? 1.f / 32768.f : 1.f;
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) red_acc[w][h][dg * VEC + e] = acc[h][e];
+      for (int e = 0; e < C::VE; ++e) red_acc[w][h][dg * C::VE + e] = acc[h][e] * unscale;
   }
   if (wave_bad) bad_flag = 1;
   __syncthreads();

@@ -6,18 +6,21 @@
 //   M = max_k lse_k,  w_k = exp(lse_k - M),
 //   out = sum_k w_k o_k / sum_k w_k,  lse = M + log sum_k w_k,
 // the same rescaling step the online softmax applies between key blocks
-// (page 2, section 2.2).  Parts are combined in ascending k order, so the
-// result does not depend on the schedule.
+// (page 2, section 2.2).  The combination order is fixed by (n_parts, D), so
+// the result does not depend on the schedule.
 //
-// One wavefront per row.  The lse values of a row are read lane-parallel for
-// the maximum and the weight sum; the D outputs are spread over the lanes and
-// each loops over the parts, reading o_k rows with coalesced loads.
+// One 256-thread workgroup per row.  The lse values are reduced block-wide for
+// the maximum and the weight sum; the o_k rows are then read as float4 by
+// groups of D/4 lanes, group j taking parts j, j + n_groups, ... with all of
+// its loads independent, and the groups' sums are added in LDS.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
 namespace pkv {
 
 namespace {
+
+constexpr int kMergeThreads = 256;
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -31,54 +34,101 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-template <typename TT>
-__global__ __launch_bounds__(64) void merge_kernel(const float* __restrict__ o_parts,
-                                                   const float* __restrict__ lse_parts,
-                                                   int32_t n_parts, int32_t head_dim,
-                                                   void* __restrict__ out,
-                                                   float* __restrict__ lse_out) {
-  const int64_t row = blockIdx.x;
-  const int lane = threadIdx.x;
-  const float* lp = lse_parts + row * n_parts;
-  const float* op = o_parts + row * n_parts * (int64_t)head_dim;
+template <typename TT, int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(
+    const float* __restrict__ o_parts, const float* __restrict__ lse_parts, int32_t n_parts,
+    void* __restrict__ out, float* __restrict__ lse_out) {
+  constexpr int LPP = D / 4;                    // lanes per part row (float4 each)
+  constexpr int NG = kMergeThreads / LPP;       // part groups
+  __shared__ float red[NG][D];
+  __shared__ float wred[4];
+  __shared__ int nan_red[4];
 
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const float* lp = lse_parts + row * n_parts;
+  const float* op = o_parts + row * n_parts * (int64_t)D;
+
+  // block max and NaN check
   float mx = -INFINITY;
-  bool nan_seen = false;
-  for (int k = lane; k < n_parts; k += 64) {
+  int nan_seen = 0;
+  for (int k = tid; k < n_parts; k += kMergeThreads) {
     const float l = lp[k];
     nan_seen |= (l != l);
     mx = fmaxf(mx, l);
   }
-  if (__ballot(nan_seen) != 0) {  // a poisoned part poisons the row
-    for (int d = lane; d < head_dim; d += 64)
-      store_elem<TT>(out, row * head_dim + d, __builtin_nanf(""));
-    if (lane == 0 && lse_out) lse_out[row] = __builtin_nanf("");
+  mx = wave_max(mx);
+  nan_seen = __ballot(nan_seen) != 0;
+  if (lane == 0) {
+    wred[wv] = mx;
+    nan_red[wv] = nan_seen;
+  }
+  __syncthreads();
+  const float M = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
+  const bool any_nan = (nan_red[0] | nan_red[1] | nan_red[2] | nan_red[3]) != 0;
+  if (any_nan || M == -INFINITY) {  // a poisoned part poisons the row; all empty gives 0
+    const float o = any_nan ? __builtin_nanf("") : 0.f;
+    for (int d = tid; d < D; d += kMergeThreads) store_elem<TT>(out, row * D + d, o);
+    if (tid == 0 && lse_out) lse_out[row] = any_nan ? __builtin_nanf("") : -INFINITY;
     return;
   }
-  const float M = wave_max(mx);
-  if (M == -INFINITY) {  // every part empty
-    for (int d = lane; d < head_dim; d += 64) store_elem<TT>(out, row * head_dim + d, 0.f);
-    if (lane == 0 && lse_out) lse_out[row] = -INFINITY;
-    return;
-  }
-  float ws = 0.f;
-  for (int k = lane; k < n_parts; k += 64) {
-    const float l = lp[k];
-    if (l != -INFINITY) ws += exp2_fast((l - M) * kLog2e);
-  }
-  const float wsum = wave_sum(ws);
-  const float inv = 1.f / wsum;
+  __syncthreads();  // wred is reused below
 
-  for (int d = lane; d < head_dim; d += 64) {
-    float acc = 0.f;
-    for (int k = 0; k < n_parts; ++k) {
-      const float l = lp[k];
-      if (l == -INFINITY) continue;
-      acc = fmaf(exp2_fast((l - M) * kLog2e), op[(int64_t)k * head_dim + d], acc);
-    }
-    store_elem<TT>(out, row * head_dim + d, acc * inv);
+  float ws = 0.f;
+  for (int k = tid; k < n_parts; k += kMergeThreads) {
+    const float l = lp[k];
+    ws += (l == -INFINITY) ? 0.f : exp2_fast((l - M) * kLog2e);
   }
-  if (lane == 0 && lse_out) lse_out[row] = M + log2_fast(wsum) * kLn2;
+  ws = wave_sum(ws);
+  if (lane == 0) wred[wv] = ws;
+
+  const int grp = tid / LPP, li = tid % LPP;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int k = grp; k < n_parts; k += NG) {
+    const float l = lp[k];
+    const float4 o = *reinterpret_cast<const float4*>(op + (int64_t)k * D + li * 4);
+    const bool skip = (l == -INFINITY);
+    const float wk = skip ? 0.f : exp2_fast((l - M) * kLog2e);
+    acc.x += skip ? 0.f : wk * o.x;
+    acc.y += skip ? 0.f : wk * o.y;
+    acc.z += skip ? 0.f : wk * o.z;
+    acc.w += skip ? 0.f : wk * o.w;
+  }
+  red[grp][li * 4 + 0] = acc.x;
+  red[grp][li * 4 + 1] = acc.y;
+  red[grp][li * 4 + 2] = acc.z;
+  red[grp][li * 4 + 3] = acc.w;
+  __syncthreads();
+  const float wsum = wred[0] + wred[1] + wred[2] + wred[3];
+  const float inv = 1.f / wsum;
+  for (int d = tid; d < D; d += kMergeThreads) {
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < NG; ++j) s += red[j][d];
+    store_elem<TT>(out, row * D + d, s * inv);
+  }
+  if (tid == 0 && lse_out) lse_out[row] = M + log2_fast(wsum) * kLn2;
+}
+
+template <typename TT>
+hipError_t launch_t(int head_dim, const float* o_parts, const float* lse_parts, int32_t rows,
+                    int32_t n_parts, void* out, float* lse_out, hipStream_t stream) {
+  const dim3 grid((unsigned)rows), block(kMergeThreads);
+  switch (head_dim) {
+    case 64:
+      hipLaunchKernelGGL((merge_kernel<TT, 64>), grid, block, 0, stream, o_parts, lse_parts,
+                         n_parts, out, lse_out);
+      break;
+    case 128:
+      hipLaunchKernelGGL((merge_kernel<TT, 128>), grid, block, 0, stream, o_parts, lse_parts,
+                         n_parts, out, lse_out);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -87,24 +137,12 @@ hipError_t launch_merge(int out_dtype, int head_dim, const float* o_parts,
                         const float* lse_parts, int32_t rows, int32_t n_parts, void* out,
                         float* lse_out, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  const dim3 grid((unsigned)rows), block(64);
   switch (out_dtype) {
-    case 0:
-      hipLaunchKernelGGL(merge_kernel<TF32>, grid, block, 0, stream, o_parts, lse_parts,
-                         n_parts, head_dim, out, lse_out);
-      break;
-    case 1:
-      hipLaunchKernelGGL(merge_kernel<TF16>, grid, block, 0, stream, o_parts, lse_parts,
-                         n_parts, head_dim, out, lse_out);
-      break;
-    case 2:
-      hipLaunchKernelGGL(merge_kernel<TBF16>, grid, block, 0, stream, o_parts, lse_parts,
-                         n_parts, head_dim, out, lse_out);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case 0: return launch_t<TF32>(head_dim, o_parts, lse_parts, rows, n_parts, out, lse_out, stream);
+    case 1: return launch_t<TF16>(head_dim, o_parts, lse_parts, rows, n_parts, out, lse_out, stream);
+    case 2: return launch_t<TBF16>(head_dim, o_parts, lse_parts, rows, n_parts, out, lse_out, stream);
+    default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace pkv

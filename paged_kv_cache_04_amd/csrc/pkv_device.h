@@ -25,6 +25,18 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
   return r;
 }
 
+struct u32x2 {
+  uint32_t w[2];
+};
+
+__device__ __forceinline__ u32x2 load8(const void* p) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  u32x2 r;
+  r.w[0] = v.x;
+  r.w[1] = v.y;
+  return r;
+}
+
 __device__ __forceinline__ void store16(void* p, const u32x4& r) {
   uint4 v;
   v.x = r.w[0];
@@ -40,12 +52,14 @@ __device__ __forceinline__ float u2f(uint32_t u) { return __uint_as_float(u); }
 // 4 / bytes elements; lo()/hi() widen the elements of one word to float.
 struct TF32 {
   static constexpr int bytes = 4;
+  static constexpr bool is_f16 = false;
   static __device__ __forceinline__ float lo(uint32_t u) { return u2f(u); }
   static __device__ __forceinline__ float store_cvt(float x) { return x; }
 };
 
 struct TF16 {
   static constexpr int bytes = 2;
+  static constexpr bool is_f16 = true;
   static __device__ __forceinline__ float lo(uint32_t u) {
     return (float)__builtin_bit_cast(half2_t, u).x;
   }
@@ -64,6 +78,7 @@ struct TF16 {
 
 struct TBF16 {
   static constexpr int bytes = 2;
+  static constexpr bool is_f16 = false;
   static __device__ __forceinline__ float lo(uint32_t u) { return u2f(u << 16); }
   static __device__ __forceinline__ float hi(uint32_t u) { return u2f(u & 0xffff0000u); }
   static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {

@@ -296,8 +296,11 @@ int pkv_merge_states(const float* o_parts, const float* lse_parts, int32_t rows,
   if (n_parts <= 0) return fail(PKV_ERR_INVALID, "n_parts %d <= 0", n_parts);
   if (head_dim <= 0) return fail(PKV_ERR_INVALID, "head_dim %d <= 0", head_dim);
   if (int rc = check_dtype(out_dtype)) return rc;
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d: only 64 and 128 are built", head_dim);
   if (rows == 0) return ok();
   if (!o_parts || !lse_parts || !out) return fail(PKV_ERR_INVALID, "NULL pointer");
+  if (!aligned16(o_parts)) return fail(PKV_ERR_INVALID, "o_parts must be 16-byte aligned");
   return hip_status(pkv::launch_merge(out_dtype, head_dim, o_parts, lse_parts, rows, n_parts,
                                       out, lse_out, (hipStream_t)stream),
                     "merge launch");
