@@ -182,22 +182,27 @@ int pkv_merge_states(const float* o_parts, const float* lse_parts, int32_t rows,
  * chunk's K/V with pkv_kv_append first; kv_lens[b] counts history plus chunk.
  * Chunk row i of sequence b (C_b rows) sits at position kv_lens[b] - C_b + i
  * and attends to keys 0 .. that position (bottom-right aligned causal mask).
- *   q, out       : device, packed [sum_b C_b][H_q][D] of desc->dtype.
+ *   q, out       : device, packed [total_q_rows][H_q][D] of desc->dtype;
+ *                  total_q_rows = sum_b C_b.
  *   q_indptr     : device int32 [batch + 1]; rows of sequence b are
- *                  q_indptr[b] .. q_indptr[b+1]-1; q_indptr[0] = 0.
+ *                  q_indptr[b] .. q_indptr[b+1]-1; q_indptr[0] = 0.  Rows
+ *                  outside [0, total_q_rows) are never read or written.
  *   max_q_len    : host bound >= every C_b; sizes the grid.
  *   block_table, block_table_stride : as for decode.
  *   kv_lens      : device int32 [batch]; C_b <= kv_lens[b] <= stride * P.
  *   max_kv_len   : host bound >= every kv_lens[b], <= stride * P.
- *   lse_out      : device float [sum C_b][H_q] or NULL.
- * QK^T and PV run on the matrix cores; needs f16 or bf16, head_dim 128.
+ *   lse_out      : device float [total_q_rows][H_q] or NULL.
+ * QK^T and PV run on the matrix cores (MFMA, fp32 accumulation); the
+ * probabilities enter the PV product rounded to the K/V type.  Needs f16 or
+ * bf16 and head_dim 128.
  */
 int pkv_paged_attn_prefill_chunk(const pkv_cache_desc* desc, const void* k_cache,
                                  const void* v_cache, const void* q, const int32_t* q_indptr,
-                                 int32_t batch, int32_t num_q_heads, int32_t max_q_len,
-                                 const int32_t* block_table, int32_t block_table_stride,
-                                 const int32_t* kv_lens, int32_t max_kv_len, float scale,
-                                 void* out, float* lse_out, void* stream);
+                                 int32_t batch, int32_t num_q_heads, int32_t total_q_rows,
+                                 int32_t max_q_len, const int32_t* block_table,
+                                 int32_t block_table_stride, const int32_t* kv_lens,
+                                 int32_t max_kv_len, float scale, void* out, float* lse_out,
+                                 void* stream);
 
 /*
  * validate_tables -- host-side check of host copies of the tables (no HIP

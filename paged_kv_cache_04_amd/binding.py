@@ -58,8 +58,8 @@ def lib():
         L.pkv_paged_attn_decode_partials.argtypes = [dp, vp, vp, vp, i32, i32, vp, i32, vp, i32,
                                                      f32, i32, vp, sz, vp]
         L.pkv_merge_states.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
-        L.pkv_paged_attn_prefill_chunk.argtypes = [dp, vp, vp, vp, vp, i32, i32, i32, vp, i32, vp,
-                                                   i32, f32, vp, vp, vp]
+        L.pkv_paged_attn_prefill_chunk.argtypes = [dp, vp, vp, vp, vp, i32, i32, i32, i32, vp,
+                                                   i32, vp, i32, f32, vp, vp, vp]
         L.pkv_validate_tables.argtypes = [dp, vp, i32, vp, i32, vp, i32]
         for name in ("pkv_kv_append", "pkv_gather_kv", "pkv_decode_plan", "pkv_paged_attn_decode",
                      "pkv_paged_attn_decode_partials", "pkv_merge_states",
@@ -250,9 +250,11 @@ def paged_attn_prefill_chunk(q, k_cache, v_cache, q_indptr, block_table, kv_lens
         out = torch.empty_like(q)
     if return_lse and lse_out is None:
         lse_out = torch.empty((q.shape[0], hq), dtype=torch.float32, device=q.device)
+    if q.dim() != 3 or q.shape[2] != desc.head_dim:
+        raise ValueError("q must be [sum C][H_q][D]")
     _check(lib().pkv_paged_attn_prefill_chunk(
         C.byref(desc), _p(k_cache), _p(v_cache), _p(q), _p(q_indptr), batch, hq,
-        int(max_q_len), _p(block_table), int(block_table.shape[1]), _p(kv_lens),
+        int(q.shape[0]), int(max_q_len), _p(block_table), int(block_table.shape[1]), _p(kv_lens),
         int(max_kv_len), float(scale), _p(out), _p(lse_out), _stream()))
     return (out, lse_out) if return_lse else out
 

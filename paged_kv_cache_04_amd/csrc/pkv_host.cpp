@@ -308,15 +308,58 @@ int pkv_merge_states(const float* o_parts, const float* lse_parts, int32_t rows,
 
 int pkv_paged_attn_prefill_chunk(const pkv_cache_desc* desc, const void* k_cache,
                                  const void* v_cache, const void* q, const int32_t* q_indptr,
-                                 int32_t batch, int32_t num_q_heads, int32_t max_q_len,
-                                 const int32_t* block_table, int32_t block_table_stride,
-                                 const int32_t* kv_lens, int32_t max_kv_len, float scale,
-                                 void* out, float* lse_out, void* stream) {
-  (void)k_cache; (void)v_cache; (void)q; (void)q_indptr; (void)batch; (void)num_q_heads;
-  (void)max_q_len; (void)block_table; (void)block_table_stride; (void)kv_lens;
-  (void)max_kv_len; (void)scale; (void)out; (void)lse_out; (void)stream;
+                                 int32_t batch, int32_t num_q_heads, int32_t total_q_rows,
+                                 int32_t max_q_len, const int32_t* block_table,
+                                 int32_t block_table_stride, const int32_t* kv_lens,
+                                 int32_t max_kv_len, float scale, void* out, float* lse_out,
+                                 void* stream) {
   if (int rc = check_desc(desc)) return rc;
-  return fail(PKV_ERR_UNSUPPORTED, "prefill chunk not built yet");
+  int group = 0;
+  if (int rc = check_heads(desc, num_q_heads, &group)) return rc;
+  if (desc->dtype == PKV_F32)
+    return fail(PKV_ERR_UNSUPPORTED, "prefill runs on the matrix cores: f16 or bf16 only");
+  if (desc->head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "prefill is built for head_dim 128 (got %d)",
+                desc->head_dim);
+  if (batch < 0) return fail(PKV_ERR_INVALID, "batch %d < 0", batch);
+  if (total_q_rows < 0) return fail(PKV_ERR_INVALID, "total_q_rows %d < 0", total_q_rows);
+  if (max_q_len < 0) return fail(PKV_ERR_INVALID, "max_q_len %d < 0", max_q_len);
+  if (block_table_stride <= 0)
+    return fail(PKV_ERR_INVALID, "block_table_stride %d <= 0", block_table_stride);
+  if (max_kv_len < 0 || (int64_t)max_kv_len > (int64_t)block_table_stride * desc->page_size)
+    return fail(PKV_ERR_INVALID, "max_kv_len %d outside [0, stride * page_size]", max_kv_len);
+  if (max_q_len > max_kv_len)
+    return fail(PKV_ERR_INVALID, "max_q_len %d > max_kv_len %d", max_q_len, max_kv_len);
+  if (!(scale == scale)) return fail(PKV_ERR_INVALID, "scale is NaN");
+  if (batch == 0 || max_q_len == 0 || total_q_rows == 0) return ok();
+  if (!k_cache || !v_cache || !q || !q_indptr || !block_table || !kv_lens || !out)
+    return fail(PKV_ERR_INVALID, "NULL pointer");
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q) || !aligned16(out))
+    return fail(PKV_ERR_INVALID, "k_cache, v_cache, q and out must be 16-byte aligned");
+  pkv::PrefillArgs a{};
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.q = q;
+  a.q_indptr = q_indptr;
+  a.block_table = block_table;
+  a.kv_lens = kv_lens;
+  a.num_pages = desc->num_pages;
+  a.stride = block_table_stride;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.num_q_heads = num_q_heads;
+  a.batch = batch;
+  a.max_q_len = max_q_len;
+  a.total_q = total_q_rows;
+  const int rows = pkv::prefill_rows_per_tile(group);
+  a.m_tiles = (max_q_len + rows - 1) / rows;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.out = out;
+  a.lse_out = lse_out;
+  const int64_t blocks = (int64_t)batch * desc->num_kv_heads * a.m_tiles;
+  if (blocks > 0x7fffffff) return fail(PKV_ERR_INVALID, "grid too large");
+  return hip_status(pkv::launch_prefill(desc->dtype, desc->head_dim, group, a,
+                                        (hipStream_t)stream),
+                    "prefill launch");
 }
 
 int pkv_validate_tables(const pkv_cache_desc* desc, const int32_t* block_table_host,

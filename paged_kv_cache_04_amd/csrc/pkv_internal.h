@@ -44,6 +44,7 @@ struct PrefillArgs {
   int32_t num_q_heads;
   int32_t batch;
   int32_t max_q_len;
+  int64_t total_q;              // rows of q / out
   int32_t m_tiles;              // query-row tiles per (b, kv head)
   float scale_log2;
   void* out;

@@ -131,3 +131,20 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(4, 2, 16, 128, dtype=torch.bfloat16)
     with pytest.raises(TypeError):
         binding.kv_append(x, x, x[0], x[0], torch.zeros(4, dtype=torch.int32))
+
+
+def _prefill(L, d, *, batch=2, hq=4, total=10, max_q=8, stride=8, max_kv=100, q=FAKE):
+    return L.pkv_paged_attn_prefill_chunk(C.byref(d), FAKE, FAKE, q, FAKE, batch, hq, total,
+                                          max_q, FAKE, stride, FAKE, max_kv, 0.125, FAKE, None,
+                                          None)
+
+
+def test_prefill_args(L):
+    assert _prefill(L, desc(dtype=0)) == -2              # f32 is not built on MFMA
+    assert _prefill(L, desc(d=64)) == -2                 # head_dim 64 not built
+    assert _prefill(L, desc(), hq=3) == -1
+    assert _prefill(L, desc(), max_kv=8 * 16 + 1) == -1
+    assert _prefill(L, desc(), max_q=200) == -1          # longer than max_kv
+    assert _prefill(L, desc(), q=None) == -1
+    assert _prefill(L, desc(), total=-1) == -1
+    assert _prefill(L, desc(), batch=0) == 0
