@@ -13,24 +13,27 @@
 // (sequence, KV head): 128 / G chunk positions times the G query heads that
 // share the KV head (page 4, section 2.2, GQA), so the G heads reuse every
 // K/V tile.  Wave w owns rows 32w .. 32w+31.  Keys go in tiles of 64 (four
-// pages), double-buffered in LDS: while the waves compute on one buffer, the
-// next tile's pages are loaded into registers and then written to the other.
+// pages) through two LDS buffers: while the waves compute on one, direct
+// global-to-LDS loads (no registers) fill the other with the next tile.
+//
+// LDS layout: K and V tiles are stored as they sit in the pages, one 256-byte
+// row per key, with the sixteen 16-byte chunks of row r permuted by
+// chunk ^ swz(r) so that the operand reads below hit distinct banks.
 //
 // Per tile and wave, on 32x32x16 MFMAs with fp32 accumulation:
-//   S^T (64 keys x 32 rows) = K (from LDS) x Q^T (registers); the scores of a
-//       query row sit in one lane (16 per 32-key block, the other half of the
-//       block in lane + 32), so the row max is an in-lane max and one
-//       exchange.
-//   online softmax in base 2 (log2 e folded into the scale), rescaling the
-//       accumulators only when some row's running max grew (wave vote).
-//   O^T (128 x 32) += V^T (from LDS) x P^T: the probabilities are converted in
-//       place to bf16/f16; the 32x32 output layout of S^T is already the
-//       operand layout P^T needs, given that the V^T operand takes its keys
-//       in the same order.  V is written to LDS transposed (key pairs packed
-//       with v_perm), K as rows; rows are padded against bank conflicts.
-// Keys past the causal limit or the sequence end are selected out of S; K and
-// V slots past the sequence end are zero-filled in LDS, so stale or NaN slots
-// in a partly filled last page never leak into the products.
+//   S^T (64 keys x 32 rows) = K x Q^T: K rows are read as 16-byte chunks, Q^T
+//       stays in registers.  The scores of a query row sit in one lane (16 per
+//       32-key block, the other 16 in lane + 32): the row max is an in-lane
+//       max and one exchange.
+//   online softmax in base 2 (log2 e folded into the scale); accumulators are
+//       rescaled only when some row's running max grew (wave vote).
+//   O^T (128 x 32) += V^T x P^T: the probabilities are converted in place to
+//       bf16/f16 (the S^T output layout is the P^T operand layout), and the
+//       V^T operand comes from transposing LDS reads (ds_read_b64_tr_b16) of
+//       the row-major V tile, with keys taken in the order P^T holds them.
+// Keys past the causal limit or the sequence end are selected out of S; V
+// rows past the sequence end are zeroed in LDS before use, so stale or NaN
+// slots in a partly filled last page never reach the products.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -39,17 +42,22 @@ namespace pkv {
 namespace {
 
 constexpr int P = kPageSize;
-constexpr int D = 128;          // head_dim of the MFMA kernel
-constexpr int BK = 64;          // keys per tile (4 pages)
-constexpr int NWP = 4;          // waves per workgroup
-constexpr int ROWS = 128;       // query rows per workgroup
-constexpr int KLD = D + 8;      // K tile row stride in elements (272 bytes)
-constexpr int VLD = BK + 4;     // V^T tile row stride in elements (136 bytes)
+constexpr int D = 128;           // head_dim of the MFMA kernel
+constexpr int BK = 64;           // keys per tile (4 pages)
+constexpr int NWP = 4;           // waves per workgroup
+constexpr int ROWS = 128;        // query rows per workgroup
+constexpr int ROWB = D * 2;      // bytes per key row (256)
+constexpr int TILEB = BK * ROWB; // bytes per K or V tile (16 KiB)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef uint8_t __attribute__((address_space(3))) lds_u8;
 
 template <typename TT>
 struct Mfma;
@@ -62,7 +70,8 @@ struct Mfma<TBF16> {
                                                    0);
   }
   static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
-    return (uint32_t)TBF16::from_float(lo) | ((uint32_t)TBF16::from_float(hi) << 16);
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));  // RNE
   }
   static constexpr float POFF = 0.f;
 };
@@ -74,24 +83,38 @@ struct Mfma<TF16> {
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
   }
   static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
-    return (uint32_t)TF16::from_float(lo) | ((uint32_t)TF16::from_float(hi) << 16);
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));  // RNE
   }
   // f16 probabilities are carried as p * 2^15 so small weights keep precision
   static constexpr float POFF = 15.f;
 };
 
-// Registers holding one tile's K and V loads before they go to LDS.
-struct TileRegs {
-  u32x4 k[4];   // K: thread t holds token t/16 of each of the 4 pages, vector t%16
-  u32x4 v[4];   // V: two (key pair, 8-element column) tasks, two rows each
-};
+// Chunk permutation of key row r: 16 distinct values over 16 consecutive rows,
+// and it maps 16-byte chunk pairs (2j, 2j+1) onto chunk pairs.
+__device__ __forceinline__ int swz(int r) { return 2 * (r & 7) + ((r >> 3) & 1); }
+
+// Direct global-to-LDS copy: lane i's 16 bytes go to lds_base + 16 * i.
+__device__ __forceinline__ void dma16(const void* gsrc, lds_u8* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, lds_base, 16, 0, 0);
+}
+
+// Transposing LDS read: in each group of 16 lanes, lane i receives element
+// i % 4 of the 8-byte chunks addressed by lanes 4k + i / 4, k = 0..3.
+__device__ __forceinline__ uint2 read_tr(const lds_u8* p) {
+  const i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (i16x4_t __attribute__((address_space(3)))*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
 
 template <typename TT, int G>
 __global__ __launch_bounds__(NWP * 64, 2) void prefill_kernel(PrefillArgs a) {
   using M = Mfma<TT>;
   constexpr int NPOS = ROWS / G;  // chunk positions per workgroup
-  __shared__ __align__(16) uint16_t k_lds[2][BK * KLD];
-  __shared__ __align__(16) uint16_t v_lds[2][D * VLD];
+  __shared__ __align__(1024) uint8_t k_lds0[TILEB];
+  __shared__ __align__(1024) uint8_t k_lds1[TILEB];
+  __shared__ __align__(1024) uint8_t v_lds0[TILEB];
+  __shared__ __align__(1024) uint8_t v_lds1[TILEB];
   __shared__ int bad_flag;
 
   const int tid = threadIdx.x;
@@ -147,77 +170,41 @@ __global__ __launch_bounds__(NWP * 64, 2) void prefill_kernel(PrefillArgs a) {
       for (int e = 0; e < 4; ++e) qreg[ks][e] = neg ? (x.w[e] ^ 0x80008000u) : x.w[e];
     }
   }
-  const float c = fabsf(a.scale_log2);
+  // scale in log2 units; kept >= 1e-30 so that a masked score (-inf) times it
+  // stays -inf (a zero scale would give NaN; 1e-30 changes no result)
+  const float c = fmaxf(fabsf(a.scale_log2), 1e-30f);
 
   if (tid == 0) bad_flag = bad ? 1 : 0;
 
-  // ---- staging: global pages -> registers -> LDS
+  // ---- staging: wave w copies page w of the tile (key rows 16w .. 16w+15)
+  // of K and V as four 1-KiB LDS chunks of four rows; lane i of a chunk fills
+  // row 4j + i/16, physical chunk i%16 with logical chunk (i%16) ^ swz(row).
   const int64_t head_block = (int64_t)P * D * 2;
   bool my_bad = false;
-  auto page_of = [&](int pi) -> int64_t {  // physical page of logical page pi (or -1)
-    if (pi >= seq_pages) return -1;
-    int pid = bt_row[pi];
-    if (pid < 0 || pid >= a.num_pages) {
-      my_bad = true;
-      return -1;
-    }
-    return pid;
-  };
-  auto load_tile = [&](TileRegs& r, int it) {
-    const int pg0 = it * (BK / P);
-    int64_t pids[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) pids[j] = page_of(pg0 + j);   // uniform: scalar loads
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {  // K: page j, token tid/16, vector tid%16
-      const int tok = tid >> 4, vec = tid & 15;
-      const int key = it * BK + j * P + tok;
-      if (pids[j] >= 0 && key < kvl) {
-        r.k[j] = load16((const char*)a.k_cache + (pids[j] * a.num_kv_heads + g) * head_block +
-                        (tok * D + vec * 8) * 2);
-      } else {
-        r.k[j].w[0] = r.k[j].w[1] = r.k[j].w[2] = r.k[j].w[3] = 0u;
-      }
-    }
-#pragma unroll
-    for (int j2 = 0; j2 < 2; ++j2) {  // V: keys 2kp, 2kp+1; 8 columns from 8*dv
-      const int task = tid + 256 * j2;
-      const int kp = task & 31, dv = task >> 5;
-      const int key = 2 * kp;                      // within the tile
-      const int pj = key / P;
-      const int64_t pid = pj == 0 ? pids[0] : pj == 1 ? pids[1] : pj == 2 ? pids[2] : pids[3];
-      const int tok = key % P;
-      const char* src = (const char*)a.v_cache +
-                        (pid < 0 ? 0 : (pid * a.num_kv_heads + g)) * head_block +
-                        (tok * D + dv * 8) * 2;
-      const int kabs = it * BK + key;
-      u32x4 z;
-      z.w[0] = z.w[1] = z.w[2] = z.w[3] = 0u;
-      r.v[2 * j2] = (pid >= 0 && kabs < kvl) ? load16(src) : z;
-      r.v[2 * j2 + 1] = (pid >= 0 && kabs + 1 < kvl) ? load16(src + D * 2) : z;
-    }
-  };
-  auto store_tile = [&](const TileRegs& r, int buf) {
+  auto issue_tile = [&](int it, lds_u8* kdst, lds_u8* vdst) {
+    const int pi = it * (BK / P) + w;
+    int pid = pi < seq_pages ? bt_row[pi] : 0;
+    if (pi < seq_pages && (pid < 0 || pid >= a.num_pages)) my_bad = true;
+    if (pid < 0 || pid >= a.num_pages) pid = 0;   // always a readable page
+    const int64_t base = ((int64_t)pid * a.num_kv_heads + g) * head_block;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int key = j * P + (tid >> 4);
-      store16(&k_lds[buf][key * KLD + (tid & 15) * 8], r.k[j]);
+      const int r = 16 * w + 4 * j + (lane >> 4);    // key row within the tile
+      const int tok = r % P;
+      const int lc = (lane & 15) ^ swz(r);           // logical 16-byte chunk
+      const int64_t off = base + tok * ROWB + lc * 16;
+      dma16((const char*)a.k_cache + off, kdst + (16 * w + 4 * j) * ROWB);
+      dma16((const char*)a.v_cache + off, vdst + (16 * w + 4 * j) * ROWB);
     }
-#pragma unroll
-    for (int j2 = 0; j2 < 2; ++j2) {
-      const int task = tid + 256 * j2;
-      const int kp = task & 31, dv = task >> 5;
-      uint32_t* vt = reinterpret_cast<uint32_t*>(&v_lds[buf][0]);
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const uint32_t x0 = r.v[2 * j2].w[e2], x1 = r.v[2 * j2 + 1].w[e2];
-        // column d = 8dv + 2e2 (low halves) and d + 1 (high halves): (key 2kp, key 2kp+1)
-        const uint32_t lo = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
-        const uint32_t hi = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
-        const int d = 8 * dv + 2 * e2;
-        vt[(d * VLD) / 2 + kp] = lo;
-        vt[((d + 1) * VLD) / 2 + kp] = hi;
-      }
+  };
+  // V rows of keys past the sequence end become zero (edge tiles only)
+  auto zero_tail = [&](int it, uint8_t* vdst) {
+    const int first = kvl - it * BK;   // first row to clear
+    for (int idx = tid; idx < BK * (ROWB / 16); idx += NWP * 64) {
+      const int r = idx / (ROWB / 16);
+      if (r >= first)
+        *reinterpret_cast<uint4*>(vdst + r * ROWB + (idx % (ROWB / 16)) * 16) =
+            make_uint4(0u, 0u, 0u, 0u);
     }
   };
 
@@ -230,48 +217,9 @@ __global__ __launch_bounds__(NWP * 64, 2) void prefill_kernel(PrefillArgs a) {
   float m_run = -INFINITY;  // running max of the raw (unscaled) scores of this row
   float l_run = 0.f;        // running sum of exp2(c * s - c * m_run) over this lane's keys
 
-  TileRegs tr;
-  load_tile(tr, 0);
-  store_tile(tr, 0);
-  __syncthreads();
-
-  for (int it = 0; it < n_tiles; ++it) {
-    const int buf = it & 1;
-    const bool more = it + 1 < n_tiles;
-    if (more) load_tile(tr, it + 1);
-
-    // S^T = K Q^T for two 32-key blocks
-    f32x16_t s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-    const uint16_t* kt = k_lds[buf];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const u32x4_t av =
-            *reinterpret_cast<const u32x4_t*>(kt + (32 * kb + n) * KLD + 16 * ks + 8 * half);
-        s[kb] = M::run(av, qreg[ks], s[kb]);
-      }
-    }
-
-    // keys past this row's position (or the sequence end) are selected out
-    const int t0 = it * BK;
-    const bool masked = t0 + BK - 1 > hist + pos0;
-    auto visible = [&](int kb, int i) {
-      const int t = t0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
-      return t <= apos && t < kvl;
-    };
-    if (masked) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = visible(kb, i) ? s[kb][i] : -INFINITY;
-    }
-
-    // running max (raw units; c >= 0)
+  // Online-softmax update for one tile: running max, rescale, probabilities
+  // packed as the B operands of the PV MFMA (k-step ks = keys 16ks..16ks+15).
+  auto softmax_tile = [&](f32x16_t (&s)[2], u32x4_t (&pk)[4]) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -289,9 +237,6 @@ __global__ __launch_bounds__(NWP * 64, 2) void prefill_kernel(PrefillArgs a) {
       m_run = m_new;
     }
     const float mc = (m_run == -INFINITY) ? 0.f : m_run * c - M::POFF;
-
-    // probabilities -> packed B operands of the PV MFMA (k-step ks = keys 16ks..16ks+15)
-    u32x4_t pk[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -299,24 +244,58 @@ __global__ __launch_bounds__(NWP * 64, 2) void prefill_kernel(PrefillArgs a) {
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float pe = exp2_fast(fmaf(s[kb][8 * sub + e], c, -mc));
-          p[e] = (masked && !visible(kb, 8 * sub + e)) ? 0.f : pe;
+          p[e] = exp2_fast(fmaf(s[kb][8 * sub + e], c, -mc));   // masked: exp2(-inf) = 0
           l_run += p[e];
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) pk[2 * kb + sub][e] = M::pack(p[2 * e], p[2 * e + 1]);
       }
+  };
 
-    // O^T += V^T P^T
-    const uint16_t* vt = v_lds[buf];
+  // One tile from LDS buffers (kt, vt).
+  auto compute_tile = [&](int it, const lds_u8* kt, const lds_u8* vt) {
+    // S^T = K Q^T for two 32-key blocks
+    f32x16_t s[2];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int r = 32 * kb + n;
+        const u32x4_t av = *reinterpret_cast<const u32x4_t __attribute__((address_space(3)))*>(
+            kt + r * ROWB + (((2 * ks + half) ^ swz(r)) * 16));
+        s[kb] = M::run(av, qreg[ks], ks == 0 ? f32x16_t{} : s[kb]);
+      }
+    }
+    // keys past this row's position (or the sequence end) are selected out:
+    // score i of block kb is key t0 + 32kb + 8(i/4) + 4half + i%4
+    const int t0 = it * BK;
+    if (t0 + BK - 1 > hist + pos0) {
+      const int thr = min(apos, kvl - 1) - t0 - 4 * half;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          s[kb][i] = (32 * kb + 8 * (i >> 2) + (i & 3) <= thr) ? s[kb][i] : -INFINITY;
+    }
+    u32x4_t pk[4];
+    softmax_tile(s, pk);
+
+    // O^T += V^T P^T.  The 16-lane group q16 = lane / 16 covers head dims
+    // 32db + 16 (q16 & 1) .. +15 with key half h = q16 >> 1; source lane
+    // 4k + j of the group points at key (16ks + 4h + k) (+8 for slots 4..7),
+    // dims +4j .. +4j+3, so result lane i holds dim +i for keys k = 0..3.
+    const int q16 = lane >> 4, li = lane & 15;
+    const int kk = li >> 2, jj = li & 3;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int koff = 16 * ks + 4 * half;  // keys koff..koff+3 and koff+8..koff+11
+      const int key_a = 16 * ks + 4 * (q16 >> 1) + kk;   // slots e = 0..3
+      const int key_b = key_a + 8;                       // slots e = 4..7
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const uint16_t* rowp = vt + (32 * db + n) * VLD + koff;
-        const uint2 lo = *reinterpret_cast<const uint2*>(rowp);
-        const uint2 hi = *reinterpret_cast<const uint2*>(rowp + 8);
+        const int dcol = 32 * db + 16 * (q16 & 1) + 4 * jj;   // first of 4 dims
+        const int lc = dcol >> 3, sub8 = (dcol & 7) * 2;      // chunk, byte in chunk
+        const uint2 lo = read_tr(vt + key_a * ROWB + ((lc ^ swz(key_a)) * 16) + sub8);
+        const uint2 hi = read_tr(vt + key_b * ROWB + ((lc ^ swz(key_b)) * 16) + sub8);
         u32x4_t av;
         av[0] = lo.x;
         av[1] = lo.y;
@@ -325,8 +304,35 @@ __global__ __launch_bounds__(NWP * 64, 2) void prefill_kernel(PrefillArgs a) {
         o[db] = M::run(av, pk[ks], o[db]);
       }
     }
+  };
 
-    if (more) store_tile(tr, buf ^ 1);
+  lds_u8* kb0 = (lds_u8*)k_lds0;
+  lds_u8* kb1 = (lds_u8*)k_lds1;
+  lds_u8* vb0 = (lds_u8*)v_lds0;
+  lds_u8* vb1 = (lds_u8*)v_lds1;
+
+  issue_tile(0, kb0, vb0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int it = 0; it < n_tiles; it += 2) {
+    // tile it from buffer 0 while tile it+1 loads into buffer 1
+    if (it * BK + BK > kvl) {
+      zero_tail(it, v_lds0);
+      __syncthreads();
+    }
+    if (it + 1 < n_tiles) issue_tile(it + 1, kb1, vb1);
+    compute_tile(it, kb0, vb0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (it + 1 >= n_tiles) break;
+    // tile it+1 from buffer 1 while tile it+2 loads into buffer 0
+    if ((it + 1) * BK + BK > kvl) {
+      zero_tail(it + 1, v_lds1);
+      __syncthreads();
+    }
+    if (it + 2 < n_tiles) issue_tile(it + 2, kb0, vb0);
+    compute_tile(it + 1, kb1, vb1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
