@@ -242,13 +242,14 @@ def main():
 
 
 def _kernel_sha() -> str:
+    """Hash of the sources the partial-decode kernel is built from; a stored
+    traffic figure is reported only while it matches."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_04_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(f.read())
+    for name in ("decode.hip", "pkv_device.h", "pkv_internal.h"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
