@@ -17,7 +17,7 @@
 // w, w+4, w+8, ... of the split.  Each wave keeps its own (m, l, acc) state;
 // the four are combined through LDS at the end.  Every wave keeps the loads
 // of its next two pages in flight while it computes the current one (three
-// register buffers).
+// register buffers).  K/V are read once, with streaming (non-temporal) loads.
 //
 // Per page (16 tokens x D elements, one contiguous 2-8 KiB block per head):
 //   K, "row layout": 8 lanes per token, 8 tokens per pass, 2 passes; lane c of
@@ -249,16 +249,16 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeArgs a) {
     for (int rr = 0; rr < C::KP; ++rr)
 #pragma unroll
       for (int v = 0; v < C::KV; ++v)
-        r.k[rr][v] = load16(kb + ((tk + C::KT * rr) * D + v * C::KL * VEC + c * VEC) * ES);
+        r.k[rr][v] = load16_stream(kb + ((tk + C::KT * rr) * D + v * C::KL * VEC + c * VEC) * ES);
 #pragma unroll
     for (int j = 0; j < C::VT; ++j) {
       const char* src = vb + ((tg + C::TG * j) * D + dg * C::VE) * ES;
       if constexpr (C::VW == 2) {
-        const u32x2 x = load8(src);
+        const u32x2 x = load8_stream(src);
         r.v[j][0] = x.w[0];
         r.v[j][1] = x.w[1];
       } else {
-        const u32x4 x = load16(src);
+        const u32x4 x = load16_stream(src);
 #pragma unroll
         for (int e = 0; e < 4; ++e) r.v[j][e] = x.w[e];
       }

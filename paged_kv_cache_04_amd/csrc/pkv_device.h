@@ -37,6 +37,29 @@ __device__ __forceinline__ u32x2 load8(const void* p) {
   return r;
 }
 
+// Streaming (non-temporal) loads: data read exactly once is not kept in the
+// caches, which leaves L2 and the Infinity Cache to the data that is reused.
+typedef uint32_t u32v4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32v2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x4 load16_stream(const void* p) {
+  const u32v4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32v4_t*>(p));
+  u32x4 r;
+  r.w[0] = v[0];
+  r.w[1] = v[1];
+  r.w[2] = v[2];
+  r.w[3] = v[3];
+  return r;
+}
+
+__device__ __forceinline__ u32x2 load8_stream(const void* p) {
+  const u32v2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32v2_t*>(p));
+  u32x2 r;
+  r.w[0] = v[0];
+  r.w[1] = v[1];
+  return r;
+}
+
 __device__ __forceinline__ void store16(void* p, const u32x4& r) {
   uint4 v;
   v.x = r.w[0];

@@ -73,8 +73,9 @@ int hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
-// Decode split plan.  Auto rule: aim for about 1024 workgroups (four per CU
-// on a 256-CU device) and never less than 16 pages (256 keys) per split.
+// Decode split plan.  Auto rule: aim for about 512 workgroups (two per CU
+// on a 256-CU device, one round of residency) and never less than 16 pages
+// (256 keys) per split.
 struct Plan {
   int32_t n_split;
   int32_t pages_per_split;
@@ -82,7 +83,7 @@ struct Plan {
   size_t ws_bytes;     // o_bytes + lse bytes
 };
 
-constexpr int64_t kTargetWorkgroups = 1024;
+constexpr int64_t kTargetWorkgroups = 512;
 constexpr int32_t kMinSplitPages = 16;
 
 int make_plan(const pkv_cache_desc* d, int32_t batch, int32_t num_q_heads,

@@ -86,7 +86,7 @@ def test_decode_workspace_required_when_split(L):
 
 
 @pytest.mark.parametrize("name,batch,hq,hkv,max_len,want_split", [
-    ("llama70b_128k", 8, 16, 2, 131072, 64),
+    ("llama70b_128k", 8, 16, 2, 131072, 32),
     ("tiny", 4, 8, 8, 511, 2),
     ("prefix", 256, 32, 8, 2560, 1),
 ])
