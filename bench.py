@@ -127,16 +127,23 @@ def main():
     lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=dev)
     dargs = (q, kc, vc, bt, cl, w.max_context_len, w.scale)
 
+    # one call to each entry point per step, arguments marshalled once
+    o_parts, l_parts, _ = pkv.paged_attn_decode_partials(
+        *dargs, split_tokens=args.split_tokens, workspace=workspace)
+    call_append = (pkv.binding.prepare_kv_append(kc, vc, k_new, v_new, slots)
+                   if has_append else None)
+    call_partials = pkv.binding.prepare_decode_partials(*dargs, args.split_tokens, workspace)
+    call_merge = pkv.binding.prepare_merge_states(o_parts, l_parts, out, lse)
+
     def step(ev=None):
-        if has_append:
-            pkv.kv_append(kc, vc, k_new, v_new, slots)
+        if call_append is not None:
+            call_append()
         if ev is not None:
             ev[0].record()
-        o_parts, l_parts, _ = pkv.paged_attn_decode_partials(
-            *dargs, split_tokens=args.split_tokens, workspace=workspace)
+        call_partials()
         if ev is not None:
             ev[1].record()
-        pkv.merge_states(o_parts, l_parts, out_dtype=q.dtype, out=out, lse_out=lse)
+        call_merge()
 
     for _ in range(args.warmup):
         step()

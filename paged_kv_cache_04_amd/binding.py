@@ -267,3 +267,56 @@ def validate_tables(desc: CacheDesc, block_table, lens, slots=None) -> None:
     _check(lib().pkv_validate_tables(C.byref(desc), _p(bt), int(bt.shape[1]) if bt.dim() == 2 else 0,
                                      _p(ln), int(ln.shape[0]), _p(sl),
                                      0 if sl is None else int(sl.shape[0])))
+
+
+class PreparedCall:
+    """A library call with its arguments marshalled once (device pointers,
+    sizes and the stream current at preparation).  Calling it performs only
+    the C call; the tensors must stay alive and unchanged in shape."""
+
+    def __init__(self, fn, args, keep):
+        self._fn = fn
+        self._args = args
+        self._keep = keep          # tensors whose storage the pointers refer to
+
+    def __call__(self) -> None:
+        rc = self._fn(*self._args)
+        if rc != 0:
+            _check(rc)
+
+
+def prepare_kv_append(k_cache, v_cache, k_new, v_new, slots) -> PreparedCall:
+    desc = _check_pools(k_cache, v_cache)
+    _dev(k_new, "k_new", k_cache.dtype)
+    _dev(v_new, "v_new", k_cache.dtype)
+    _dev(slots, "slots", torch.int32)
+    n = int(slots.shape[0])
+    if k_new.shape != (n, desc.num_kv_heads, desc.head_dim) or v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new must be [n][H_kv][D]")
+    args = (C.byref(desc), _p(k_cache), _p(v_cache), _p(k_new), _p(v_new), _p(slots), n,
+            _stream())
+    return PreparedCall(lib().pkv_kv_append, args, (desc, k_cache, v_cache, k_new, v_new, slots))
+
+
+def prepare_decode_partials(q, k_cache, v_cache, block_table, context_lens,
+                            max_context_len: int, scale: float, split_tokens: int,
+                            workspace) -> PreparedCall:
+    desc, batch, hq = _decode_common(q, k_cache, v_cache, block_table, context_lens,
+                                     max_context_len)
+    _dev(workspace, "workspace")
+    ws_len = workspace.numel() * workspace.element_size()
+    args = (C.byref(desc), _p(k_cache), _p(v_cache), _p(q), batch, hq, _p(block_table),
+            int(block_table.shape[1]), _p(context_lens), int(max_context_len), float(scale),
+            int(split_tokens), _p(workspace), ws_len, _stream())
+    return PreparedCall(lib().pkv_paged_attn_decode_partials, args,
+                        (desc, q, k_cache, v_cache, block_table, context_lens, workspace))
+
+
+def prepare_merge_states(o_parts, lse_parts, out, lse_out=None) -> PreparedCall:
+    _dev(o_parts, "o_parts", torch.float32)
+    _dev(lse_parts, "lse_parts", torch.float32)
+    _dev(out, "out")
+    rows, n, d = (int(x) for x in o_parts.shape)
+    args = (_p(o_parts), _p(lse_parts), rows, n, d, _TORCH_TO_CODE[out.dtype], _p(out),
+            _p(lse_out), _stream())
+    return PreparedCall(lib().pkv_merge_states, args, (o_parts, lse_parts, out, lse_out))

@@ -25,8 +25,9 @@
 //       stays in registers.  The scores of a query row sit in one lane (16 per
 //       32-key block, the other 16 in lane + 32): the row max is an in-lane
 //       max and one exchange.
-//   online softmax in base 2 (log2 e folded into the scale); accumulators are
-//       rescaled only when some row's running max grew (wave vote).
+//   online softmax in base 2 (log2 e folded into the scale); the reference
+//       max of a row moves only when a score exceeds it by more than 8 (in
+//       log2 units), so the accumulators are rescaled rarely (wave vote).
 //   O^T (128 x 32) += V^T x P^T: the probabilities are converted in place to
 //       bf16/f16 (the S^T output layout is the P^T operand layout), and the
 //       V^T operand comes from transposing LDS reads (ds_read_b64_tr_b16) of
@@ -48,6 +49,7 @@ constexpr int NWP = 4;           // waves per workgroup
 constexpr int ROWS = 128;        // query rows per workgroup
 constexpr int ROWB = D * 2;      // bytes per key row (256)
 constexpr int TILEB = BK * ROWB; // bytes per K or V tile (16 KiB)
+constexpr float kLazyLog2 = 8.f; // rescale when a row max grows by > 2^8
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -58,6 +60,11 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef uint8_t __attribute__((address_space(3))) lds_u8;
+
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
 
 template <typename TT>
 struct Mfma;
@@ -86,13 +93,18 @@ struct Mfma<TF16> {
     const f32x2_t v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));  // RNE
   }
-  // f16 probabilities are carried as p * 2^15 so small weights keep precision
-  static constexpr float POFF = 15.f;
+  // f16 probabilities are carried as p * 2^7 (p <= 2^8, so <= 2^15 < 65504)
+  // so that small weights keep their precision
+  static constexpr float POFF = 7.f;
 };
 
-// Chunk permutation of key row r: 16 distinct values over 16 consecutive rows,
-// and it maps 16-byte chunk pairs (2j, 2j+1) onto chunk pairs.
-__device__ __forceinline__ int swz(int r) { return 2 * (r & 7) + ((r >> 3) & 1); }
+// Chunk permutation of key row r (physical chunk = logical chunk ^ swz(r)),
+// for 64 LDS banks (256 bytes per cycle).  It is a bijection on r % 16, so
+// the K operand reads of 16 consecutive rows at one logical chunk hit all 16
+// chunk positions; and it puts r % 4 into chunk bits 2-3 and r / 4 % 4 into
+// bits 0-1, so the transposing V reads of 32 lanes (4 keys x two adjacent
+// 32-byte chunk pairs) cover 8 distinct chunk pairs.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 // Direct global-to-LDS copy: lane i's 16 bytes go to lds_base + 16 * i.
 __device__ __forceinline__ void dma16(const void* gsrc, lds_u8* lds_base) {
@@ -226,8 +238,13 @@ __global__ __launch_bounds__(NWP * 64, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
     mx = fmaxf(mx, xor_f(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    if (__ballot(m_new > m_run) != 0) {
+    // The reference max moves only when a row's max exceeds it by more than
+    // 2^8 in probability, so the accumulators are rarely rescaled; every
+    // probability stays <= 2^8 (times the f16 offset 2^POFF <= 2^15).
+    const bool grow = (m_run == -INFINITY) ? (mx > -INFINITY) : ((mx - m_run) * c > kLazyLog2);
+    if (__ballot(grow) != 0) {
+      __asm__ volatile("");   // keep this a branch: the rescale is rare
+      const float m_new = grow ? mx : m_run;
       const float alpha = (m_run == -INFINITY) ? 0.f : exp2_fast((m_run - m_new) * c);
       l_run *= alpha;
 #pragma unroll
@@ -252,24 +269,44 @@ __global__ __launch_bounds__(NWP * 64, 2) void prefill_kernel(PrefillArgs a) {
       }
   };
 
-  // One tile from LDS buffers (kt, vt).
-  auto compute_tile = [&](int it, const lds_u8* kt, const lds_u8* vt) {
+  // Per-lane LDS byte offsets, the same for every tile: the K operand of
+  // k-step ks (row n, logical chunk 2ks + half) and the V^T operand reads of
+  // head-dim block db for key slots 0..3 (a) and 4..7 (b) at k-step 0.
+  int k_off[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) k_off[ks] = n * ROWB + (((2 * ks + half) ^ swz(n)) * 16);
+  const int q16 = lane >> 4, li = lane & 15;
+  const int kk = li >> 2, jj = li & 3;
+  const int key_a0 = 4 * (q16 >> 1) + kk;      // key of slots 0..3 at k-step 0
+  int va_off[4], vb_off[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int dcol = 32 * db + 16 * (q16 & 1) + 4 * jj;   // first of 4 head dims
+    const int lc = dcol >> 3, sub8 = (dcol & 7) * 2;      // chunk, byte in chunk
+    va_off[db] = key_a0 * ROWB + ((lc ^ swz(key_a0)) * 16) + sub8;
+    vb_off[db] = (key_a0 + 8) * ROWB + ((lc ^ swz(key_a0 + 8)) * 16) + sub8;
+  }
+
+  // One tile from LDS buffers (kt, vt); MASKED tiles are the few that reach
+  // past some row's causal limit or the sequence end.
+  auto compute_tile = [&](int it, const lds_u8* kt, const lds_u8* vt, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     // S^T = K Q^T for two 32-key blocks
     f32x16_t s[2];
+    const f32x16_t zero16 = {};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int r = 32 * kb + n;
         const u32x4_t av = *reinterpret_cast<const u32x4_t __attribute__((address_space(3)))*>(
-            kt + r * ROWB + (((2 * ks + half) ^ swz(r)) * 16));
-        s[kb] = M::run(av, qreg[ks], ks == 0 ? f32x16_t{} : s[kb]);
+            kt + kb * 32 * ROWB + k_off[ks]);
+        s[kb] = M::run(av, qreg[ks], ks == 0 ? zero16 : s[kb]);
       }
     }
     // keys past this row's position (or the sequence end) are selected out:
     // score i of block kb is key t0 + 32kb + 8(i/4) + 4half + i%4
     const int t0 = it * BK;
-    if (t0 + BK - 1 > hist + pos0) {
+    if constexpr (MASKED) {
       const int thr = min(apos, kvl - 1) - t0 - 4 * half;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -284,18 +321,14 @@ __global__ __launch_bounds__(NWP * 64, 2) void prefill_kernel(PrefillArgs a) {
     // 32db + 16 (q16 & 1) .. +15 with key half h = q16 >> 1; source lane
     // 4k + j of the group points at key (16ks + 4h + k) (+8 for slots 4..7),
     // dims +4j .. +4j+3, so result lane i holds dim +i for keys k = 0..3.
-    const int q16 = lane >> 4, li = lane & 15;
-    const int kk = li >> 2, jj = li & 3;
+    // The swizzle of key 16ks + x equals that of key x, so k-step ks only
+    // adds 16 rows to the k-step 0 offsets.
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int key_a = 16 * ks + 4 * (q16 >> 1) + kk;   // slots e = 0..3
-      const int key_b = key_a + 8;                       // slots e = 4..7
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const int dcol = 32 * db + 16 * (q16 & 1) + 4 * jj;   // first of 4 dims
-        const int lc = dcol >> 3, sub8 = (dcol & 7) * 2;      // chunk, byte in chunk
-        const uint2 lo = read_tr(vt + key_a * ROWB + ((lc ^ swz(key_a)) * 16) + sub8);
-        const uint2 hi = read_tr(vt + key_b * ROWB + ((lc ^ swz(key_b)) * 16) + sub8);
+        const uint2 lo = read_tr(vt + ks * 16 * ROWB + va_off[db]);
+        const uint2 hi = read_tr(vt + ks * 16 * ROWB + vb_off[db]);
         u32x4_t av;
         av[0] = lo.x;
         av[1] = lo.y;
@@ -311,30 +344,42 @@ __global__ __launch_bounds__(NWP * 64, 2) void prefill_kernel(PrefillArgs a) {
   lds_u8* vb0 = (lds_u8*)v_lds0;
   lds_u8* vb1 = (lds_u8*)v_lds1;
 
+  // Tile it computes from buffer it % 2 while tile it + 1 loads into the
+  // other one.  Tiles [0, n_full) lie wholly below every row's causal limit
+  // (and inside the sequence); only the rest need the mask and the tail fill.
+  auto run_tile = [&](int it, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const bool odd = (it & 1) != 0;
+    if (MASKED && it * BK + BK > kvl) {
+      zero_tail(it, odd ? v_lds1 : v_lds0);
+      __syncthreads();
+    }
+    if (it + 1 < n_tiles) issue_tile(it + 1, odd ? kb0 : kb1, odd ? vb0 : vb1);
+    compute_tile(it, odd ? kb1 : kb0, odd ? vb1 : vb0, masked_tag);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  const int n_full = min(n_tiles, (hist + pos0 + 1) / BK);
+
   issue_tile(0, kb0, vb0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int it = 0; it < n_tiles; it += 2) {
-    // tile it from buffer 0 while tile it+1 loads into buffer 1
-    if (it * BK + BK > kvl) {
-      zero_tail(it, v_lds0);
-      __syncthreads();
-    }
-    if (it + 1 < n_tiles) issue_tile(it + 1, kb1, vb1);
-    compute_tile(it, kb0, vb0);
+  // Unmasked tiles in pairs, so that each half names its LDS buffers at
+  // compile time (which lets the compiler see that the reads of one buffer
+  // never wait for the copy into the other).
+  int it = 0;
+  for (; it + 1 < n_full; it += 2) {
+    issue_tile(it + 1, kb1, vb1);
+    compute_tile(it, kb0, vb0, BoolTag<false>{});
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (it + 1 >= n_tiles) break;
-    // tile it+1 from buffer 1 while tile it+2 loads into buffer 0
-    if ((it + 1) * BK + BK > kvl) {
-      zero_tail(it + 1, v_lds1);
-      __syncthreads();
-    }
     if (it + 2 < n_tiles) issue_tile(it + 2, kb0, vb0);
-    compute_tile(it + 1, kb1, vb1);
+    compute_tile(it + 1, kb1, vb1, BoolTag<false>{});
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
+  for (; it < n_full; ++it) run_tile(it, BoolTag<false>{});
+  for (; it < n_tiles; ++it) run_tile(it, BoolTag<true>{});
 
   // ---- epilogue
   if (my_bad) bad_flag = 1;

@@ -253,3 +253,30 @@ def test_bad_page_id_and_length_poison_only_their_row():
         assert torch.isfinite(out[0].float()).all()
         for b in (1, 2, 3):
             assert torch.isnan(out[b].float()).all(), (split, b)
+
+
+def test_prepared_calls_match_regular_calls():
+    """The pre-marshalled calls the benchmark uses give bit-identical results."""
+    w = W.make_decode("prep", seed=16, batch=4, hq=16, hkv=2, d=128, dtype="f16",
+                      hist_lens=[3000, 17, 900, 4100], append=True)
+    d = to_dev(w, DEV)
+    args = (d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["context_lens"],
+            w.max_context_len, w.scale)
+    k0, v0 = d["k_cache"].clone(), d["v_cache"].clone()
+    pkv.kv_append(d["k_cache"], d["v_cache"], d["k_new"], d["v_new"], d["slots"])
+    ref_out, ref_lse = pkv.paged_attn_decode(*args, split_tokens=256, return_lse=True)
+    torch.cuda.synchronize()
+    d["k_cache"].copy_(k0)
+    d["v_cache"].copy_(v0)
+    o_parts, l_parts, ws = pkv.paged_attn_decode_partials(*args, split_tokens=256)
+    out = torch.empty_like(d["q"])
+    lse = torch.empty(4, 16, dtype=torch.float32, device=DEV)
+    calls = [pkv.binding.prepare_kv_append(d["k_cache"], d["v_cache"], d["k_new"], d["v_new"],
+                                           d["slots"]),
+             pkv.binding.prepare_decode_partials(*args, 256, ws),
+             pkv.binding.prepare_merge_states(o_parts, l_parts, out, lse)]
+    for _ in range(2):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    assert torch.equal(bits(out), bits(ref_out)) and torch.equal(bits(lse), bits(ref_lse))
