@@ -106,9 +106,16 @@ struct Mfma<TF16> {
 // 32-byte chunk pairs) cover 8 distinct chunk pairs.
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
-// Direct global-to-LDS copy: lane i's 16 bytes go to lds_base + 16 * i.
-__device__ __forceinline__ void dma16(const void* gsrc, lds_u8* lds_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, lds_base, 16, 0, 0);
+// Direct global-to-LDS copy through a buffer descriptor: lane i's 16 bytes
+// at byte offset voff of the buffer go to lds_base + 16 * i.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, lds_u8* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)lds_base,
+                                           16, voff, 0, 0, 0);
+}
+// Descriptor of one 4-KiB (page, head) block: base address, no stride, range
+// 4096 bytes, 32-bit data format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const char* base) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, P * D * 2, 0x00020000);
 }
 
 // Transposing LDS read: in each group of 16 lanes, lane i receives element
@@ -191,22 +198,36 @@ __global__ __launch_bounds__(NWP * 64, 2) void prefill_kernel(PrefillArgs a) {
   // ---- staging: wave w copies page w of the tile (key rows 16w .. 16w+15)
   // of K and V as four 1-KiB LDS chunks of four rows; lane i of a chunk fills
   // row 4j + i/16, physical chunk i%16 with logical chunk (i%16) ^ swz(row).
+  // The page, its descriptor and the LDS destination are the same for the
+  // whole wave (scalar registers); each lane adds a fixed offset.  The page id
+  // of the next tile is loaded one tile ahead.
   const int64_t head_block = (int64_t)P * D * 2;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  uint32_t dma_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 4 * j + (lane >> 4);               // key row within the page
+    dma_off[j] = (uint32_t)(r * ROWB + (((lane & 15) ^ swz(r)) * 16));
+  }
   bool my_bad = false;
+  int pid_next = 0;
+  auto fetch_pid = [&](int it) {
+    const int pi = it * (BK / P) + wu;
+    pid_next = (it < n_tiles && pi < seq_pages) ? bt_row[pi] : 0;
+  };
   auto issue_tile = [&](int it, lds_u8* kdst, lds_u8* vdst) {
-    const int pi = it * (BK / P) + w;
-    int pid = pi < seq_pages ? bt_row[pi] : 0;
+    const int pi = it * (BK / P) + wu;
+    int pid = __builtin_amdgcn_readfirstlane(pid_next);
+    fetch_pid(it + 1);
     if (pi < seq_pages && (pid < 0 || pid >= a.num_pages)) my_bad = true;
     if (pid < 0 || pid >= a.num_pages) pid = 0;   // always a readable page
     const int64_t base = ((int64_t)pid * a.num_kv_heads + g) * head_block;
+    const __amdgpu_buffer_rsrc_t kr = page_rsrc((const char*)a.k_cache + base);
+    const __amdgpu_buffer_rsrc_t vr = page_rsrc((const char*)a.v_cache + base);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int r = 16 * w + 4 * j + (lane >> 4);    // key row within the tile
-      const int tok = r % P;
-      const int lc = (lane & 15) ^ swz(r);           // logical 16-byte chunk
-      const int64_t off = base + tok * ROWB + lc * 16;
-      dma16((const char*)a.k_cache + off, kdst + (16 * w + 4 * j) * ROWB);
-      dma16((const char*)a.v_cache + off, vdst + (16 * w + 4 * j) * ROWB);
+      dma16(kr, dma_off[j], kdst + (16 * wu + 4 * j) * ROWB);
+      dma16(vr, dma_off[j], vdst + (16 * wu + 4 * j) * ROWB);
     }
   };
   // V rows of keys past the sequence end become zero (edge tiles only)
@@ -237,14 +258,11 @@ __global__ __launch_bounds__(NWP * 64, 2) void prefill_kernel(PrefillArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = fmaxf(mx, xor_f(mx, 32));
-    // The reference max moves only when a row's max exceeds it by more than
-    // 2^8 in probability, so the accumulators are rarely rescaled; every
-    // probability stays <= 2^8 (times the f16 offset 2^POFF <= 2^15).
     const bool grow = (m_run == -INFINITY) ? (mx > -INFINITY) : ((mx - m_run) * c > kLazyLog2);
     if (__ballot(grow) != 0) {
       __asm__ volatile("");   // keep this a branch: the rescale is rare
-      const float m_new = grow ? mx : m_run;
+      mx = fmaxf(mx, xor_f(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
       const float alpha = (m_run == -INFINITY) ? 0.f : exp2_fast((m_run - m_new) * c);
       l_run *= alpha;
 #pragma unroll
@@ -361,6 +379,7 @@ __global__ __launch_bounds__(NWP * 64, 2) void prefill_kernel(PrefillArgs a) {
   };
   const int n_full = min(n_tiles, (hist + pos0 + 1) / BK);
 
+  fetch_pid(0);
   issue_tile(0, kb0, vb0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
