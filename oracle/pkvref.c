@@ -27,10 +27,20 @@
  *     kv_len - C + i and sees keys 0 .. that position (bottom-right causal).
  *   - Merging partial results over disjoint key sets by their log-sum-exp,
  *     the same recursion that the pages' online softmax rests on.
+ *   - An fp8 KV cache (page 1, section 4.1 and page 4, section 3.2 name the
+ *     e4m3 and e5m2 cache types; page 4, chapter 6 calls fp8 the most
+ *     cost-effective saving): element = per-tensor fp32 scale times the
+ *     OCP 8-bit float value; a new token is stored as the code nearest to
+ *     x / scale (x / scale taken in fp32, ties to the even code), clipped to
+ *     the largest finite value.
+ *   - A sliding window (page 4, section 2.3: each token attends to a local
+ *     window, mixed with a few global tokens): with window w > 0 the query at
+ *     the last position L - 1 sees keys t >= L - w and the first `sink` keys.
  *
  * Inputs are converted to double exactly (f32 cast; f16 decoded from its
  * sign/exponent/mantissa fields, subnormals included; bf16 shifted into the
- * high half of an f32).  exp and log are the host libm's.
+ * high half of an f32; fp8 decoded from its fields).  exp and log are the
+ * host libm's.
  *
  * Cache layout: K and V pools [num_pages][H_kv][P][D] of the element type.
  * Return value: 0 on success, -1 on an invalid argument or an index out of
@@ -44,15 +54,56 @@
 #include <omp.h>
 #endif
 
-enum { REF_F32 = 0, REF_F16 = 1, REF_BF16 = 2 };
+enum { REF_F32 = 0, REF_F16 = 1, REF_BF16 = 2, REF_FP8_E4M3 = 3, REF_FP8_E5M2 = 4 };
 
 static int elem_bytes(int dtype) {
   switch (dtype) {
     case REF_F32: return 4;
     case REF_F16: return 2;
     case REF_BF16: return 2;
+    case REF_FP8_E4M3: return 1;
+    case REF_FP8_E5M2: return 1;
     default: return 0;
   }
+}
+
+static int is_fp8(int dtype) { return dtype == REF_FP8_E4M3 || dtype == REF_FP8_E5M2; }
+
+/* OCP 8-bit float E4M3 ("FN": no infinities): sign, 4 exponent bits with
+   bias 7, 3 mantissa bits; the single pattern S.1111.111 is NaN. */
+static double fp8_e4m3_to_double(uint8_t b) {
+  int sign = b >> 7;
+  int expo = (b >> 3) & 15;
+  int mant = b & 7;
+  double v;
+  if (expo == 15 && mant == 7) return NAN;
+  if (expo == 0) {
+    v = ldexp((double)mant, -9);                 /* mant/8 * 2^(1-7) */
+  } else {
+    v = ldexp((double)(8 + mant), expo - 10);    /* (1 + mant/8) * 2^(expo-7) */
+  }
+  return sign ? -v : v;
+}
+
+/* OCP 8-bit float E5M2: sign, 5 exponent bits with bias 15, 2 mantissa bits,
+   infinities and NaNs as in IEEE 754. */
+static double fp8_e5m2_to_double(uint8_t b) {
+  int sign = b >> 7;
+  int expo = (b >> 2) & 31;
+  int mant = b & 3;
+  double v;
+  if (expo == 31) {
+    v = mant ? NAN : INFINITY;
+  } else if (expo == 0) {
+    v = ldexp((double)mant, -16);                /* mant/4 * 2^(1-15) */
+  } else {
+    v = ldexp((double)(4 + mant), expo - 17);    /* (1 + mant/4) * 2^(expo-15) */
+  }
+  return sign ? -v : v;
+}
+
+static double fp8_to_double(int dtype, uint8_t b) {
+  return dtype == REF_FP8_E4M3 ? fp8_e4m3_to_double(b) : fp8_e5m2_to_double(b);
 }
 
 /* IEEE binary16 -> double, field by field. */
@@ -80,6 +131,7 @@ static double bf16_to_double(uint16_t b) {
 }
 
 static double load_elem(const void* base, int64_t idx, int dtype) {
+  if (is_fp8(dtype)) return fp8_to_double(dtype, ((const uint8_t*)base)[idx]);
   if (dtype == REF_F32) {
     float f;
     memcpy(&f, (const char*)base + idx * 4, 4);
@@ -96,6 +148,45 @@ int pkvref_version(void) { return 1; }
 int pkvref_to_double(int dtype, const void* src, int64_t n, double* dst) {
   if (!elem_bytes(dtype) || n < 0 || (n > 0 && (!src || !dst))) return -1;
   for (int64_t i = 0; i < n; ++i) dst[i] = load_elem(src, i, dtype);
+  return 0;
+}
+
+/*
+ * fp8 code of y: the non-negative code whose value is nearest to |y| (on a
+ * tie, the even code), with the sign bit of y.  |y| at or beyond the largest
+ * finite value gives that value; NaN gives 0x7F.  A search over the codes.
+ */
+static uint8_t fp8_encode(int dtype, float y) {
+  if (y != y) return 0x7F;
+  const int max_code = dtype == REF_FP8_E4M3 ? 0x7E : 0x7B;   /* 448, 57344 */
+  const double a = fabs((double)y);
+  int best = max_code;
+  if (a < fp8_to_double(dtype, (uint8_t)max_code)) {
+    double best_d = INFINITY;
+    for (int c = 0; c <= max_code; ++c) {
+      const double d = fabs(fp8_to_double(dtype, (uint8_t)c) - a);
+      if (d < best_d || (d == best_d && (c & 1) == 0)) {
+        best = c;
+        best_d = d;
+      }
+    }
+  }
+  return (uint8_t)(best | (signbit(y) ? 0x80 : 0));
+}
+
+/*
+ * quant_fp8: dst[i] = fp8 code of (float)x_i / scale, x_i of src_dtype
+ * (exactly representable as float), the division in IEEE fp32.
+ */
+int pkvref_quant_fp8(int fp8_dtype, int src_dtype, const void* src, int64_t n, float scale,
+                     uint8_t* dst) {
+  if (!is_fp8(fp8_dtype) || !elem_bytes(src_dtype) || is_fp8(src_dtype) || n < 0) return -1;
+  if (n > 0 && (!src || !dst)) return -1;
+  for (int64_t i = 0; i < n; ++i) {
+    const float x = (float)load_elem(src, i, src_dtype);
+    const float y = x / scale;
+    dst[i] = fp8_encode(fp8_dtype, y);
+  }
   return 0;
 }
 
@@ -166,39 +257,51 @@ int pkvref_gather(int dtype, int32_t num_pages, int32_t page_size, int32_t num_k
   return 0;
 }
 
+/* Key t of a sequence of n_keys is visible unless a window hides it:
+   visible iff t >= lo or t < sink_n (lo = 0, sink_n = 0 without a window). */
+static int visible(int64_t t, int64_t lo, int64_t sink_n) { return t >= lo || t < sink_n; }
+
 /*
- * One query row against keys 0 .. n_keys-1 of one sequence and KV head g.
- * q_row: D doubles.  s: scratch of n_keys doubles.  Writes out[D], *lse.
- * n_keys == 0: out = 0, lse = -inf (an empty sum).
+ * One query row against the visible keys among 0 .. n_keys-1 of one sequence
+ * and KV head g.  K and V elements are k_scale (v_scale) times the cache
+ * value.  q_row: D doubles.  s: scratch of n_keys doubles.  Writes out[D],
+ * *lse.  No visible key: out = 0, lse = -inf (an empty sum).
  */
-static int attend_row(int dtype, int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
-                      int32_t head_dim, const void* k_cache, const void* v_cache,
-                      const int32_t* table_row, int64_t n_keys, int32_t g, const double* q_row,
-                      double scale, double* s, double* out, double* lse) {
+static int attend_row(int kv_dtype, int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
+                      int32_t head_dim, const void* k_cache, const void* v_cache, double k_scale,
+                      double v_scale, const int32_t* table_row, int64_t n_keys, int64_t lo,
+                      int64_t sink_n, int32_t g, const double* q_row, double scale, double* s,
+                      double* out, double* lse) {
   for (int32_t d = 0; d < head_dim; ++d) out[d] = 0.0;
-  if (n_keys == 0) {
-    *lse = -INFINITY;
-    return 0;
-  }
-  /* pass 1: scores and their maximum */
+  /* pass 1: scores of the visible keys and their maximum */
   double m = -INFINITY;
+  int64_t n_vis = 0;
   for (int64_t t = 0; t < n_keys; ++t) {
+    if (!visible(t, lo, sink_n)) continue;
     int64_t page = page_of(table_row, t, page_size, num_pages);
     if (page < 0) return -1;
     int64_t base = row_index(page, t, g, page_size, num_kv_heads, head_dim);
     double dot = 0.0;
-    for (int32_t d = 0; d < head_dim; ++d) dot += q_row[d] * load_elem(k_cache, base + d, dtype);
+    for (int32_t d = 0; d < head_dim; ++d)
+      dot += q_row[d] * (k_scale * load_elem(k_cache, base + d, kv_dtype));
     s[t] = scale * dot;
     if (s[t] > m) m = s[t];
+    ++n_vis;
+  }
+  if (n_vis == 0) {
+    *lse = -INFINITY;
+    return 0;
   }
   /* pass 2: exponentials, their sum, weighted sum of V rows */
   double l = 0.0;
   for (int64_t t = 0; t < n_keys; ++t) {
+    if (!visible(t, lo, sink_n)) continue;
     double w = exp(s[t] - m);
     l += w;
     int64_t page = page_of(table_row, t, page_size, num_pages);
     int64_t base = row_index(page, t, g, page_size, num_kv_heads, head_dim);
-    for (int32_t d = 0; d < head_dim; ++d) out[d] += w * load_elem(v_cache, base + d, dtype);
+    for (int32_t d = 0; d < head_dim; ++d)
+      out[d] += w * (v_scale * load_elem(v_cache, base + d, kv_dtype));
   }
   for (int32_t d = 0; d < head_dim; ++d) out[d] /= l;
   *lse = m + log(l);
@@ -214,19 +317,27 @@ static void set_threads(int32_t n_threads) {
 }
 
 /*
- * decode: one query token per sequence.  q [B][H_q][D]; block_table
- * [B][stride]; context_lens [B].  rows: indices r = b * H_q + h to compute,
- * or NULL for all B * H_q rows in order.  out [n_rows][D], lse [n_rows]
- * (natural log).  scale is the float32 value the GPU receives, widened.
+ * decode_ex: one query token per sequence.  q [B][H_q][D] of q_dtype; the
+ * pools hold kv_dtype (for fp8, element = k_scale or v_scale times the code's
+ * value; otherwise the scales must be 1 and kv_dtype == q_dtype).
+ * block_table [B][stride]; context_lens [B].  window > 0 restricts the keys
+ * to t >= L - window plus the first `sink` (window 0: all keys).  rows:
+ * indices r = b * H_q + h to compute, or NULL for all B * H_q rows in order.
+ * out [n_rows][D], lse [n_rows] (natural log).  scale is the float32 value
+ * the GPU receives, widened.
  */
-int pkvref_decode(int dtype, int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
-                  int32_t head_dim, const void* k_cache, const void* v_cache, const void* q,
-                  int32_t batch, int32_t num_q_heads, const int32_t* block_table,
-                  int32_t stride, const int32_t* context_lens, float scale,
-                  const int64_t* rows, int64_t n_rows, double* out, double* lse,
-                  int32_t n_threads) {
-  if (!elem_bytes(dtype) || page_size <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-      batch < 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0 || stride <= 0)
+int pkvref_decode_ex(int q_dtype, int kv_dtype, int32_t num_pages, int32_t page_size,
+                     int32_t num_kv_heads, int32_t head_dim, const void* k_cache,
+                     const void* v_cache, float k_scale, float v_scale, const void* q,
+                     int32_t batch, int32_t num_q_heads, const int32_t* block_table,
+                     int32_t stride, const int32_t* context_lens, float scale, int32_t window,
+                     int32_t sink, const int64_t* rows, int64_t n_rows, double* out, double* lse,
+                     int32_t n_threads) {
+  if (!elem_bytes(q_dtype) || is_fp8(q_dtype) || !elem_bytes(kv_dtype) || page_size <= 0 ||
+      num_kv_heads <= 0 || head_dim <= 0 || batch < 0 || num_q_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || stride <= 0 || window < 0 || sink < 0)
+    return -1;
+  if (!is_fp8(kv_dtype) && (kv_dtype != q_dtype || k_scale != 1.0f || v_scale != 1.0f))
     return -1;
   int64_t all = (int64_t)batch * num_q_heads;
   if (!rows) n_rows = all;
@@ -250,20 +361,39 @@ int pkvref_decode(int dtype, int32_t num_pages, int32_t page_size, int32_t num_k
       int64_t b = r / num_q_heads;
       int32_t h = (int32_t)(r % num_q_heads);
       int64_t n_keys = context_lens[b];
+      int64_t lo = 0, sink_n = 0;
+      if (window > 0) {
+        lo = n_keys - window > 0 ? n_keys - window : 0;
+        sink_n = sink < n_keys ? sink : n_keys;
+      }
       if (n_keys > s_cap) {
         free(s);
         s_cap = n_keys;
         s = (double*)malloc(sizeof(double) * s_cap);
       }
-      for (int32_t d = 0; d < head_dim; ++d) qd[d] = load_elem(q, r * head_dim + d, dtype);
-      err |= attend_row(dtype, num_pages, page_size, num_kv_heads, head_dim, k_cache, v_cache,
-                        block_table + b * stride, n_keys, h / group, qd, (double)scale, s,
-                        out + i * head_dim, lse + i);
+      for (int32_t d = 0; d < head_dim; ++d) qd[d] = load_elem(q, r * head_dim + d, q_dtype);
+      err |= attend_row(kv_dtype, num_pages, page_size, num_kv_heads, head_dim, k_cache,
+                        v_cache, (double)k_scale, (double)v_scale, block_table + b * stride,
+                        n_keys, lo, sink_n, h / group, qd, (double)scale, s, out + i * head_dim,
+                        lse + i);
     }
     free(s);
     free(qd);
   }
   return err ? -1 : 0;
+}
+
+/* decode: decode_ex with one element type, unit scales and no window. */
+int pkvref_decode(int dtype, int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
+                  int32_t head_dim, const void* k_cache, const void* v_cache, const void* q,
+                  int32_t batch, int32_t num_q_heads, const int32_t* block_table,
+                  int32_t stride, const int32_t* context_lens, float scale,
+                  const int64_t* rows, int64_t n_rows, double* out, double* lse,
+                  int32_t n_threads) {
+  if (is_fp8(dtype)) return -1;
+  return pkvref_decode_ex(dtype, dtype, num_pages, page_size, num_kv_heads, head_dim, k_cache,
+                          v_cache, 1.0f, 1.0f, q, batch, num_q_heads, block_table, stride,
+                          context_lens, scale, 0, 0, rows, n_rows, out, lse, n_threads);
 }
 
 /*
@@ -278,8 +408,9 @@ int pkvref_prefill(int dtype, int32_t num_pages, int32_t page_size, int32_t num_
                    const int32_t* block_table, int32_t stride, const int32_t* kv_lens,
                    float scale, const int64_t* rows, int64_t n_rows, double* out, double* lse,
                    int32_t n_threads) {
-  if (!elem_bytes(dtype) || page_size <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-      batch < 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0 || stride <= 0)
+  if (!elem_bytes(dtype) || is_fp8(dtype) || page_size <= 0 || num_kv_heads <= 0 ||
+      head_dim <= 0 || batch < 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
+      stride <= 0)
     return -1;
   if (q_indptr[0] != 0) return -1;
   for (int32_t b = 0; b < batch; ++b) {
@@ -318,8 +449,8 @@ int pkvref_prefill(int dtype, int32_t num_pages, int32_t page_size, int32_t num_
       }
       for (int32_t d = 0; d < head_dim; ++d) qd[d] = load_elem(q, r * head_dim + d, dtype);
       err |= attend_row(dtype, num_pages, page_size, num_kv_heads, head_dim, k_cache, v_cache,
-                        block_table + (int64_t)b * stride, n_keys, h / group, qd,
-                        (double)scale, s, out + i * head_dim, lse + i);
+                        1.0, 1.0, block_table + (int64_t)b * stride, n_keys, 0, 0, h / group,
+                        qd, (double)scale, s, out + i * head_dim, lse + i);
     }
     free(s);
     free(qd);

@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpkvref.so")
 _lib = None
 
-DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "fp8_e4m3": 3, "fp8_e5m2": 4}
 
 
 def _configure(L):
@@ -32,10 +32,13 @@ def _configure(L):
                                 vp, f32, vp, i64, vp, vp, i32]
     L.pkvref_prefill.argtypes = [C.c_int, i32, i32, i32, i32, vp, vp, vp, vp, i32, i32, vp,
                                  i32, vp, f32, vp, i64, vp, vp, i32]
+    L.pkvref_decode_ex.argtypes = [C.c_int, C.c_int, i32, i32, i32, i32, vp, vp, f32, f32, vp,
+                                   i32, i32, vp, i32, vp, f32, i32, i32, vp, i64, vp, vp, i32]
     L.pkvref_merge.argtypes = [vp, vp, i64, i32, i32, vp, vp]
     L.pkvref_to_double.argtypes = [C.c_int, vp, i64, vp]
+    L.pkvref_quant_fp8.argtypes = [C.c_int, C.c_int, vp, i64, f32, vp]
     for fn in ("pkvref_kv_append", "pkvref_gather", "pkvref_decode", "pkvref_prefill",
-               "pkvref_merge", "pkvref_to_double"):
+               "pkvref_merge", "pkvref_to_double", "pkvref_decode_ex", "pkvref_quant_fp8"):
         getattr(L, fn).restype = C.c_int
     return L
 
@@ -133,6 +136,42 @@ def decode(dtype: str, k_cache, v_cache, q, block_table, context_lens, scale: fl
                                _ptr(cl), float(scale), _ptr(r), n, _ptr(out), _ptr(lse),
                                int(n_threads)), "decode")
     return out, lse
+
+
+def decode_ex(q_dtype: str, kv_dtype: str, k_cache, v_cache, q, block_table, context_lens,
+              scale: float, k_scale: float = 1.0, v_scale: float = 1.0, window: int = 0,
+              sink: int = 0, rows: Optional[Sequence[int]] = None, n_threads: int = 0):
+    """Decode attention with a cache type apart from the query type (fp8 pools
+    with per-tensor scales) and an optional sliding window: with window > 0
+    the query sees keys t >= L - window and t < sink.  Returns (out, lse) in
+    float64 as decode() does."""
+    num_pages, hkv, p, d = k_cache.shape
+    batch, hq, dq = q.shape
+    assert dq == d
+    bt = _i32(block_table)
+    cl = _i32(context_lens)
+    r = _rows(rows)
+    n = batch * hq if r is None else int(r.shape[0])
+    out = np.zeros((n, d), dtype=np.float64)
+    lse = np.zeros((n,), dtype=np.float64)
+    _check(lib().pkvref_decode_ex(DTYPE_CODES[q_dtype], DTYPE_CODES[kv_dtype], num_pages, p, hkv,
+                                  d, _ptr(k_cache), _ptr(v_cache), float(k_scale),
+                                  float(v_scale), _ptr(q), batch, hq, _ptr(bt), int(bt.shape[1]),
+                                  _ptr(cl), float(scale), int(window), int(sink), _ptr(r), n,
+                                  _ptr(out), _ptr(lse), int(n_threads)), "decode_ex")
+    return out, lse
+
+
+def quant_fp8(fp8_dtype: str, src_dtype: str, x, scale: float) -> np.ndarray:
+    """fp8 codes (uint8, same shape) of x / scale: the division in fp32, the
+    nearest code with ties to the even one, clipped to the largest finite
+    value; NaN gives 0x7F."""
+    x = x.contiguous() if torch is not None and isinstance(x, torch.Tensor) else x
+    n = int(np.prod(x.shape))
+    out = np.zeros(tuple(x.shape), dtype=np.uint8)
+    _check(lib().pkvref_quant_fp8(DTYPE_CODES[fp8_dtype], DTYPE_CODES[src_dtype], _ptr(x), n,
+                                  float(scale), _ptr(out)), "quant_fp8")
+    return out
 
 
 def prefill(dtype: str, k_cache, v_cache, q, q_indptr, block_table, kv_lens, scale: float,

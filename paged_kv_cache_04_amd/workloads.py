@@ -27,6 +27,11 @@ kernel that reads outside the valid range turns its output into NaN.
 Every tensor is drawn from one CPU ``torch.Generator`` per workload, in a
 fixed order: lengths, page permutation, Q, K, V, new-token K/V.  Normal draws
 are float32 N(0, 1), rounded to the cache dtype (round-to-nearest-even).
+
+fp8 caches (OCP e4m3 / e5m2, one fp32 scale per pool): the stored values are
+float32 N(0, 1) draws divided by the pool's scale and converted by torch's own
+float8 conversion, so that scale times the stored value follows N(0, 1) up to
+the format's rounding.  Q and the new tokens' K/V stay in the query dtype.
 """
 from __future__ import annotations
 
@@ -38,8 +43,11 @@ import torch
 
 PAGE_SIZE = 16
 
-DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
-DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}  # matches pkv_dtype in include/pkv.h
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+          "fp8_e4m3": torch.float8_e4m3fn, "fp8_e5m2": torch.float8_e5m2}
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "fp8_e4m3": 3,
+               "fp8_e5m2": 4}  # matches pkv_dtype in include/pkv.h
+FP8 = ("fp8_e4m3", "fp8_e5m2")
 
 # The five workloads.  Shapes follow the pages' models: Llama-3-8B has 32 query
 # heads over 8 KV heads and Llama-3-70B 64 over 8 (page 4, section 2.2 on GQA);
@@ -57,6 +65,11 @@ CONFIGS: Dict[str, dict] = {
                    prefix=2048, suffix_range=(32, 512), append=False),
     "prefill": dict(kind="prefill", seed=5, batch=4, hq=32, hkv=8, d=128, dtype="bf16",
                     hist=32768, chunk=512),
+    # the 128K decode with an fp8 (e4m3) cache: page 1, section 4.1 recommends
+    # that cache type for this deployment; f16 queries and outputs
+    "llama70b_128k_fp8": dict(kind="decode", seed=6, batch=8, hq=16, hkv=2, d=128,
+                              dtype="f16", kv_dtype="fp8_e4m3", k_scale=0.0234375,
+                              v_scale=0.01953125, ctx=131072, append=True),
 }
 
 
@@ -64,7 +77,7 @@ CONFIGS: Dict[str, dict] = {
 class Workload:
     name: str
     kind: str                      # "decode" or "prefill"
-    dtype: str                     # "f32" | "f16" | "bf16"
+    dtype: str                     # "f32" | "f16" | "bf16": queries, outputs, new tokens
     num_pages: int
     page_size: int
     num_kv_heads: int
@@ -84,10 +97,21 @@ class Workload:
     q_indptr: Optional[torch.Tensor] = None  # int32 [B+1] (prefill)
     poison_page: int = -1
     meta: dict = dataclasses.field(default_factory=dict)
+    kv_dtype: str = ""             # cache element type ("" = dtype)
+    k_scale: float = 1.0           # fp8 caches: K element = k_scale * stored value
+    v_scale: float = 1.0
+
+    def __post_init__(self):
+        if not self.kv_dtype:
+            self.kv_dtype = self.dtype
 
     @property
     def dtype_code(self) -> int:
         return DTYPE_CODES[self.dtype]
+
+    @property
+    def is_fp8(self) -> bool:
+        return self.kv_dtype in FP8
 
     @property
     def stride(self) -> int:
@@ -113,8 +137,23 @@ def _normal(gen: torch.Generator, shape, dtype: str) -> torch.Tensor:
     return torch.randn(*shape, generator=gen, dtype=torch.float32).to(DTYPES[dtype])
 
 
+def _normal_kv(gen: torch.Generator, shape, kv_dtype: str, scale: float) -> torch.Tensor:
+    """Cache contents: N(0, 1) in the cache dtype, or for fp8 N(0, 1) / scale
+    converted by torch's float8 conversion."""
+    if kv_dtype in FP8:
+        x = torch.randn(*shape, generator=gen, dtype=torch.float32)
+        x.div_(torch.tensor(scale, dtype=torch.float32))
+        return x.to(DTYPES[kv_dtype])
+    return _normal(gen, shape, kv_dtype)
+
+
 def _poison(cache: torch.Tensor, valid: torch.Tensor) -> None:
-    """Fill every (page, slot) row not marked valid with NaN, all heads."""
+    """Fill every (page, slot) row not marked valid with NaN, all heads (for
+    fp8 the byte 0x7F, a NaN in both OCP formats)."""
+    if cache.dtype in (torch.float8_e4m3fn, torch.float8_e5m2):
+        view = cache.view(torch.uint8).permute(0, 2, 1, 3)
+        view[~valid] = 0x7F
+        return
     view = cache.permute(0, 2, 1, 3)          # [pages][P][H_kv][D] view of the same storage
     view[~valid] = float("nan")
 
@@ -147,7 +186,9 @@ def _slot_of(page_list: List[int], pos: int, page_size: int) -> int:
 def make_decode(name: str, *, seed: int, batch: int, hq: int, hkv: int, d: int, dtype: str,
                 hist_lens: List[int], append: bool, num_pages: Optional[int] = None,
                 pool_slack: float = 0.0, shared_prefix: int = 0,
-                page_size: int = PAGE_SIZE, gen: Optional[torch.Generator] = None) -> Workload:
+                page_size: int = PAGE_SIZE, gen: Optional[torch.Generator] = None,
+                kv_dtype: Optional[str] = None, k_scale: float = 1.0,
+                v_scale: float = 1.0) -> Workload:
     """Decode workload.
 
     hist_lens[b] tokens are already stored.  With ``append`` one more token per
@@ -155,8 +196,13 @@ def make_decode(name: str, *, seed: int, batch: int, hq: int, hkv: int, d: int, 
     attends to hist_lens[b] + 1 tokens (the appended token included).
     ``shared_prefix`` > 0 makes the first shared_prefix tokens of every
     sequence live in the same physical pages (must be a multiple of P);
-    hist_lens then count prefix + suffix.
+    hist_lens then count prefix + suffix.  ``kv_dtype`` (default: dtype) sets
+    the cache type; fp8 pools carry k_scale / v_scale and the appended token
+    arrives in dtype, to be quantized into the cache.
     """
+    kv_dtype = kv_dtype or dtype
+    if kv_dtype not in FP8:
+        assert kv_dtype == dtype and k_scale == 1.0 and v_scale == 1.0
     if gen is None:
         gen = torch.Generator().manual_seed(seed)
     assert shared_prefix % page_size == 0
@@ -181,8 +227,8 @@ def make_decode(name: str, *, seed: int, batch: int, hq: int, hkv: int, d: int, 
     block_table = _build_tables(page_lists, stride, poison_page if poison_page >= 0 else 0)
 
     q = _normal(gen, (batch, hq, d), dtype)
-    k_cache = _normal(gen, (num_pages, hkv, page_size, d), dtype)
-    v_cache = _normal(gen, (num_pages, hkv, page_size, d), dtype)
+    k_cache = _normal_kv(gen, (num_pages, hkv, page_size, d), kv_dtype, k_scale)
+    v_cache = _normal_kv(gen, (num_pages, hkv, page_size, d), kv_dtype, v_scale)
     valid = _valid_mask(num_pages, page_lists, hist_lens, page_size)
     _poison(k_cache, valid)
     _poison(v_cache, valid)
@@ -201,7 +247,8 @@ def make_decode(name: str, *, seed: int, batch: int, hq: int, hkv: int, d: int, 
                     scale=float32_scale(d), k_new=k_new, v_new=v_new, slots=slots,
                     poison_page=poison_page,
                     meta=dict(page_lists=page_lists, hist_lens=list(hist_lens),
-                              shared_prefix=shared_prefix, seed=seed))
+                              shared_prefix=shared_prefix, seed=seed),
+                    kv_dtype=kv_dtype, k_scale=float(k_scale), v_scale=float(v_scale))
 
 
 def make_prefill(name: str, *, seed: int, batch: int, hq: int, hkv: int, d: int, dtype: str,
@@ -281,10 +328,12 @@ def make(name: str, seed: Optional[int] = None) -> Workload:
         return make_decode(name, seed=seed, batch=b, hq=cfg["hq"], hkv=cfg["hkv"], d=cfg["d"],
                            dtype=cfg["dtype"], hist_lens=hist, append=True,
                            pool_slack=cfg["pool_slack"], gen=gen)
-    if name == "llama70b_128k":
+    if name in ("llama70b_128k", "llama70b_128k_fp8"):
         hist = [cfg["ctx"] - 1] * b        # the appended token makes the context 131072
         return make_decode(name, seed=seed, batch=b, hq=cfg["hq"], hkv=cfg["hkv"], d=cfg["d"],
-                           dtype=cfg["dtype"], hist_lens=hist, append=True, gen=gen)
+                           dtype=cfg["dtype"], hist_lens=hist, append=True, gen=gen,
+                           kv_dtype=cfg.get("kv_dtype"), k_scale=cfg.get("k_scale", 1.0),
+                           v_scale=cfg.get("v_scale", 1.0))
     if name == "prefix":
         lo, hi = cfg["suffix_range"]
         suf = torch.randint(lo, hi + 1, (b,), generator=gen).tolist()

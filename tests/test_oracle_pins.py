@@ -9,6 +9,13 @@
 - invariances: physical page renumbering, shared prefix pages versus private
   copies, and the log-sum-exp merge of any split of the keys,
 - exhaustive widening of every 16-bit half / bfloat16 pattern,
+- fp8 caches: every OCP e4m3 / e5m2 code widened as torch's own float8 types
+  widen it (and e5m2 as the top byte of an IEEE half, by numpy), the
+  quantizer against torch's float8 rounding of the clipped fp32 quotient, and
+  decode over fp8 pools against dense attention on the dequantized rows,
+- sliding window: the last row of the pages' mixed local/global attention
+  mask (page 4, section 2.3) computed densely, a window of one key returning
+  that key's V row exactly, and pages outside the window never read,
 - a mutation battery: plausible mistakes planted in a copy of the oracle
   source must each fail at least one of these pins.
 """
@@ -455,6 +462,183 @@ def test_prefill_pair_count():
     assert accounting.prefill_flops([33280] * 4, [512] * 4, 32, 128) == 4 * 128 * 32 * 4 * 16908544
 
 
+# ------------------------------------------------------ fp8 caches and windows
+
+FP8 = {"fp8_e4m3": (torch.float8_e4m3fn, 448.0), "fp8_e5m2": (torch.float8_e5m2, 57344.0)}
+
+
+def _same_values(a, b):
+    nan = np.isnan(b)
+    assert np.array_equal(np.isnan(a), nan)
+    assert np.array_equal(a[~nan], b[~nan])
+    assert np.array_equal(np.signbit(a[~nan]), np.signbit(b[~nan]))
+
+
+def check_fp8_widening():
+    codes = torch.arange(256, dtype=torch.uint8)
+    for name, (tdt, _) in FP8.items():
+        _same_values(pkvref.to_double(name, codes), codes.view(tdt).to(torch.float64).numpy())
+    # e5m2 is the upper byte of an IEEE binary16 (numpy's float16, another implementation)
+    h = (codes.numpy().astype(np.uint16) << 8).view(np.float16).astype(np.float64)
+    _same_values(pkvref.to_double("fp8_e5m2", codes), h)
+    # values the OCP formats define: largest finite, smallest subnormal and
+    # normal, one, the NaN / infinity patterns, negative zero
+    e4 = pkvref.to_double("fp8_e4m3", torch.tensor([0x7E, 0x01, 0x08, 0x38, 0x7F, 0xFF, 0x80],
+                                                   dtype=torch.uint8))
+    assert list(e4[:4]) == [448.0, 2.0 ** -9, 2.0 ** -6, 1.0]
+    assert np.isnan(e4[4]) and np.isnan(e4[5]) and e4[6] == 0.0 and np.signbit(e4[6])
+    e5 = pkvref.to_double("fp8_e5m2", torch.tensor([0x7B, 0x7C, 0xFC, 0x7D, 0x01, 0x04, 0x3C],
+                                                   dtype=torch.uint8))
+    assert e5[0] == 57344.0 and e5[1] == math.inf and e5[2] == -math.inf and np.isnan(e5[3])
+    assert list(e5[4:]) == [2.0 ** -16, 2.0 ** -14, 1.0]
+
+
+def test_fp8_widening():
+    check_fp8_widening()
+
+
+def _fp8_midpoints(name):
+    """Exact midpoints between adjacent finite codes (ties), as float32."""
+    v = pkvref.to_double(name, torch.arange(128, dtype=torch.uint8))
+    v = v[np.isfinite(v)]
+    mids = (v[:-1] + v[1:]) / 2
+    return torch.tensor(np.concatenate([mids, -mids]), dtype=torch.float32)
+
+
+def check_fp8_quant():
+    gen = torch.Generator().manual_seed(41)
+    special = torch.tensor([0.0, -0.0, math.inf, -math.inf, math.nan, 1e-30, -1e-30, 1e30,
+                            -1e30, 448.0, 464.0, 465.0, 57344.0, 61440.0, 61441.0],
+                           dtype=torch.float32)
+    for name, (tdt, mx) in FP8.items():
+        for src, scale in (("f32", 1.0), ("f32", 0.75), ("f16", 0.0234375), ("bf16", 3.0)):
+            parts = [torch.randn(3000, generator=gen) * 200, torch.randn(1000, generator=gen)]
+            if src == "f32" and scale == 1.0:
+                parts += [_fp8_midpoints(name), special]
+            x = torch.cat(parts).to(W.DTYPES[src])
+            got = pkvref.quant_fp8(name, src, x, scale)
+            y = x.float() / torch.tensor(scale, dtype=torch.float32)
+            want = torch.clamp(y, -mx, mx).to(tdt).view(torch.uint8).numpy()
+            nan = torch.isnan(y).numpy()
+            assert np.array_equal(got[~nan], want[~nan]), (name, src, scale)
+            assert np.all(got[nan] == 0x7F)
+
+
+def test_fp8_quant():
+    check_fp8_quant()
+
+
+def _fp8_workload(kv_dtype, seed=51, lens=(1, 17, 40, 77), qd="bf16"):
+    return W.make_decode("f8", seed=seed, batch=len(lens), hq=8, hkv=2, d=32, dtype=qd,
+                         hist_lens=list(lens), append=False, pool_slack=0.25,
+                         kv_dtype=kv_dtype, k_scale=0.046875, v_scale=0.0234375)
+
+
+def check_dense_decode_fp8(kv_dtype):
+    w = _fp8_workload(kv_dtype)
+    out, lse = pkvref.decode_ex(w.dtype, kv_dtype, w.k_cache, w.v_cache, w.q, w.block_table,
+                                w.context_lens, w.scale, k_scale=w.k_scale, v_scale=w.v_scale)
+    G = w.num_q_heads // w.num_kv_heads
+    for b in range(w.batch):
+        kc, vc = W.contiguous_kv(w, b)
+        kd = (kc.to(torch.float64) * w.k_scale).permute(1, 0, 2).repeat_interleave(G, dim=0)
+        vd = (vc.to(torch.float64) * w.v_scale).permute(1, 0, 2).repeat_interleave(G, dim=0)
+        qd = w.q[b].double().unsqueeze(1)
+        ref = _sdpa_rows(qd, kd, vd, w.scale)[:, 0, :].numpy()
+        scores = torch.matmul(qd, kd.transpose(1, 2))[:, 0, :] * float(w.scale)
+        rows = slice(b * w.num_q_heads, (b + 1) * w.num_q_heads)
+        np.testing.assert_allclose(out[rows], ref, rtol=1e-10, atol=1e-11)
+        np.testing.assert_allclose(lse[rows], torch.logsumexp(scores, -1).numpy(), rtol=1e-11,
+                                   atol=1e-11)
+
+
+@pytest.mark.parametrize("kv_dtype", ["fp8_e4m3", "fp8_e5m2"])
+def test_dense_decode_fp8(kv_dtype):
+    check_dense_decode_fp8(kv_dtype)
+
+
+def _listing_mask_last_row(n, window_size, global_tokens):
+    """Row n-1 of the mixed local/global mask of page 4, section 2.3: row i
+    sees columns [i - window_size // 2, i + window_size // 2] clipped to the
+    sequence, every row sees the first global_tokens columns, and the first
+    global_tokens rows see every column."""
+    m = np.zeros((n, n), dtype=bool)
+    for i in range(n):
+        m[i, max(0, i - window_size // 2): min(n, i + window_size // 2 + 1)] = True
+    m[:global_tokens, :] = True
+    m[:, :global_tokens] = True
+    return m[n - 1]
+
+
+def check_window_listing():
+    """The decode row with window = window_size // 2 + 1 and sink =
+    global_tokens attends to exactly the keys the listing's mask opens."""
+    cases = [(4, 0), (6, 3), (30, 5), (17, 16), (64, 1), (2, 40)]
+    w = _small_decode(61, "f32", lens=(1, 15, 16, 17, 40, 77))
+    G = w.num_q_heads // w.num_kv_heads
+    for ws, gt in cases:
+        window, sink = ws // 2 + 1, gt
+        out, lse = pkvref.decode_ex("f32", "f32", w.k_cache, w.v_cache, w.q, w.block_table,
+                                    w.context_lens, w.scale, window=window, sink=sink)
+        for b in range(w.batch):
+            kc, vc = W.contiguous_kv(w, b)
+            L = kc.shape[0]
+            mask = torch.from_numpy(_listing_mask_last_row(L, ws, gt)).reshape(1, 1, L)
+            kd = kc.double().permute(1, 0, 2).repeat_interleave(G, dim=0)
+            vd = vc.double().permute(1, 0, 2).repeat_interleave(G, dim=0)
+            qd = w.q[b].double().unsqueeze(1)
+            ref = _sdpa_rows(qd, kd, vd, w.scale, mask=mask)[:, 0, :].numpy()
+            scores = (torch.matmul(qd, kd.transpose(1, 2)) * float(w.scale)).masked_fill(
+                ~mask, float("-inf"))[:, 0, :]
+            rows = slice(b * w.num_q_heads, (b + 1) * w.num_q_heads)
+            np.testing.assert_allclose(out[rows], ref, rtol=1e-10, atol=1e-11)
+            np.testing.assert_allclose(lse[rows], torch.logsumexp(scores, -1).numpy(),
+                                       rtol=1e-11, atol=1e-11)
+
+
+def test_window_matches_listing_mask():
+    check_window_listing()
+
+
+def test_window_of_one_returns_last_v_exactly():
+    w = _small_decode(62, "bf16", lens=(3, 16, 17, 50))
+    out, lse = pkvref.decode_ex("bf16", "bf16", w.k_cache, w.v_cache, w.q, w.block_table,
+                                w.context_lens, w.scale, window=1)
+    G = w.num_q_heads // w.num_kv_heads
+    for b in range(w.batch):
+        t = int(w.context_lens[b]) - 1
+        pg = w.meta["page_lists"][b][t // w.page_size]
+        for h in range(w.num_q_heads):
+            v = w.v_cache[pg, h // G, t % w.page_size].double().numpy()
+            k = w.k_cache[pg, h // G, t % w.page_size].double()
+            assert np.array_equal(out[b * w.num_q_heads + h], v)
+            s = float(torch.dot(w.q[b, h].double(), k)) * float(w.scale)
+            assert abs(lse[b * w.num_q_heads + h] - s) < 1e-12
+
+
+def test_window_never_reads_hidden_pages():
+    """Keys outside the window and the sink may hold NaN and their table
+    entries may point anywhere: the result is unchanged."""
+    w = _small_decode(63, "f16", lens=(40, 77, 100, 200))
+    window, sink = 20, 5
+    a = pkvref.decode_ex("f16", "f16", w.k_cache, w.v_cache, w.q, w.block_table,
+                         w.context_lens, w.scale, window=window, sink=sink)
+    k, v, bt = w.k_cache.clone(), w.v_cache.clone(), w.block_table.clone()
+    for b in range(w.batch):
+        L = int(w.context_lens[b])
+        pl = w.meta["page_lists"][b]
+        for t in range(sink, L - window):
+            k[pl[t // w.page_size], :, t % w.page_size] = float("nan")
+            v[pl[t // w.page_size], :, t % w.page_size] = float("nan")
+        for i in range(len(pl)):   # pages wholly hidden: the table entry is garbage
+            if i * w.page_size >= sink and (i + 1) * w.page_size <= L - window:
+                bt[b, i] = -12345
+    b_ = pkvref.decode_ex("f16", "f16", k, v, w.q, bt, w.context_lens, w.scale,
+                          window=window, sink=sink)
+    assert np.array_equal(a[0], b_[0]) and np.array_equal(a[1], b_[1])
+    assert np.all(np.isfinite(a[0]))
+
+
 # ------------------------------------------------------------ mutation battery
 
 MUTATIONS = [
@@ -471,7 +655,20 @@ MUTATIONS = [
     ("f16 subnormal scale", "ldexp((double)mant, -24)", "ldexp((double)mant, -25)"),
     ("bf16 shift", "(uint32_t)b << 16", "(uint32_t)b << 15"),
     ("append offset", "int64_t off = s % page_size;", "int64_t off = (s + 1) % page_size;"),
-    ("softmax weight from V", "out[d] += w * load_elem(v_cache", "out[d] += load_elem(v_cache"),
+    ("softmax weight from V", "out[d] += w * (v_scale * load_elem(v_cache",
+     "out[d] += (v_scale * load_elem(v_cache"),
+    ("e4m3 exponent bias", "ldexp((double)(8 + mant), expo - 10)",
+     "ldexp((double)(8 + mant), expo - 9)"),
+    ("e4m3 subnormal scale", "ldexp((double)mant, -9)", "ldexp((double)mant, -10)"),
+    ("e4m3 nan pattern", "if (expo == 15 && mant == 7) return NAN;", "if (expo == 15) return NAN;"),
+    ("e5m2 subnormal scale", "ldexp((double)mant, -16)", "ldexp((double)mant, -15)"),
+    ("quantiser ties to odd", "(d == best_d && (c & 1) == 0)", "(d == best_d && (c & 1) == 1)"),
+    ("quantiser without saturation", "int best = max_code;", "int best = 0;"),
+    ("k scale dropped", "q_row[d] * (k_scale * load_elem", "q_row[d] * (load_elem"),
+    ("v scale dropped", "w * (v_scale * load_elem", "w * (1.0 * load_elem"),
+    ("window one key short", "lo = n_keys - window > 0 ? n_keys - window : 0;",
+     "lo = n_keys - window + 1 > 0 ? n_keys - window + 1 : 0;"),
+    ("sink ignored", "return t >= lo || t < sink_n;", "return t >= lo;"),
 ]
 
 
@@ -485,6 +682,11 @@ def _battery():
     check_merge_identity()
     check_half_widening()
     test_kv_append_and_gather_bitwise()
+    check_fp8_widening()
+    check_fp8_quant()
+    for kv in FP8:
+        check_dense_decode_fp8(kv)
+    check_window_listing()
 
 
 def test_battery_passes_on_the_real_oracle():
