@@ -29,7 +29,10 @@
  *     pkv_last_error() gives a message (per calling thread).
  *   - Supported shapes: page_size 16; head_dim 64 or 128; dtype f32, f16,
  *     bf16; H_q a multiple of H_kv with G in {1, 2, 4, 8}; the prefill call
- *     needs f16 or bf16 and head_dim 128.
+ *     needs f16 or bf16 and head_dim 128.  fp8 caches (PKV_FP8_E4M3,
+ *     PKV_FP8_E5M2) are read by the *_ex decode calls with head_dim 128 and
+ *     f16 or bf16 queries; kv_append and gather_kv copy their bytes, and
+ *     kv_append_quant fills them from wider types.
  *   - Contents of device tables (page ids, lengths, slots) are preconditions
  *     the host cannot see.  Kernels keep every memory access inside the
  *     buffers described by the arguments even when a precondition is broken;
@@ -46,9 +49,21 @@
 extern "C" {
 #endif
 
-#define PKV_VERSION 1
+#define PKV_VERSION 2
 
-typedef enum pkv_dtype { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+/*
+ * Element types.  The fp8 types are the OCP 8-bit floats (E4M3 without
+ * infinities, largest finite 448; E5M2 with IEEE infinities and NaNs, largest
+ * finite 57344); page 1, section 4.1 and page 4, section 3.2 name them as KV
+ * cache types.  An fp8 pool carries one fp32 scale: element = scale * value.
+ */
+typedef enum pkv_dtype {
+  PKV_F32 = 0,
+  PKV_F16 = 1,
+  PKV_BF16 = 2,
+  PKV_FP8_E4M3 = 3,
+  PKV_FP8_E5M2 = 4
+} pkv_dtype;
 
 typedef enum pkv_status {
   PKV_OK = 0,
@@ -64,8 +79,35 @@ typedef struct pkv_cache_desc {
   int32_t page_size;    /* tokens per page, P */
   int32_t num_kv_heads; /* H_kv */
   int32_t head_dim;     /* D */
-  int32_t dtype;        /* pkv_dtype of K, V, Q and the output */
+  int32_t dtype;        /* pkv_dtype of K and V (and of Q and the output,
+                           except for fp8 caches: see pkv_decode_opts) */
 } pkv_cache_desc;
+
+/*
+ * Options of the *_ex decode calls.  NULL options mean: q_dtype = the cache
+ * dtype, unit scales, no window.
+ *   q_dtype  : pkv_dtype of q and out.  Must equal desc->dtype for f32, f16
+ *              and bf16 caches; PKV_F16 or PKV_BF16 for fp8 caches.
+ *   k_scale, v_scale : fp8 caches only (1 otherwise): a K (V) element is
+ *              k_scale (v_scale) times the stored fp8 value.  Finite, > 0.
+ *   window   : 0 = every key.  window > 0: the query, at position L - 1 of a
+ *              context of L keys, sees the keys t >= L - window (the window
+ *              most recent, itself included) and the first `sink` keys,
+ *              nothing else (page 4, section 2.3: a local sliding window
+ *              mixed with a few global tokens; that page's mask with
+ *              window_size W and global_tokens n opens exactly these keys of
+ *              the last row for window = W / 2 + 1, sink = n).  Pages that
+ *              hold no visible key are never read, and their block-table
+ *              entries are not looked at.
+ *   sink     : >= 0; ignored when window == 0.
+ */
+typedef struct pkv_decode_opts {
+  int32_t q_dtype;
+  float k_scale;
+  float v_scale;
+  int32_t window;
+  int32_t sink;
+} pkv_decode_opts;
 
 /* Library version (PKV_VERSION). */
 int pkv_version(void);
@@ -160,6 +202,53 @@ int pkv_paged_attn_decode_partials(const pkv_cache_desc* desc, const void* k_cac
                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * decode_plan_ex, paged_attn_decode_ex, paged_attn_decode_partials_ex -- the
+ * three decode calls above with options (fp8 caches, a q type apart from the
+ * cache type, a sliding window).  Same arguments and layouts otherwise; q and
+ * out hold opts->q_dtype.  With a window the split plan counts only the pages
+ * a window can reach (at most ceil(sink / P) + ceil(window / P) + 1 per
+ * sequence), so the plan and the workspace must come from decode_plan_ex with
+ * the same options.  opts may be NULL.  fp8 caches need head_dim 128.
+ */
+int pkv_decode_plan_ex(const pkv_cache_desc* desc, int32_t batch, int32_t num_q_heads,
+                       int32_t max_context_len, int32_t split_tokens,
+                       const pkv_decode_opts* opts, int32_t* n_split, size_t* workspace_bytes);
+
+int pkv_paged_attn_decode_ex(const pkv_cache_desc* desc, const void* k_cache,
+                             const void* v_cache, const void* q, int32_t batch,
+                             int32_t num_q_heads, const int32_t* block_table,
+                             int32_t block_table_stride, const int32_t* context_lens,
+                             int32_t max_context_len, float scale, int32_t split_tokens,
+                             const pkv_decode_opts* opts, void* out, float* lse_out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+int pkv_paged_attn_decode_partials_ex(const pkv_cache_desc* desc, const void* k_cache,
+                                      const void* v_cache, const void* q, int32_t batch,
+                                      int32_t num_q_heads, const int32_t* block_table,
+                                      int32_t block_table_stride, const int32_t* context_lens,
+                                      int32_t max_context_len, float scale,
+                                      int32_t split_tokens, const pkv_decode_opts* opts,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kv_append_quant -- kv_append into an fp8 cache from wider new tokens.
+ * For each i with s = slot_mapping[i] >= 0 (and < num_pages * P), every KV
+ * head g and element d:
+ *     k_cache[s / P][g][s % P][d] = fp8(k_new[i][g][d] / k_scale)   (V alike)
+ * where the quotient is taken in IEEE fp32 and fp8() rounds to the nearest
+ * code, ties to the even code, clips values beyond the largest finite one to
+ * it (infinities included) and maps NaN to the byte 0x7F.  The pages fix no
+ * quantization rule; this is the plainest per-tensor one.
+ *   desc->dtype      : PKV_FP8_E4M3 or PKV_FP8_E5M2.
+ *   k_new, v_new     : device [n_tokens][H_kv][D] of src_dtype (f32, f16, bf16).
+ *   k_scale, v_scale : finite, > 0.
+ */
+int pkv_kv_append_quant(const pkv_cache_desc* desc, void* k_cache, void* v_cache,
+                        const void* k_new, const void* v_new, int32_t src_dtype, float k_scale,
+                        float v_scale, const int32_t* slot_mapping, int32_t n_tokens,
+                        void* stream);
+
+/*
  * merge_states -- combine n_parts partial attention states per row:
  *     M = max_k lse_k,  w_k = exp(lse_k - M),
  *     out = sum_k w_k o_k / sum_k w_k,  lse = M + log(sum_k w_k),
@@ -168,7 +257,7 @@ int pkv_paged_attn_decode_partials(const pkv_cache_desc* desc, const void* k_cac
  *   o_parts   : device float [rows][n_parts][head_dim], 16-byte aligned;
  *               head_dim 64 or 128
  *   lse_parts : device float [rows][n_parts]
- *   out       : device [rows][head_dim] of out_dtype (pkv_dtype)
+ *   out       : device [rows][head_dim] of out_dtype (f32, f16 or bf16)
  *   lse_out   : device float [rows] or NULL
  */
 int pkv_merge_states(const float* o_parts, const float* lse_parts, int32_t rows,

@@ -6,11 +6,14 @@ that library, the seeded workload generators and the work/byte accounting.
 """
 from .binding import (  # noqa: F401
     CacheDesc,
+    DecodeOpts,
     PkvError,
     cache_desc,
+    decode_opts,
     decode_plan,
     gather_kv,
     kv_append,
+    kv_append_quant,
     merge_states,
     paged_attn_decode,
     paged_attn_decode_partials,

@@ -17,9 +17,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkv.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "pkv.h")
 
-PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
-_TORCH_TO_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
+PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3, PKV_FP8_E5M2 = 0, 1, 2, 3, 4
+_TORCH_TO_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16,
+                  torch.float8_e4m3fn: PKV_FP8_E4M3, torch.float8_e5m2: PKV_FP8_E5M2}
 _CODE_TO_TORCH = {v: k for k, v in _TORCH_TO_CODE.items()}
+_FP8 = (torch.float8_e4m3fn, torch.float8_e5m2)
 STATUS = {0: "PKV_OK", -1: "PKV_ERR_INVALID", -2: "PKV_ERR_UNSUPPORTED",
           -3: "PKV_ERR_WORKSPACE", -4: "PKV_ERR_HIP"}
 
@@ -33,6 +35,11 @@ class PkvError(RuntimeError):
 class CacheDesc(C.Structure):
     _fields_ = [("num_pages", C.c_int32), ("page_size", C.c_int32),
                 ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("dtype", C.c_int32)]
+
+
+class DecodeOpts(C.Structure):
+    _fields_ = [("q_dtype", C.c_int32), ("k_scale", C.c_float), ("v_scale", C.c_float),
+                ("window", C.c_int32), ("sink", C.c_int32)]
 
 
 _lib = None
@@ -61,9 +68,19 @@ def lib():
         L.pkv_paged_attn_prefill_chunk.argtypes = [dp, vp, vp, vp, vp, i32, i32, i32, i32, vp,
                                                    i32, vp, i32, f32, vp, vp, vp]
         L.pkv_validate_tables.argtypes = [dp, vp, i32, vp, i32, vp, i32]
+        op = C.POINTER(DecodeOpts)
+        L.pkv_decode_plan_ex.argtypes = [dp, i32, i32, i32, i32, op, C.POINTER(i32),
+                                         C.POINTER(sz)]
+        L.pkv_paged_attn_decode_ex.argtypes = [dp, vp, vp, vp, i32, i32, vp, i32, vp, i32, f32,
+                                               i32, op, vp, vp, vp, sz, vp]
+        L.pkv_paged_attn_decode_partials_ex.argtypes = [dp, vp, vp, vp, i32, i32, vp, i32, vp,
+                                                        i32, f32, i32, op, vp, sz, vp]
+        L.pkv_kv_append_quant.argtypes = [dp, vp, vp, vp, vp, i32, f32, f32, vp, i32, vp]
         for name in ("pkv_kv_append", "pkv_gather_kv", "pkv_decode_plan", "pkv_paged_attn_decode",
                      "pkv_paged_attn_decode_partials", "pkv_merge_states",
-                     "pkv_paged_attn_prefill_chunk", "pkv_validate_tables"):
+                     "pkv_paged_attn_prefill_chunk", "pkv_validate_tables",
+                     "pkv_decode_plan_ex", "pkv_paged_attn_decode_ex",
+                     "pkv_paged_attn_decode_partials_ex", "pkv_kv_append_quant"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -142,14 +159,48 @@ def gather_kv(k_cache, v_cache, table_row, length: int) -> Tuple[torch.Tensor, t
     return k_out, v_out
 
 
+def kv_append_quant(k_cache, v_cache, k_new, v_new, slots, k_scale: float,
+                    v_scale: float) -> None:
+    """pkv_kv_append_quant: quantize new tokens' K/V rows [n][H_kv][D] (f32,
+    f16 or bf16) into an fp8 cache at their slots."""
+    desc = _check_pools(k_cache, v_cache)
+    if k_cache.dtype not in _FP8:
+        raise TypeError("kv_append_quant writes fp8 caches")
+    _dev(k_new, "k_new")
+    _dev(v_new, "v_new", k_new.dtype)
+    _dev(slots, "slots", torch.int32)
+    n = int(slots.shape[0])
+    if k_new.shape != (n, desc.num_kv_heads, desc.head_dim) or v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new must be [n][H_kv][D]")
+    _check(lib().pkv_kv_append_quant(C.byref(desc), _p(k_cache), _p(v_cache), _p(k_new),
+                                     _p(v_new), _TORCH_TO_CODE[k_new.dtype], float(k_scale),
+                                     float(v_scale), _p(slots), n, _stream()))
+
+
+def decode_opts(q_dtype: torch.dtype, k_cache_dtype: torch.dtype, k_scale: float = 1.0,
+                v_scale: float = 1.0, window: int = 0, sink: int = 0) -> Optional[DecodeOpts]:
+    """pkv_decode_opts for the *_ex calls, or None when every option has its
+    default (plain calls)."""
+    if (q_dtype == k_cache_dtype and k_scale == 1.0 and v_scale == 1.0 and window == 0
+            and sink == 0):
+        return None
+    return DecodeOpts(_TORCH_TO_CODE[q_dtype], float(k_scale), float(v_scale), int(window),
+                      int(sink))
+
+
 def decode_plan(desc: CacheDesc, batch: int, num_q_heads: int, max_context_len: int,
-                split_tokens: int = 0) -> Tuple[int, int]:
-    """pkv_decode_plan: (n_split, workspace_bytes)."""
+                split_tokens: int = 0, opts: Optional[DecodeOpts] = None) -> Tuple[int, int]:
+    """pkv_decode_plan (pkv_decode_plan_ex with options): (n_split, workspace_bytes)."""
     n = C.c_int32(0)
     ws = C.c_size_t(0)
-    _check(lib().pkv_decode_plan(C.byref(desc), int(batch), int(num_q_heads),
-                                 int(max_context_len), int(split_tokens), C.byref(n),
-                                 C.byref(ws)))
+    if opts is None:
+        _check(lib().pkv_decode_plan(C.byref(desc), int(batch), int(num_q_heads),
+                                     int(max_context_len), int(split_tokens), C.byref(n),
+                                     C.byref(ws)))
+    else:
+        _check(lib().pkv_decode_plan_ex(C.byref(desc), int(batch), int(num_q_heads),
+                                        int(max_context_len), int(split_tokens), C.byref(opts),
+                                        C.byref(n), C.byref(ws)))
     return int(n.value), int(ws.value)
 
 
@@ -163,7 +214,12 @@ def partials_bytes(batch: int, num_q_heads: int, n_split: int, head_dim: int) ->
 
 def _decode_common(q, k_cache, v_cache, block_table, context_lens, max_context_len):
     desc = _check_pools(k_cache, v_cache)
-    _dev(q, "q", k_cache.dtype)
+    if k_cache.dtype in _FP8:
+        _dev(q, "q")
+        if q.dtype not in (torch.float16, torch.bfloat16):
+            raise TypeError("queries over an fp8 cache must be float16 or bfloat16")
+    else:
+        _dev(q, "q", k_cache.dtype)
     _dev(block_table, "block_table", torch.int32)
     _dev(context_lens, "context_lens", torch.int32)
     if q.dim() != 3 or q.shape[2] != desc.head_dim:
@@ -176,41 +232,56 @@ def _decode_common(q, k_cache, v_cache, block_table, context_lens, max_context_l
 
 def paged_attn_decode(q, k_cache, v_cache, block_table, context_lens, max_context_len: int,
                       scale: float, split_tokens: int = 0, out=None, lse_out=None,
-                      workspace=None, return_lse: bool = False):
-    """pkv_paged_attn_decode.  Returns out [B][H_q][D] (and lse [B][H_q])."""
+                      workspace=None, return_lse: bool = False, k_scale: float = 1.0,
+                      v_scale: float = 1.0, window: int = 0, sink: int = 0):
+    """pkv_paged_attn_decode (pkv_paged_attn_decode_ex when an fp8 cache, its
+    scales or a window are given).  Returns out [B][H_q][D] in q's dtype (and
+    lse [B][H_q])."""
     desc, batch, hq = _decode_common(q, k_cache, v_cache, block_table, context_lens,
                                      max_context_len)
+    opts = decode_opts(q.dtype, k_cache.dtype, k_scale, v_scale, window, sink)
     if out is None:
         out = torch.empty_like(q)
     if return_lse and lse_out is None:
         lse_out = torch.empty((batch, hq), dtype=torch.float32, device=q.device)
-    n_split, ws_bytes = decode_plan(desc, batch, hq, max_context_len, split_tokens)
+    n_split, ws_bytes = decode_plan(desc, batch, hq, max_context_len, split_tokens, opts)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().pkv_paged_attn_decode(
-        C.byref(desc), _p(k_cache), _p(v_cache), _p(q), batch, hq, _p(block_table),
-        int(block_table.shape[1]), _p(context_lens), int(max_context_len), float(scale),
-        int(split_tokens), _p(out), _p(lse_out), _p(workspace), ws_len, _stream()))
+    common = (C.byref(desc), _p(k_cache), _p(v_cache), _p(q), batch, hq, _p(block_table),
+              int(block_table.shape[1]), _p(context_lens), int(max_context_len), float(scale),
+              int(split_tokens))
+    tail = (_p(out), _p(lse_out), _p(workspace), ws_len, _stream())
+    if opts is None:
+        _check(lib().pkv_paged_attn_decode(*common, *tail))
+    else:
+        _check(lib().pkv_paged_attn_decode_ex(*common, C.byref(opts), *tail))
     return (out, lse_out) if return_lse else out
 
 
 def paged_attn_decode_partials(q, k_cache, v_cache, block_table, context_lens,
                                max_context_len: int, scale: float, split_tokens: int = 0,
-                               workspace=None):
-    """pkv_paged_attn_decode_partials.  Returns (o_parts [B*H_q][n][D],
-    lse_parts [B*H_q][n], workspace) as views of the workspace."""
+                               workspace=None, k_scale: float = 1.0, v_scale: float = 1.0,
+                               window: int = 0, sink: int = 0):
+    """pkv_paged_attn_decode_partials (or its _ex form).  Returns (o_parts
+    [B*H_q][n][D], lse_parts [B*H_q][n], workspace) as views of the
+    workspace."""
     desc, batch, hq = _decode_common(q, k_cache, v_cache, block_table, context_lens,
                                      max_context_len)
-    n_split, _ = decode_plan(desc, batch, hq, max_context_len, split_tokens)
+    opts = decode_opts(q.dtype, k_cache.dtype, k_scale, v_scale, window, sink)
+    n_split, _ = decode_plan(desc, batch, hq, max_context_len, split_tokens, opts)
     ob, total = partials_bytes(batch, hq, n_split, desc.head_dim)
     if workspace is None:
         workspace = torch.empty(total, dtype=torch.uint8, device=q.device)
     ws_len = workspace.numel() * workspace.element_size()
-    _check(lib().pkv_paged_attn_decode_partials(
-        C.byref(desc), _p(k_cache), _p(v_cache), _p(q), batch, hq, _p(block_table),
-        int(block_table.shape[1]), _p(context_lens), int(max_context_len), float(scale),
-        int(split_tokens), _p(workspace), ws_len, _stream()))
+    common = (C.byref(desc), _p(k_cache), _p(v_cache), _p(q), batch, hq, _p(block_table),
+              int(block_table.shape[1]), _p(context_lens), int(max_context_len), float(scale),
+              int(split_tokens))
+    if opts is None:
+        _check(lib().pkv_paged_attn_decode_partials(*common, _p(workspace), ws_len, _stream()))
+    else:
+        _check(lib().pkv_paged_attn_decode_partials_ex(*common, C.byref(opts), _p(workspace),
+                                                       ws_len, _stream()))
     rows = batch * hq
     o_parts = workspace[:rows * n_split * desc.head_dim * 4].view(torch.float32).view(
         rows, n_split, desc.head_dim)
@@ -300,16 +371,39 @@ def prepare_kv_append(k_cache, v_cache, k_new, v_new, slots) -> PreparedCall:
 
 def prepare_decode_partials(q, k_cache, v_cache, block_table, context_lens,
                             max_context_len: int, scale: float, split_tokens: int,
-                            workspace) -> PreparedCall:
+                            workspace, k_scale: float = 1.0, v_scale: float = 1.0,
+                            window: int = 0, sink: int = 0) -> PreparedCall:
     desc, batch, hq = _decode_common(q, k_cache, v_cache, block_table, context_lens,
                                      max_context_len)
+    opts = decode_opts(q.dtype, k_cache.dtype, k_scale, v_scale, window, sink)
     _dev(workspace, "workspace")
     ws_len = workspace.numel() * workspace.element_size()
-    args = (C.byref(desc), _p(k_cache), _p(v_cache), _p(q), batch, hq, _p(block_table),
-            int(block_table.shape[1]), _p(context_lens), int(max_context_len), float(scale),
-            int(split_tokens), _p(workspace), ws_len, _stream())
-    return PreparedCall(lib().pkv_paged_attn_decode_partials, args,
-                        (desc, q, k_cache, v_cache, block_table, context_lens, workspace))
+    common = (C.byref(desc), _p(k_cache), _p(v_cache), _p(q), batch, hq, _p(block_table),
+              int(block_table.shape[1]), _p(context_lens), int(max_context_len), float(scale),
+              int(split_tokens))
+    if opts is None:
+        fn, args = lib().pkv_paged_attn_decode_partials, common + (_p(workspace), ws_len,
+                                                                   _stream())
+    else:
+        fn = lib().pkv_paged_attn_decode_partials_ex
+        args = common + (C.byref(opts), _p(workspace), ws_len, _stream())
+    return PreparedCall(fn, args,
+                        (desc, opts, q, k_cache, v_cache, block_table, context_lens, workspace))
+
+
+def prepare_kv_append_quant(k_cache, v_cache, k_new, v_new, slots, k_scale: float,
+                            v_scale: float) -> PreparedCall:
+    desc = _check_pools(k_cache, v_cache)
+    if k_cache.dtype not in _FP8:
+        raise TypeError("kv_append_quant writes fp8 caches")
+    _dev(k_new, "k_new")
+    _dev(v_new, "v_new", k_new.dtype)
+    _dev(slots, "slots", torch.int32)
+    n = int(slots.shape[0])
+    args = (C.byref(desc), _p(k_cache), _p(v_cache), _p(k_new), _p(v_new),
+            _TORCH_TO_CODE[k_new.dtype], float(k_scale), float(v_scale), _p(slots), n, _stream())
+    return PreparedCall(lib().pkv_kv_append_quant, args,
+                        (desc, k_cache, v_cache, k_new, v_new, slots))
 
 
 def prepare_merge_states(o_parts, lse_parts, out, lse_out=None) -> PreparedCall:

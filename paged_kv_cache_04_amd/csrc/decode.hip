@@ -42,6 +42,21 @@
 //      For f32 the probabilities stay fp32 and PV is plain FMA.
 // Tokens past the end of the sequence (the tail of the last page) are
 // selected out, never multiplied by zero, so stale or NaN slots never leak.
+//
+// fp8 caches (OCP E4M3 / E5M2, one scale per pool): K vectors hold 16
+// elements, each widened exactly to the query's type (f16 or bf16) with the
+// hardware pair conversion right before the packed dot products; V rows of
+// two tokens are interleaved byte-wise with v_perm and widened into the same
+// token pairs the 16-bit path forms.  The K scale is folded into the softmax
+// scale, the V scale into the final normalisation.  Pages carry half the
+// bytes, so five pages per wave are kept in flight instead of three.
+//
+// Sliding window (page 4, section 2.3): with window w > 0 a sequence of L
+// keys shows keys t >= L - w and t < sink.  The visited logical pages are
+// [0, sp) (the sink) and [wp, n_pages) (the window); splits run over this
+// list of visited pages, so hidden pages cost nothing, not even a table
+// lookup.  Keys inside a visited page that are hidden are selected out like
+// the tail of the last page.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -54,45 +69,63 @@ constexpr int NW = kDecodeWaves;
 
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 
-template <typename TT, int D, int G>
+// QT: type of q and out; CT: type of the cache elements (QT itself, or an
+// fp8 type with QT f16 / bf16).
+template <typename QT, typename CT, int D, int G>
 struct DecodeCfg {
-  static constexpr int ES = TT::bytes;
+  static constexpr int ES = CT::bytes;       // cache element bytes
+  static constexpr int QES = QT::bytes;
+  static constexpr bool FP8 = CT::is_fp8;
   static constexpr int VEC = 16 / ES;        // elements per 16-byte K vector
   static constexpr int KL = 8;               // lanes per K row
   static constexpr int KT = 64 / KL;         // tokens per K pass
   static constexpr int KP = P / KT;          // K passes per page
   static constexpr int KV = D / (KL * VEC);  // 16-byte vectors per lane per K row
+  static constexpr int QW = VEC * QES / 16;  // 16-byte q vectors per K vector
   static constexpr int VE = 4;               // V elements per lane per token
-  static constexpr int VW = VE * ES / 4;     // 32-bit words of one V load (2 or 4)
+  static constexpr int VW = VE * ES / 4;     // 32-bit words of one V load (1, 2 or 4)
   static constexpr int DG = D / VE;          // lanes per V row
   static constexpr int TG = 64 / DG;         // V token groups
   static constexpr int VT = P / TG;          // V tokens per lane per page
   static constexpr int HSHIFT = 3 - ilog2(G);  // lane c owns head c >> HSHIFT
-  static constexpr bool PACKED = (ES == 2);  // packed-pair PV for 16-bit types
+  static constexpr bool PACKED = (QES == 2); // packed-pair PV for 16-bit queries
   // f16 probabilities are stored as p * 2^15
-  static constexpr float POFF = TT::is_f16 ? 15.f : 0.f;
+  static constexpr float POFF = QT::is_f16 ? 15.f : 0.f;
   // pages in flight per wave: the one being computed plus NB - 1 ahead
-  static constexpr int NB = (ES == 4) ? 2 : 3;
+  static constexpr int NB = FP8 ? 5 : ((ES == 4) ? 2 : 3);
   static_assert(KV >= 1 && KV * KL * VEC == D, "head_dim / vector mismatch");
+  static_assert(QW >= 1, "q vector layout");
   static_assert(TG >= 1 && VT * TG == P, "V layout mismatch");
   static_assert(!PACKED || VT % 2 == 0, "packed PV pairs tokens");
+  static_assert(!FP8 || QES == 2, "fp8 caches take f16 or bf16 queries");
+  static_assert(FP8 || ES == QES, "one element type unless the cache is fp8");
   static_assert(G >= 1 && G <= 8 && (G & (G - 1)) == 0, "group size");
 };
 
 // Partial dot product of one lane's slice of q and of a K row.
-template <typename TT, int KV>
-__device__ __forceinline__ float dot_slice(const u32x4 (&q)[KV], const u32x4 (&k)[KV]) {
+template <typename QT, typename CT, int KV, int QW>
+__device__ __forceinline__ float dot_slice(const u32x4 (&q)[KV][QW], const u32x4 (&k)[KV]) {
   float acc = 0.f;
-  if constexpr (TT::bytes == 4) {
+  if constexpr (CT::bytes == 4) {
 #pragma unroll
     for (int v = 0; v < KV; ++v)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc = fmaf(u2f(q[v].w[i]), u2f(k[v].w[i]), acc);
+      for (int i = 0; i < 4; ++i) acc = fmaf(u2f(q[v][0].w[i]), u2f(k[v].w[i]), acc);
+  } else if constexpr (CT::is_fp8) {
+    // k word i holds elements 4i .. 4i+3; q word j holds elements 2j, 2j+1
+#pragma unroll
+    for (int v = 0; v < KV; ++v)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t kw = k[v].w[i];
+        acc = QT::dot2(q[v][i / 2].w[(2 * i) % 4], CT::template cvt2<QT, false>(kw), acc);
+        acc = QT::dot2(q[v][i / 2].w[(2 * i) % 4 + 1], CT::template cvt2<QT, true>(kw), acc);
+      }
   } else {
 #pragma unroll
     for (int v = 0; v < KV; ++v)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc = TT::dot2(q[v].w[i], k[v].w[i], acc);
+      for (int i = 0; i < 4; ++i) acc = QT::dot2(q[v][0].w[i], k[v].w[i], acc);
   }
   return acc;
 }
@@ -136,16 +169,17 @@ __device__ __forceinline__ float sum_tokens(float x) {
   return x + xor_f(x, 32);
 }
 
-template <typename TT, int D, int G>
+template <typename QT, typename CT, int D, int G>
 struct PageRegs {
-  using C = DecodeCfg<TT, D, G>;
+  using C = DecodeCfg<QT, CT, D, G>;
   u32x4 k[C::KP][C::KV];
   uint32_t v[C::VT][C::VW];
 };
 
-template <typename TT, int D, int G>
+template <typename QT, typename CT, int D, int G>
 __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeArgs a) {
-  using C = DecodeCfg<TT, D, G>;
+  using C = DecodeCfg<QT, CT, D, G>;
+  using TT = QT;
   constexpr int ES = C::ES, VEC = C::VEC;
   // probabilities of the current page: packed pairs (16-bit) or floats [t][h]
   constexpr int PWORDS = C::PACKED ? (P / 2) * G : P * G;
@@ -166,15 +200,32 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeArgs a) {
   const int b = bid / a.num_kv_heads;
   const int hq0 = g * G;
 
-  // Pages reachable through the grid and the table row; a length outside
-  // [0, that * P] breaks a precondition: clamp it and poison the row.
-  const int cover = min(a.n_split * a.pages_per_split, a.stride);
+  // A length outside [0, stride * P], or more visited pages than the grid
+  // covers, breaks a precondition: clamp and poison the row.
   int L = a.context_lens[b];
-  const bool len_bad = (L < 0) || (L > cover * P);
-  L = len_bad ? max(0, min(L, cover * P)) : L;
+  bool len_bad = (L < 0) || (L > a.stride * P);
+  L = max(0, min(L, a.stride * P));
   const int n_pages = (L + P - 1) / P;
+  // visible keys: t >= lo, and t < sink_n (without a window: all of them)
+  int lo = 0, sink_n = 0;
+  if (a.window > 0) {
+    lo = max(0, L - a.window);
+    sink_n = min(a.sink, L);
+  }
+  // visited pages: logical [0, sp) then [wp, n_pages); virtual page v is
+  // logical page v (v < sp) or v + gap
+  const int sp = lo > 0 ? (sink_n + P - 1) / P : 0;
+  const int wp = max(sp, lo / P);
+  const int gap = wp - sp;
+  int n_vp = n_pages - gap;
+  const int cover = a.n_split * a.pages_per_split;
+  if (n_vp > cover) {
+    len_bad = true;
+    n_vp = cover;
+  }
   const int p0 = ks * a.pages_per_split;
-  const int p1 = min(n_pages, p0 + a.pages_per_split);
+  const int p1 = min(n_vp, p0 + a.pages_per_split);
+  auto lpage = [&](int v) { return v < sp ? v : v + gap; };
 
   if (p0 >= p1) {  // empty split: no keys, o = 0 and lse = -inf
     for (int idx = tid; idx < G * D; idx += NW * 64) {
@@ -203,14 +254,16 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeArgs a) {
   const int dg = lane % C::DG;
   const int tg = lane / C::DG;
 
-  u32x4 qv[G][C::KV];
+  u32x4 qv[G][C::KV][C::QW];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int v = 0; v < C::KV; ++v)
-      qv[h][v] = load16((const char*)a.q +
-                        (((int64_t)b * a.num_q_heads + hq0 + h) * D + v * C::KL * VEC + c * VEC) *
-                            ES);
+#pragma unroll
+      for (int qw = 0; qw < C::QW; ++qw)
+        qv[h][v][qw] = load16((const char*)a.q +
+                              (((int64_t)b * a.num_q_heads + hq0 + h) * D + v * C::KL * VEC +
+                               c * VEC) * C::QES + 16 * qw);
 
   float m_own = -INFINITY, l_own = 0.f;
   float acc[G][C::VE];
@@ -229,10 +282,10 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeArgs a) {
   // Issue the loads of this wave's i-th page into r.  The wave's page ids are
   // staged in LDS 64 at a time, so a lookup waits only on LDS, never on the
   // K/V loads in flight (those drain only at a refill, once per 64 pages).
-  auto issue = [&](PageRegs<TT, D, G>& r, int i) {
+  auto issue = [&](PageRegs<QT, CT, D, G>& r, int i) {
     if ((i & 63) == 0) {
       const int idx = i + lane;
-      const int v = idx < my_pages ? bt_row[p0 + w + NW * idx] : 0;
+      const int v = idx < my_pages ? bt_row[lpage(p0 + w + NW * idx)] : 0;
       wave_lds_sync();
       pid_lds[w][lane] = v;
       wave_lds_sync();
@@ -253,7 +306,9 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < C::VT; ++j) {
       const char* src = vb + ((tg + C::TG * j) * D + dg * C::VE) * ES;
-      if constexpr (C::VW == 2) {
+      if constexpr (C::VW == 1) {
+        r.v[j][0] = load4_stream(src);
+      } else if constexpr (C::VW == 2) {
         const u32x2 x = load8_stream(src);
         r.v[j][0] = x.w[0];
         r.v[j][1] = x.w[1];
@@ -266,19 +321,22 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeArgs a) {
   };
 
   // Online-softmax update with the wave's i-th page held in r.
-  auto compute = [&](const PageRegs<TT, D, G>& r, int i) {
-    const int pi = p0 + w + NW * i;  // logical page index
+  // key t of a visited page is visible
+  auto vis = [&](int t) { return t < L && (t >= lo || t < sink_n); };
+  auto compute = [&](const PageRegs<QT, CT, D, G>& r, int i) {
+    const int pi = lpage(p0 + w + NW * i);  // logical page index
     const int t0 = pi * P;
-    const bool partial = t0 + P > L;
+    // some key of the page is past the end or hidden by the window
+    const bool partial = t0 + P > L || max(t0, sink_n) < min(t0 + P, lo);
 
     float s[C::KP];
 #pragma unroll
     for (int rr = 0; rr < C::KP; ++rr) {
       float part[8];
 #pragma unroll
-      for (int h = 0; h < G; ++h) part[h] = dot_slice<TT, C::KV>(qv[h], r.k[rr]);
+      for (int h = 0; h < G; ++h) part[h] = dot_slice<QT, CT, C::KV, C::QW>(qv[h], r.k[rr]);
       const float sc = reduce_heads<G>(part, c) * a.scale_log2;
-      const bool valid = !partial || (t0 + tk + C::KT * rr < L);
+      const bool valid = !partial || vis(t0 + tk + C::KT * rr);
       s[rr] = valid ? sc : -INFINITY;
     }
 
@@ -325,7 +383,7 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeArgs a) {
       for (int pp = 0; pp < C::VT / 2; ++pp) {
         const int ta = tg + C::TG * 2 * pp, tb = ta + C::TG;
         uint32_t wa[C::VW], wb[C::VW];
-        const bool va = !partial || (t0 + ta < L), vb_ok = !partial || (t0 + tb < L);
+        const bool va = !partial || vis(t0 + ta), vb_ok = !partial || vis(t0 + tb);
 #pragma unroll
         for (int e = 0; e < C::VW; ++e) {
           wa[e] = va ? r.v[2 * pp][e] : 0u;
@@ -334,14 +392,28 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeArgs a) {
         uint32_t pr[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) pr[h] = pw[(tg + C::TG * pp) * G + h];
+        if constexpr (C::FP8) {
+          // bytes (a0 b0 a1 b1) and (a2 b2 a3 b3), widened to (a_e, b_e) pairs
+          const uint32_t x0 = __builtin_amdgcn_perm(wb[0], wa[0], 0x05010400u);
+          const uint32_t x1 = __builtin_amdgcn_perm(wb[0], wa[0], 0x07030602u);
+          const uint32_t y[4] = {CT::template cvt2<QT, false>(x0),
+                                 CT::template cvt2<QT, true>(x0),
+                                 CT::template cvt2<QT, false>(x1),
+                                 CT::template cvt2<QT, true>(x1)};
 #pragma unroll
-        for (int i2 = 0; i2 < C::VW; ++i2) {
-          const uint32_t lo = __builtin_amdgcn_perm(wb[i2], wa[i2], 0x05040100u);
-          const uint32_t hi = __builtin_amdgcn_perm(wb[i2], wa[i2], 0x07060302u);
+          for (int h = 0; h < G; ++h)
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            acc[h][2 * i2] = TT::dot2(pr[h], lo, acc[h][2 * i2]);
-            acc[h][2 * i2 + 1] = TT::dot2(pr[h], hi, acc[h][2 * i2 + 1]);
+            for (int e = 0; e < 4; ++e) acc[h][e] = TT::dot2(pr[h], y[e], acc[h][e]);
+        } else {
+#pragma unroll
+          for (int i2 = 0; i2 < C::VW; ++i2) {
+            const uint32_t lo2 = __builtin_amdgcn_perm(wb[i2], wa[i2], 0x05040100u);
+            const uint32_t hi2 = __builtin_amdgcn_perm(wb[i2], wa[i2], 0x07060302u);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+              acc[h][2 * i2] = TT::dot2(pr[h], lo2, acc[h][2 * i2]);
+              acc[h][2 * i2 + 1] = TT::dot2(pr[h], hi2, acc[h][2 * i2 + 1]);
+            }
           }
         }
       }
@@ -349,7 +421,7 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < C::VT; ++j) {
         const int t = tg + C::TG * j;
-        const bool valid = !partial || (t0 + t < L);
+        const bool valid = !partial || vis(t0 + t);
         const float* pf = reinterpret_cast<const float*>(pw) + t * G;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -364,7 +436,7 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeArgs a) {
 
   {
     // software pipeline: NB register buffers, loads issued NB - 1 pages ahead
-    PageRegs<TT, D, G> rb[C::NB];
+    PageRegs<QT, CT, D, G> rb[C::NB];
 #pragma unroll
     for (int j = 0; j < C::NB - 1; ++j)
       if (j < my_pages) issue(rb[j], j);
@@ -395,7 +467,8 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeArgs a) {
     red_l[w][h_own] = l_own;
   }
   if (tg == 0) {
-    constexpr float unscale = C::POFF != 0.f ? 1.f / 32768.f : 1.f;
+    // undo the f16 probability offset 2^15 (exact) and apply the V scale
+    const float unscale = (C::POFF != 0.f ? 1.f / 32768.f : 1.f) * a.v_scale;
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -435,16 +508,16 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeArgs a) {
   }
 }
 
-template <typename TT, int D>
+template <typename QT, typename CT, int D>
 hipError_t launch_g(int group, int batch, const DecodeArgs& a, hipStream_t stream) {
   const int64_t blocks = (int64_t)batch * a.num_kv_heads * a.n_split;
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)blocks), block(NW * 64);
   switch (group) {
-    case 1: hipLaunchKernelGGL((decode_kernel<TT, D, 1>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<TT, D, 2>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<TT, D, 4>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((decode_kernel<TT, D, 8>), grid, block, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((decode_kernel<QT, CT, D, 1>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<QT, CT, D, 2>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<QT, CT, D, 4>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((decode_kernel<QT, CT, D, 8>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -454,20 +527,37 @@ template <typename TT>
 hipError_t launch_d(int head_dim, int group, int batch, const DecodeArgs& a,
                     hipStream_t stream) {
   switch (head_dim) {
-    case 64: return launch_g<TT, 64>(group, batch, a, stream);
-    case 128: return launch_g<TT, 128>(group, batch, a, stream);
+    case 64: return launch_g<TT, TT, 64>(group, batch, a, stream);
+    case 128: return launch_g<TT, TT, 128>(group, batch, a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// fp8 caches: head_dim 128, f16 or bf16 queries
+template <typename CT>
+hipError_t launch_fp8(int q_dtype, int head_dim, int group, int batch, const DecodeArgs& a,
+                      hipStream_t stream) {
+  if (head_dim != 128) return hipErrorInvalidValue;
+  switch (q_dtype) {
+    case 1: return launch_g<TF16, CT, 128>(group, batch, a, stream);
+    case 2: return launch_g<TBF16, CT, 128>(group, batch, a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode(int dtype, int head_dim, int group, int batch, const DecodeArgs& a,
-                         hipStream_t stream) {
-  switch (dtype) {
-    case 0: return launch_d<TF32>(head_dim, group, batch, a, stream);
-    case 1: return launch_d<TF16>(head_dim, group, batch, a, stream);
-    case 2: return launch_d<TBF16>(head_dim, group, batch, a, stream);
+hipError_t launch_decode(int kv_dtype, int q_dtype, int head_dim, int group, int batch,
+                         const DecodeArgs& a, hipStream_t stream) {
+  switch (kv_dtype) {
+    case 0: return q_dtype == 0 ? launch_d<TF32>(head_dim, group, batch, a, stream)
+                                : hipErrorInvalidValue;
+    case 1: return q_dtype == 1 ? launch_d<TF16>(head_dim, group, batch, a, stream)
+                                : hipErrorInvalidValue;
+    case 2: return q_dtype == 2 ? launch_d<TBF16>(head_dim, group, batch, a, stream)
+                                : hipErrorInvalidValue;
+    case 3: return launch_fp8<TFP8E4M3>(q_dtype, head_dim, group, batch, a, stream);
+    case 4: return launch_fp8<TFP8E5M2>(q_dtype, head_dim, group, batch, a, stream);
     default: return hipErrorInvalidValue;
   }
 }

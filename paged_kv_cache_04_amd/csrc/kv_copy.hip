@@ -1,9 +1,9 @@
 // kv_append and gather: the paged address rule as plain copies.
 //
-// A token's K/V row for one KV head is D elements, 128 or 256 bytes for the
-// 16-bit types and 256 or 512 for f32: always a whole number of 16-byte
-// vectors.  Each thread moves one 16-byte vector, so a wavefront moves 1 KiB
-// with fully coalesced loads and stores.  The slot of a token (slot = page *
+// A token's K/V row for one KV head is D elements, 64 or 128 bytes for fp8,
+// 128 or 256 bytes for the 16-bit types and 256 or 512 for f32: always a
+// whole number of 16-byte vectors.  Each thread moves one 16-byte vector, so
+// a wavefront moves 1 KiB with fully coalesced loads and stores.  The slot of a token (slot = page *
 // P + offset) gives page = slot / P and offset = slot % P (page 3, section
 // 3.2: the page of token t is page_table[t / PAGE_SIZE]).
 #include "pkv_device.h"
@@ -77,7 +77,93 @@ __global__ __launch_bounds__(kCopyThreads) void gather_kernel(
   }
 }
 
-int elem_size(int dtype) { return dtype == 0 ? 4 : 2; }
+// Four fp32 values to four fp8 codes (byte e from y[e]): values beyond the
+// largest finite one are clipped to it first (the conversion itself rounds
+// to nearest even and does not saturate), NaN becomes 0x7F.
+template <bool E4M3>
+__device__ __forceinline__ uint32_t fp8_pack4(const float (&y)[4]) {
+  constexpr float kMax = E4M3 ? 448.f : 57344.f;
+  float c[4];
+  uint32_t nan_mask = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    nan_mask |= (y[e] != y[e]) ? (0xffu << (8 * e)) : 0u;
+    c[e] = fminf(fmaxf(y[e], -kMax), kMax);
+  }
+  uint32_t w;
+  if constexpr (E4M3) {
+    w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+    w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], (int)w, true);
+  } else {
+    w = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c[0], c[1], 0, false);
+    w = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c[2], c[3], (int)w, true);
+  }
+  return (w & ~nan_mask) | (0x7f7f7f7fu & nan_mask);
+}
+
+// Source element i of a 16-byte vector group, widened exactly to fp32.
+template <typename ST>
+__device__ __forceinline__ float src_elem(const u32x4 (&v)[4], int i);
+template <>
+__device__ __forceinline__ float src_elem<TF32>(const u32x4 (&v)[4], int i) {
+  return u2f(v[i / 4].w[i % 4]);
+}
+template <>
+__device__ __forceinline__ float src_elem<TF16>(const u32x4 (&v)[4], int i) {
+  const uint32_t w = v[i / 8].w[(i % 8) / 2];
+  return (i & 1) ? TF16::hi(w) : TF16::lo(w);
+}
+template <>
+__device__ __forceinline__ float src_elem<TBF16>(const u32x4 (&v)[4], int i) {
+  const uint32_t w = v[i / 8].w[(i % 8) / 2];
+  return (i & 1) ? TBF16::hi(w) : TBF16::lo(w);
+}
+
+// One thread per (K or V, token, head, group of 16 elements): reads the 16
+// source elements, divides by the pool's scale in IEEE fp32, writes 16 fp8
+// codes as one 16-byte store.
+template <typename ST, bool E4M3>
+__global__ __launch_bounds__(kCopyThreads) void kv_append_quant_kernel(
+    char* __restrict__ k_cache, char* __restrict__ v_cache, const char* __restrict__ k_new,
+    const char* __restrict__ v_new, float k_scale, float v_scale,
+    const int32_t* __restrict__ slots, int32_t n_tokens, int32_t num_kv_heads, int32_t row_vecs,
+    int64_t num_slots) {
+  constexpr int SB = ST::bytes;          // source bytes per element
+  const int64_t per_tok = (int64_t)num_kv_heads * row_vecs;
+  const int64_t total = 2 * (int64_t)n_tokens * per_tok;
+  for (int64_t idx = (int64_t)blockIdx.x * kCopyThreads + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * kCopyThreads) {
+    const int which = idx >= (int64_t)n_tokens * per_tok;   // 0: K, 1: V
+    const int64_t r = which ? idx - (int64_t)n_tokens * per_tok : idx;
+    const int64_t i = r / per_tok;
+    const int64_t rem = r - i * per_tok;
+    const int64_t g = rem / row_vecs;
+    const int64_t vec = rem - g * row_vecs;
+    const int64_t s = slots[i];
+    if (s < 0 || s >= num_slots) continue;
+    const int64_t page = s / kPageSize;
+    const int64_t off = s - page * kPageSize;
+    const int64_t row_bytes = (int64_t)row_vecs * 16;          // fp8: D bytes
+    const int64_t dst = ((page * num_kv_heads + g) * kPageSize + off) * row_bytes + vec * 16;
+    const char* src =
+        (which ? v_new : k_new) + ((i * num_kv_heads + g) * row_vecs + vec) * 16 * SB;
+    const float scale = which ? v_scale : k_scale;
+    u32x4 in[4];
+#pragma unroll
+    for (int j = 0; j < SB; ++j) in[j] = load16(src + 16 * j);
+    u32x4 out;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = __fdiv_rn(src_elem<ST>(in, 4 * q + e), scale);
+      out.w[q] = fp8_pack4<E4M3>(y);
+    }
+    store16((which ? v_cache : k_cache) + dst, out);
+  }
+}
+
+int elem_size(int dtype) { return dtype == 0 ? 4 : (dtype >= 3 ? 1 : 2); }
 
 unsigned grid_for(int64_t total) {
   int64_t blocks = (total + kCopyThreads - 1) / kCopyThreads;
@@ -86,7 +172,50 @@ unsigned grid_for(int64_t total) {
   return (unsigned)blocks;
 }
 
+template <typename ST>
+hipError_t launch_quant_t(bool e4m3, int head_dim, int num_kv_heads, int64_t num_pages,
+                          void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                          float k_scale, float v_scale, const int32_t* slots, int32_t n_tokens,
+                          hipStream_t stream) {
+  const int row_vecs = head_dim / 16;
+  const int64_t total = 2 * (int64_t)n_tokens * num_kv_heads * row_vecs;
+  const dim3 grid(grid_for(total)), block(kCopyThreads);
+  if (e4m3)
+    hipLaunchKernelGGL((kv_append_quant_kernel<ST, true>), grid, block, 0, stream,
+                       (char*)k_cache, (char*)v_cache, (const char*)k_new, (const char*)v_new,
+                       k_scale, v_scale, slots, n_tokens, num_kv_heads, row_vecs,
+                       num_pages * kPageSize);
+  else
+    hipLaunchKernelGGL((kv_append_quant_kernel<ST, false>), grid, block, 0, stream,
+                       (char*)k_cache, (char*)v_cache, (const char*)k_new, (const char*)v_new,
+                       k_scale, v_scale, slots, n_tokens, num_kv_heads, row_vecs,
+                       num_pages * kPageSize);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_kv_append_quant(int fp8_dtype, int src_dtype, int head_dim, int num_kv_heads,
+                                  int64_t num_pages, void* k_cache, void* v_cache,
+                                  const void* k_new, const void* v_new, float k_scale,
+                                  float v_scale, const int32_t* slots, int32_t n_tokens,
+                                  hipStream_t stream) {
+  if (n_tokens == 0) return hipSuccess;
+  if (fp8_dtype != 3 && fp8_dtype != 4) return hipErrorInvalidValue;
+  const bool e4m3 = fp8_dtype == 3;
+  switch (src_dtype) {
+    case 0: return launch_quant_t<TF32>(e4m3, head_dim, num_kv_heads, num_pages, k_cache,
+                                        v_cache, k_new, v_new, k_scale, v_scale, slots,
+                                        n_tokens, stream);
+    case 1: return launch_quant_t<TF16>(e4m3, head_dim, num_kv_heads, num_pages, k_cache,
+                                        v_cache, k_new, v_new, k_scale, v_scale, slots,
+                                        n_tokens, stream);
+    case 2: return launch_quant_t<TBF16>(e4m3, head_dim, num_kv_heads, num_pages, k_cache,
+                                         v_cache, k_new, v_new, k_scale, v_scale, slots,
+                                         n_tokens, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_kv_append(int dtype, int head_dim, int num_kv_heads, int64_t num_pages,
                             void* k_cache, void* v_cache, const void* k_new, const void* v_new,

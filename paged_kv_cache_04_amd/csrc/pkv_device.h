@@ -52,6 +52,10 @@ __device__ __forceinline__ u32x4 load16_stream(const void* p) {
   return r;
 }
 
+__device__ __forceinline__ uint32_t load4_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+
 __device__ __forceinline__ u32x2 load8_stream(const void* p) {
   const u32v2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32v2_t*>(p));
   u32x2 r;
@@ -76,6 +80,7 @@ __device__ __forceinline__ float u2f(uint32_t u) { return __uint_as_float(u); }
 struct TF32 {
   static constexpr int bytes = 4;
   static constexpr bool is_f16 = false;
+  static constexpr bool is_fp8 = false;
   static __device__ __forceinline__ float lo(uint32_t u) { return u2f(u); }
   static __device__ __forceinline__ float store_cvt(float x) { return x; }
 };
@@ -83,6 +88,7 @@ struct TF32 {
 struct TF16 {
   static constexpr int bytes = 2;
   static constexpr bool is_f16 = true;
+  static constexpr bool is_fp8 = false;
   static __device__ __forceinline__ float lo(uint32_t u) {
     return (float)__builtin_bit_cast(half2_t, u).x;
   }
@@ -102,6 +108,7 @@ struct TF16 {
 struct TBF16 {
   static constexpr int bytes = 2;
   static constexpr bool is_f16 = false;
+  static constexpr bool is_fp8 = false;
   static __device__ __forceinline__ float lo(uint32_t u) { return u2f(u << 16); }
   static __device__ __forceinline__ float hi(uint32_t u) { return u2f(u & 0xffff0000u); }
   static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
@@ -110,6 +117,36 @@ struct TBF16 {
   }
   static __device__ __forceinline__ uint16_t from_float(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);    // round to nearest even
+  }
+};
+
+// fp8 cache elements (OCP E4M3 / E5M2).  cvt2<QT, HI>(w) widens the two fp8
+// values in bytes 0-1 (HI = false) or 2-3 (HI = true) of w into a packed
+// pair of QT (f16 or bf16), low half from the lower byte.  Every E4M3 and
+// E5M2 value is exact in f16 and in bf16, so the widening is exact.
+struct TFP8E4M3 {
+  static constexpr int bytes = 1;
+  static constexpr bool is_f16 = false;
+  static constexpr bool is_fp8 = true;
+  template <typename QT, bool HI>
+  static __device__ __forceinline__ uint32_t cvt2(uint32_t w) {
+    if constexpr (QT::is_f16)
+      return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, HI));
+    else
+      return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, HI));
+  }
+};
+
+struct TFP8E5M2 {
+  static constexpr int bytes = 1;
+  static constexpr bool is_f16 = false;
+  static constexpr bool is_fp8 = true;
+  template <typename QT, bool HI>
+  static __device__ __forceinline__ uint32_t cvt2(uint32_t w) {
+    if constexpr (QT::is_f16)
+      return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.f, HI));
+    else
+      return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.f, HI));
   }
 };
 

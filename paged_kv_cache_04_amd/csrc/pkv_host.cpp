@@ -30,15 +30,25 @@ int ok() {
   return PKV_OK;
 }
 
-int elem_bytes(int dtype) { return dtype == PKV_F32 ? 4 : 2; }
+bool is_fp8(int dtype) { return dtype == PKV_FP8_E4M3 || dtype == PKV_FP8_E5M2; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int check_dtype(int dtype) {
-  if (dtype != PKV_F32 && dtype != PKV_F16 && dtype != PKV_BF16)
+  if (dtype != PKV_F32 && dtype != PKV_F16 && dtype != PKV_BF16 && !is_fp8(dtype))
     return fail(PKV_ERR_INVALID, "dtype %d is not a pkv_dtype", dtype);
   return PKV_OK;
 }
+
+// Types of queries and outputs: f32, f16, bf16.
+int check_value_dtype(int dtype, const char* what) {
+  if (dtype != PKV_F32 && dtype != PKV_F16 && dtype != PKV_BF16)
+    return fail(is_fp8(dtype) ? PKV_ERR_UNSUPPORTED : PKV_ERR_INVALID,
+                "%s dtype %d: f32, f16 or bf16 expected", what, dtype);
+  return PKV_OK;
+}
+
+bool finite_positive(float x) { return x > 0.f && x <= 3.4028234663852886e38f; }
 
 int check_desc(const pkv_cache_desc* d) {
   if (!d) return fail(PKV_ERR_INVALID, "desc is NULL");
@@ -122,13 +132,58 @@ int make_plan(const pkv_cache_desc* d, int32_t batch, int32_t num_q_heads,
 struct DecodeCommon {
   int group;
   Plan plan;
+  pkv_decode_opts opts;   // resolved (defaults filled in)
 };
+
+// Options with their defaults, checked against the cache descriptor.
+int resolve_opts(const pkv_cache_desc* desc, const pkv_decode_opts* in, pkv_decode_opts* out) {
+  if (in) {
+    *out = *in;
+  } else {
+    out->q_dtype = desc->dtype;
+    out->k_scale = 1.f;
+    out->v_scale = 1.f;
+    out->window = 0;
+    out->sink = 0;
+  }
+  if (is_fp8(desc->dtype)) {
+    if (out->q_dtype != PKV_F16 && out->q_dtype != PKV_BF16)
+      return fail(in ? PKV_ERR_UNSUPPORTED : PKV_ERR_INVALID,
+                  "fp8 caches need pkv_decode_opts with q_dtype f16 or bf16 (got %d)",
+                  out->q_dtype);
+    if (desc->head_dim != 128)
+      return fail(PKV_ERR_UNSUPPORTED, "fp8 caches are built for head_dim 128 (got %d)",
+                  desc->head_dim);
+    if (!finite_positive(out->k_scale) || !finite_positive(out->v_scale))
+      return fail(PKV_ERR_INVALID, "k_scale and v_scale must be finite and > 0");
+  } else {
+    if (out->q_dtype != desc->dtype)
+      return fail(PKV_ERR_INVALID, "q_dtype %d differs from the cache dtype %d", out->q_dtype,
+                  desc->dtype);
+    if (out->k_scale != 1.f || out->v_scale != 1.f)
+      return fail(PKV_ERR_INVALID, "k_scale / v_scale apply to fp8 caches only (must be 1)");
+  }
+  if (out->window < 0 || out->sink < 0)
+    return fail(PKV_ERR_INVALID, "window %d and sink %d must be >= 0", out->window, out->sink);
+  return PKV_OK;
+}
+
+// Upper bound on the keys a sequence of at most max_len keys exposes to the
+// split plan: with a window, only its pages and the sink's are visited.
+int32_t plan_len(int32_t max_len, const pkv_decode_opts& o, int P) {
+  if (o.window <= 0) return max_len;
+  const int64_t pages = ((int64_t)o.sink + P - 1) / P + ((int64_t)o.window + P - 1) / P + 1;
+  const int64_t bound = pages * P;
+  return bound < max_len ? (int32_t)bound : max_len;
+}
 
 int check_decode(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache,
                  const void* q, int32_t batch, int32_t num_q_heads, const int32_t* block_table,
                  int32_t stride, const int32_t* context_lens, int32_t max_context_len,
-                 float scale, int32_t split_tokens, DecodeCommon* dc) {
+                 float scale, int32_t split_tokens, const pkv_decode_opts* opts,
+                 DecodeCommon* dc) {
   if (int rc = check_desc(desc)) return rc;
+  if (int rc = resolve_opts(desc, opts, &dc->opts)) return rc;
   if (int rc = check_heads(desc, num_q_heads, &dc->group)) return rc;
   if (batch < 0) return fail(PKV_ERR_INVALID, "batch %d < 0", batch);
   if (stride <= 0) return fail(PKV_ERR_INVALID, "block_table_stride %d <= 0", stride);
@@ -142,7 +197,9 @@ int check_decode(const pkv_cache_desc* desc, const void* k_cache, const void* v_
     if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q))
       return fail(PKV_ERR_INVALID, "k_cache, v_cache and q must be 16-byte aligned");
   }
-  if (int rc = make_plan(desc, batch, num_q_heads, max_context_len, split_tokens, &dc->plan))
+  if (int rc = make_plan(desc, batch, num_q_heads,
+                         plan_len(max_context_len, dc->opts, desc->page_size), split_tokens,
+                         &dc->plan))
     return rc;
   const int64_t blocks = (int64_t)batch * desc->num_kv_heads * dc->plan.n_split;
   if (blocks > 0x7fffffff) return fail(PKV_ERR_INVALID, "grid too large (%lld)", (long long)blocks);
@@ -152,7 +209,8 @@ int check_decode(const pkv_cache_desc* desc, const void* k_cache, const void* v_
 pkv::DecodeArgs decode_args(const pkv_cache_desc* desc, const void* k_cache,
                             const void* v_cache, const void* q, int32_t num_q_heads,
                             const int32_t* block_table, int32_t stride,
-                            const int32_t* context_lens, float scale, const Plan& plan) {
+                            const int32_t* context_lens, float scale, const DecodeCommon& dc) {
+  const Plan& plan = dc.plan;
   pkv::DecodeArgs a{};
   a.k_cache = k_cache;
   a.v_cache = v_cache;
@@ -165,8 +223,97 @@ pkv::DecodeArgs decode_args(const pkv_cache_desc* desc, const void* k_cache,
   a.num_q_heads = num_q_heads;
   a.pages_per_split = plan.pages_per_split;
   a.n_split = plan.n_split;
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634 * (double)dc.opts.k_scale);
+  a.v_scale = dc.opts.v_scale;
+  a.window = dc.opts.window;
+  a.sink = dc.opts.sink;
   return a;
+}
+
+int decode_impl(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache,
+                const void* q, int32_t batch, int32_t num_q_heads, const int32_t* block_table,
+                int32_t block_table_stride, const int32_t* context_lens, int32_t max_context_len,
+                float scale, int32_t split_tokens, const pkv_decode_opts* opts, void* out,
+                float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
+  DecodeCommon dc;
+  if (int rc = check_decode(desc, k_cache, v_cache, q, batch, num_q_heads, block_table,
+                            block_table_stride, context_lens, max_context_len, scale,
+                            split_tokens, opts, &dc))
+    return rc;
+  if (batch == 0) return ok();
+  if (!out) return fail(PKV_ERR_INVALID, "out is NULL");
+  pkv::DecodeArgs a = decode_args(desc, k_cache, v_cache, q, num_q_heads, block_table,
+                                  block_table_stride, context_lens, scale, dc);
+  hipStream_t s = (hipStream_t)stream;
+  const int qdt = dc.opts.q_dtype;
+  if (dc.plan.n_split == 1) {
+    a.direct = 1;
+    a.out = out;
+    a.lse_out = lse_out;
+    return hip_status(
+        pkv::launch_decode(desc->dtype, qdt, desc->head_dim, dc.group, batch, a, s),
+        "decode launch");
+  }
+  if (!workspace || workspace_bytes < dc.plan.ws_bytes)
+    return fail(PKV_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes,
+                dc.plan.ws_bytes);
+  if (!aligned16(workspace)) return fail(PKV_ERR_INVALID, "workspace must be 16-byte aligned");
+  a.direct = 0;
+  a.o_part = (float*)workspace;
+  a.lse_part = (float*)((char*)workspace + dc.plan.o_bytes);
+  if (int rc = hip_status(
+          pkv::launch_decode(desc->dtype, qdt, desc->head_dim, dc.group, batch, a, s),
+          "decode launch"))
+    return rc;
+  return hip_status(pkv::launch_merge(qdt, desc->head_dim, a.o_part, a.lse_part,
+                                      batch * num_q_heads, dc.plan.n_split, out, lse_out, s),
+                    "merge launch");
+}
+
+int partials_impl(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache,
+                  const void* q, int32_t batch, int32_t num_q_heads, const int32_t* block_table,
+                  int32_t block_table_stride, const int32_t* context_lens,
+                  int32_t max_context_len, float scale, int32_t split_tokens,
+                  const pkv_decode_opts* opts, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  DecodeCommon dc;
+  if (int rc = check_decode(desc, k_cache, v_cache, q, batch, num_q_heads, block_table,
+                            block_table_stride, context_lens, max_context_len, scale,
+                            split_tokens, opts, &dc))
+    return rc;
+  if (batch == 0) return ok();
+  if (!workspace || workspace_bytes < dc.plan.ws_bytes)
+    return fail(PKV_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes,
+                dc.plan.ws_bytes);
+  if (!aligned16(workspace)) return fail(PKV_ERR_INVALID, "workspace must be 16-byte aligned");
+  pkv::DecodeArgs a = decode_args(desc, k_cache, v_cache, q, num_q_heads, block_table,
+                                  block_table_stride, context_lens, scale, dc);
+  a.direct = 0;
+  a.o_part = (float*)workspace;
+  a.lse_part = (float*)((char*)workspace + dc.plan.o_bytes);
+  return hip_status(pkv::launch_decode(desc->dtype, dc.opts.q_dtype, desc->head_dim, dc.group,
+                                       batch, a, (hipStream_t)stream),
+                    "decode launch");
+}
+
+int plan_impl(const pkv_cache_desc* desc, int32_t batch, int32_t num_q_heads,
+              int32_t max_context_len, int32_t split_tokens, const pkv_decode_opts* opts,
+              int32_t* n_split, size_t* workspace_bytes) {
+  if (int rc = check_desc(desc)) return rc;
+  pkv_decode_opts o;
+  if (int rc = resolve_opts(desc, opts, &o)) return rc;
+  int group = 0;
+  if (int rc = check_heads(desc, num_q_heads, &group)) return rc;
+  if (batch < 0) return fail(PKV_ERR_INVALID, "batch %d < 0", batch);
+  if (max_context_len < 0) return fail(PKV_ERR_INVALID, "max_context_len %d < 0", max_context_len);
+  if (!n_split || !workspace_bytes) return fail(PKV_ERR_INVALID, "NULL output pointer");
+  Plan plan;
+  if (int rc = make_plan(desc, batch, num_q_heads,
+                         plan_len(max_context_len, o, desc->page_size), split_tokens, &plan))
+    return rc;
+  *n_split = plan.n_split;
+  *workspace_bytes = plan.n_split > 1 ? plan.ws_bytes : 0;
+  return ok();
 }
 
 }  // namespace
@@ -212,18 +359,15 @@ int pkv_gather_kv(const pkv_cache_desc* desc, const void* k_cache, const void* v
 int pkv_decode_plan(const pkv_cache_desc* desc, int32_t batch, int32_t num_q_heads,
                     int32_t max_context_len, int32_t split_tokens, int32_t* n_split,
                     size_t* workspace_bytes) {
-  if (int rc = check_desc(desc)) return rc;
-  int group = 0;
-  if (int rc = check_heads(desc, num_q_heads, &group)) return rc;
-  if (batch < 0) return fail(PKV_ERR_INVALID, "batch %d < 0", batch);
-  if (max_context_len < 0) return fail(PKV_ERR_INVALID, "max_context_len %d < 0", max_context_len);
-  if (!n_split || !workspace_bytes) return fail(PKV_ERR_INVALID, "NULL output pointer");
-  Plan plan;
-  if (int rc = make_plan(desc, batch, num_q_heads, max_context_len, split_tokens, &plan))
-    return rc;
-  *n_split = plan.n_split;
-  *workspace_bytes = plan.n_split > 1 ? plan.ws_bytes : 0;
-  return ok();
+  return plan_impl(desc, batch, num_q_heads, max_context_len, split_tokens, nullptr, n_split,
+                   workspace_bytes);
+}
+
+int pkv_decode_plan_ex(const pkv_cache_desc* desc, int32_t batch, int32_t num_q_heads,
+                       int32_t max_context_len, int32_t split_tokens,
+                       const pkv_decode_opts* opts, int32_t* n_split, size_t* workspace_bytes) {
+  return plan_impl(desc, batch, num_q_heads, max_context_len, split_tokens, opts, n_split,
+                   workspace_bytes);
 }
 
 int pkv_paged_attn_decode(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache,
@@ -232,36 +376,21 @@ int pkv_paged_attn_decode(const pkv_cache_desc* desc, const void* k_cache, const
                           const int32_t* context_lens, int32_t max_context_len, float scale,
                           int32_t split_tokens, void* out, float* lse_out, void* workspace,
                           size_t workspace_bytes, void* stream) {
-  DecodeCommon dc;
-  if (int rc = check_decode(desc, k_cache, v_cache, q, batch, num_q_heads, block_table,
-                            block_table_stride, context_lens, max_context_len, scale,
-                            split_tokens, &dc))
-    return rc;
-  if (batch == 0) return ok();
-  if (!out) return fail(PKV_ERR_INVALID, "out is NULL");
-  pkv::DecodeArgs a = decode_args(desc, k_cache, v_cache, q, num_q_heads, block_table,
-                                  block_table_stride, context_lens, scale, dc.plan);
-  hipStream_t s = (hipStream_t)stream;
-  if (dc.plan.n_split == 1) {
-    a.direct = 1;
-    a.out = out;
-    a.lse_out = lse_out;
-    return hip_status(pkv::launch_decode(desc->dtype, desc->head_dim, dc.group, batch, a, s),
-                      "decode launch");
-  }
-  if (!workspace || workspace_bytes < dc.plan.ws_bytes)
-    return fail(PKV_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes,
-                dc.plan.ws_bytes);
-  if (!aligned16(workspace)) return fail(PKV_ERR_INVALID, "workspace must be 16-byte aligned");
-  a.direct = 0;
-  a.o_part = (float*)workspace;
-  a.lse_part = (float*)((char*)workspace + dc.plan.o_bytes);
-  if (int rc = hip_status(pkv::launch_decode(desc->dtype, desc->head_dim, dc.group, batch, a, s),
-                          "decode launch"))
-    return rc;
-  return hip_status(pkv::launch_merge(desc->dtype, desc->head_dim, a.o_part, a.lse_part,
-                                      batch * num_q_heads, dc.plan.n_split, out, lse_out, s),
-                    "merge launch");
+  return decode_impl(desc, k_cache, v_cache, q, batch, num_q_heads, block_table,
+                     block_table_stride, context_lens, max_context_len, scale, split_tokens,
+                     nullptr, out, lse_out, workspace, workspace_bytes, stream);
+}
+
+int pkv_paged_attn_decode_ex(const pkv_cache_desc* desc, const void* k_cache,
+                             const void* v_cache, const void* q, int32_t batch,
+                             int32_t num_q_heads, const int32_t* block_table,
+                             int32_t block_table_stride, const int32_t* context_lens,
+                             int32_t max_context_len, float scale, int32_t split_tokens,
+                             const pkv_decode_opts* opts, void* out, float* lse_out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(desc, k_cache, v_cache, q, batch, num_q_heads, block_table,
+                     block_table_stride, context_lens, max_context_len, scale, split_tokens,
+                     opts, out, lse_out, workspace, workspace_bytes, stream);
 }
 
 int pkv_paged_attn_decode_partials(const pkv_cache_desc* desc, const void* k_cache,
@@ -270,24 +399,44 @@ int pkv_paged_attn_decode_partials(const pkv_cache_desc* desc, const void* k_cac
                                    int32_t block_table_stride, const int32_t* context_lens,
                                    int32_t max_context_len, float scale, int32_t split_tokens,
                                    void* workspace, size_t workspace_bytes, void* stream) {
-  DecodeCommon dc;
-  if (int rc = check_decode(desc, k_cache, v_cache, q, batch, num_q_heads, block_table,
-                            block_table_stride, context_lens, max_context_len, scale,
-                            split_tokens, &dc))
-    return rc;
-  if (batch == 0) return ok();
-  if (!workspace || workspace_bytes < dc.plan.ws_bytes)
-    return fail(PKV_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes,
-                dc.plan.ws_bytes);
-  if (!aligned16(workspace)) return fail(PKV_ERR_INVALID, "workspace must be 16-byte aligned");
-  pkv::DecodeArgs a = decode_args(desc, k_cache, v_cache, q, num_q_heads, block_table,
-                                  block_table_stride, context_lens, scale, dc.plan);
-  a.direct = 0;
-  a.o_part = (float*)workspace;
-  a.lse_part = (float*)((char*)workspace + dc.plan.o_bytes);
-  return hip_status(pkv::launch_decode(desc->dtype, desc->head_dim, dc.group, batch, a,
-                                       (hipStream_t)stream),
-                    "decode launch");
+  return partials_impl(desc, k_cache, v_cache, q, batch, num_q_heads, block_table,
+                       block_table_stride, context_lens, max_context_len, scale, split_tokens,
+                       nullptr, workspace, workspace_bytes, stream);
+}
+
+int pkv_paged_attn_decode_partials_ex(const pkv_cache_desc* desc, const void* k_cache,
+                                      const void* v_cache, const void* q, int32_t batch,
+                                      int32_t num_q_heads, const int32_t* block_table,
+                                      int32_t block_table_stride, const int32_t* context_lens,
+                                      int32_t max_context_len, float scale,
+                                      int32_t split_tokens, const pkv_decode_opts* opts,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  return partials_impl(desc, k_cache, v_cache, q, batch, num_q_heads, block_table,
+                       block_table_stride, context_lens, max_context_len, scale, split_tokens,
+                       opts, workspace, workspace_bytes, stream);
+}
+
+int pkv_kv_append_quant(const pkv_cache_desc* desc, void* k_cache, void* v_cache,
+                        const void* k_new, const void* v_new, int32_t src_dtype, float k_scale,
+                        float v_scale, const int32_t* slot_mapping, int32_t n_tokens,
+                        void* stream) {
+  if (int rc = check_desc(desc)) return rc;
+  if (!is_fp8(desc->dtype))
+    return fail(PKV_ERR_INVALID, "kv_append_quant writes fp8 caches (dtype %d)", desc->dtype);
+  if (int rc = check_value_dtype(src_dtype, "source")) return rc;
+  if (!finite_positive(k_scale) || !finite_positive(v_scale))
+    return fail(PKV_ERR_INVALID, "k_scale and v_scale must be finite and > 0");
+  if (n_tokens < 0) return fail(PKV_ERR_INVALID, "n_tokens %d < 0", n_tokens);
+  if (n_tokens == 0) return ok();
+  if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping)
+    return fail(PKV_ERR_INVALID, "NULL pointer");
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
+    return fail(PKV_ERR_INVALID, "cache and new-token buffers must be 16-byte aligned");
+  return hip_status(pkv::launch_kv_append_quant(desc->dtype, src_dtype, desc->head_dim,
+                                                desc->num_kv_heads, desc->num_pages, k_cache,
+                                                v_cache, k_new, v_new, k_scale, v_scale,
+                                                slot_mapping, n_tokens, (hipStream_t)stream),
+                    "kv_append_quant launch");
 }
 
 int pkv_merge_states(const float* o_parts, const float* lse_parts, int32_t rows,
@@ -296,7 +445,7 @@ int pkv_merge_states(const float* o_parts, const float* lse_parts, int32_t rows,
   if (rows < 0) return fail(PKV_ERR_INVALID, "rows %d < 0", rows);
   if (n_parts <= 0) return fail(PKV_ERR_INVALID, "n_parts %d <= 0", n_parts);
   if (head_dim <= 0) return fail(PKV_ERR_INVALID, "head_dim %d <= 0", head_dim);
-  if (int rc = check_dtype(out_dtype)) return rc;
+  if (int rc = check_value_dtype(out_dtype, "out")) return rc;
   if (head_dim != 64 && head_dim != 128)
     return fail(PKV_ERR_UNSUPPORTED, "head_dim %d: only 64 and 128 are built", head_dim);
   if (rows == 0) return ok();
@@ -317,7 +466,7 @@ int pkv_paged_attn_prefill_chunk(const pkv_cache_desc* desc, const void* k_cache
   if (int rc = check_desc(desc)) return rc;
   int group = 0;
   if (int rc = check_heads(desc, num_q_heads, &group)) return rc;
-  if (desc->dtype == PKV_F32)
+  if (desc->dtype != PKV_F16 && desc->dtype != PKV_BF16)
     return fail(PKV_ERR_UNSUPPORTED, "prefill runs on the matrix cores: f16 or bf16 only");
   if (desc->head_dim != 128)
     return fail(PKV_ERR_UNSUPPORTED, "prefill is built for head_dim 128 (got %d)",

@@ -23,7 +23,10 @@ struct DecodeArgs {
   int32_t num_q_heads;
   int32_t pages_per_split;
   int32_t n_split;
-  float scale_log2;             // scale * log2(e)
+  float scale_log2;             // scale * log2(e) (times k_scale for fp8 caches)
+  float v_scale;                // multiplies the output (fp8 caches; 1 otherwise)
+  int32_t window;               // > 0: keys t >= L - window and t < sink only
+  int32_t sink;
   int32_t direct;               // 1: final output to out/lse_out; 0: partials
   void* out;                    // [B][H_q][D] (direct)
   float* lse_out;               // [B][H_q] or null (direct)
@@ -60,8 +63,17 @@ hipError_t launch_gather(int dtype, int head_dim, int num_kv_heads, int64_t num_
                          const void* k_cache, const void* v_cache, const int32_t* table_row,
                          int32_t len, void* k_out, void* v_out, hipStream_t stream);
 
-hipError_t launch_decode(int dtype, int head_dim, int group, int batch, const DecodeArgs& a,
-                         hipStream_t stream);
+// kv_dtype: element type of the pools; q_dtype: of q and out (equal unless
+// the pools are fp8).
+hipError_t launch_decode(int kv_dtype, int q_dtype, int head_dim, int group, int batch,
+                         const DecodeArgs& a, hipStream_t stream);
+
+// fp8 quantizing append from src_dtype (f32, f16, bf16) new tokens.
+hipError_t launch_kv_append_quant(int fp8_dtype, int src_dtype, int head_dim, int num_kv_heads,
+                                  int64_t num_pages, void* k_cache, void* v_cache,
+                                  const void* k_new, const void* v_new, float k_scale,
+                                  float v_scale, const int32_t* slots, int32_t n_tokens,
+                                  hipStream_t stream);
 
 hipError_t launch_merge(int out_dtype, int head_dim, const float* o_parts,
                         const float* lse_parts, int32_t rows, int32_t n_parts, void* out,

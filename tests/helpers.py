@@ -51,7 +51,7 @@ def assert_lse_close(got, ref, dtype: str, what: str = ""):
 def bits(t: torch.Tensor) -> torch.Tensor:
     """Integer view of a tensor's bytes, for bit-exact comparisons."""
     t = t.detach().contiguous().cpu()
-    return t.view(torch.int32) if t.element_size() == 4 else t.view(torch.int16)
+    return t.view({4: torch.int32, 2: torch.int16, 1: torch.uint8}[t.element_size()])
 
 
 def to_dev(w, dev):

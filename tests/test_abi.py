@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol(L):
     assert len(names) >= 10
     for n in names:
         assert hasattr(L, n), n
-    assert L.pkv_version() == 1
+    assert L.pkv_version() == 2
 
 
 def err(L):
@@ -148,3 +148,64 @@ def test_prefill_args(L):
     assert _prefill(L, desc(), q=None) == -1
     assert _prefill(L, desc(), total=-1) == -1
     assert _prefill(L, desc(), batch=0) == 0
+
+
+def _opts(q_dtype=2, k_scale=1.0, v_scale=1.0, window=0, sink=0):
+    return binding.DecodeOpts(q_dtype, k_scale, v_scale, window, sink)
+
+
+def _decode_ex(L, d, opts, *, batch=2, hq=4, stride=8, max_len=100, split=0):
+    return L.pkv_paged_attn_decode_ex(C.byref(d), FAKE, FAKE, FAKE, batch, hq, FAKE, stride,
+                                      FAKE, max_len, 0.125, split,
+                                      None if opts is None else C.byref(opts), FAKE, None,
+                                      None, 0, None)
+
+
+def test_decode_ex_options(L):
+    f8 = desc(dtype=3)
+    assert _decode(L, f8) == -1 and "q_dtype" in err(L)       # fp8 needs options
+    assert _decode_ex(L, f8, _opts(q_dtype=0)) == -2          # f32 queries over fp8
+    assert _decode_ex(L, f8, _opts(q_dtype=3)) == -2
+    assert _decode_ex(L, desc(dtype=3, d=64), _opts(q_dtype=1)) == -2   # fp8 needs D 128
+    assert _decode_ex(L, f8, _opts(q_dtype=1, k_scale=0.0)) == -1
+    assert _decode_ex(L, f8, _opts(q_dtype=1, v_scale=float("inf"))) == -1
+    assert _decode_ex(L, f8, _opts(q_dtype=1, window=-1)) == -1
+    assert _decode_ex(L, f8, _opts(q_dtype=2), batch=0) == 0
+    bf = desc(dtype=2)
+    assert _decode_ex(L, bf, _opts(q_dtype=1)) == -1           # q type must match
+    assert _decode_ex(L, bf, _opts(k_scale=2.0)) == -1         # scales are fp8-only
+    assert _decode_ex(L, bf, None, batch=0) == 0
+    assert _decode_ex(L, bf, _opts(window=4, sink=2), batch=0) == 0
+
+
+def test_plan_ex_counts_window_pages_only(L):
+    d = desc(hkv=2)
+    n, ws = C.c_int32(), C.c_size_t()
+    assert L.pkv_decode_plan_ex(C.byref(d), 8, 16, 131072, 0, None, C.byref(n), C.byref(ws)) == 0
+    assert n.value == 32
+    o = _opts(q_dtype=2, window=4096, sink=128)
+    assert L.pkv_decode_plan_ex(C.byref(d), 8, 16, 131072, 0, C.byref(o), C.byref(n),
+                                C.byref(ws)) == 0
+    # (128/16 + 4096/16 + 1) pages = 265 pages -> at most 17 splits of >= 16 pages
+    assert 1 <= n.value <= 17
+    o = _opts(q_dtype=2, window=4096, sink=128)
+    assert L.pkv_decode_plan_ex(C.byref(d), 8, 16, 131072, 1024, C.byref(o), C.byref(n),
+                                C.byref(ws)) == 0
+    assert n.value == (265 * 16 + 1023) // 1024
+
+
+def test_kv_append_quant_args(L):
+    f8 = desc(dtype=4)
+    q = L.pkv_kv_append_quant
+    assert q(C.byref(desc(dtype=2)), FAKE, FAKE, FAKE, FAKE, 2, 1.0, 1.0, FAKE, 4, None) == -1
+    assert q(C.byref(f8), FAKE, FAKE, FAKE, FAKE, 3, 1.0, 1.0, FAKE, 4, None) == -2
+    assert q(C.byref(f8), FAKE, FAKE, FAKE, FAKE, 9, 1.0, 1.0, FAKE, 4, None) == -1
+    assert q(C.byref(f8), FAKE, FAKE, FAKE, FAKE, 2, 0.0, 1.0, FAKE, 4, None) == -1
+    assert q(C.byref(f8), FAKE, FAKE, FAKE, FAKE, 2, 1.0, float("nan"), FAKE, 4, None) == -1
+    assert q(C.byref(f8), FAKE, FAKE, FAKE, FAKE, 2, 1.0, 1.0, FAKE, -1, None) == -1
+    assert q(C.byref(f8), FAKE, FAKE, FAKE, FAKE, 2, 1.0, 1.0, FAKE, 0, None) == 0
+
+
+def test_fp8_elsewhere_rejected(L):
+    assert _prefill(L, desc(dtype=3)) == -2
+    assert L.pkv_merge_states(FAKE, FAKE, 4, 2, 128, 3, FAKE, None, None) == -2
