@@ -294,6 +294,34 @@ int pkv_paged_attn_prefill_chunk(const pkv_cache_desc* desc, const void* k_cache
                                  void* stream);
 
 /*
+ * paged_attn_mixed -- one call for a ragged batch that mixes decode rows and
+ * prefill chunks, the batch a chunked-prefill scheduler forms under a token
+ * budget (page 1, section 4.1: chunked prefill with a bound on the batched
+ * tokens; page 2, section 4.2: continuous batching puts new requests next to
+ * running ones).  It computes exactly what paged_attn_prefill_chunk computes
+ * for the whole batch (row i of sequence b at position kv_lens[b] - C_b + i,
+ * bottom-right causal), with the batch laid out decode-first: sequences
+ * 0 .. num_decode-1 have one query row each, rows 0 .. num_decode-1
+ * (q_indptr[b] = b for b <= num_decode, a precondition on device data), and
+ * the remaining sequences carry chunks.  The decode rows go through the
+ * split-KV decode kernel (workspace and merge as in paged_attn_decode, with
+ * batch = num_decode and max_context_len = max_kv_len), the chunks through
+ * the MFMA prefill kernel; both on `stream`, in that order.
+ *   num_decode : 0 <= num_decode <= batch and <= total_q_rows.
+ *   max_q_len  : host bound >= C_b of every chunk sequence (>= 1 if any).
+ *   workspace  : >= the workspace_bytes of pkv_decode_plan(desc, num_decode,
+ *                num_q_heads, max_kv_len, split_tokens); may be NULL when 0.
+ * Other arguments as for paged_attn_prefill_chunk (f16 or bf16, head_dim 128).
+ */
+int pkv_paged_attn_mixed(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache,
+                         const void* q, const int32_t* q_indptr, int32_t batch,
+                         int32_t num_decode, int32_t num_q_heads, int32_t total_q_rows,
+                         int32_t max_q_len, const int32_t* block_table,
+                         int32_t block_table_stride, const int32_t* kv_lens, int32_t max_kv_len,
+                         float scale, int32_t split_tokens, void* out, float* lse_out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * validate_tables -- host-side check of host copies of the tables (no HIP
  * call): every entry a sequence uses (the first ceil(lens[b]/P) of its row)
  * is in [0, num_pages); 0 <= lens[b] <= stride * P; every slot is < 0 or in

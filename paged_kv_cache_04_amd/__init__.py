@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     merge_states,
     paged_attn_decode,
     paged_attn_decode_partials,
+    paged_attn_mixed,
     paged_attn_prefill_chunk,
     validate_tables,
 )

@@ -76,11 +76,14 @@ def lib():
         L.pkv_paged_attn_decode_partials_ex.argtypes = [dp, vp, vp, vp, i32, i32, vp, i32, vp,
                                                         i32, f32, i32, op, vp, sz, vp]
         L.pkv_kv_append_quant.argtypes = [dp, vp, vp, vp, vp, i32, f32, f32, vp, i32, vp]
+        L.pkv_paged_attn_mixed.argtypes = [dp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32,
+                                           vp, i32, f32, i32, vp, vp, vp, sz, vp]
         for name in ("pkv_kv_append", "pkv_gather_kv", "pkv_decode_plan", "pkv_paged_attn_decode",
                      "pkv_paged_attn_decode_partials", "pkv_merge_states",
                      "pkv_paged_attn_prefill_chunk", "pkv_validate_tables",
                      "pkv_decode_plan_ex", "pkv_paged_attn_decode_ex",
-                     "pkv_paged_attn_decode_partials_ex", "pkv_kv_append_quant"):
+                     "pkv_paged_attn_decode_partials_ex", "pkv_kv_append_quant",
+                     "pkv_paged_attn_mixed"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -327,6 +330,39 @@ def paged_attn_prefill_chunk(q, k_cache, v_cache, q_indptr, block_table, kv_lens
         C.byref(desc), _p(k_cache), _p(v_cache), _p(q), _p(q_indptr), batch, hq,
         int(q.shape[0]), int(max_q_len), _p(block_table), int(block_table.shape[1]), _p(kv_lens),
         int(max_kv_len), float(scale), _p(out), _p(lse_out), _stream()))
+    return (out, lse_out) if return_lse else out
+
+
+def paged_attn_mixed(q, k_cache, v_cache, q_indptr, block_table, kv_lens, num_decode: int,
+                     max_q_len: int, max_kv_len: int, scale: float, split_tokens: int = 0,
+                     out=None, lse_out=None, workspace=None, return_lse: bool = False):
+    """pkv_paged_attn_mixed: a decode-first ragged batch (sequences
+    0 .. num_decode-1 one row each, then prefill chunks), q packed
+    [sum C][H_q][D]."""
+    desc = _check_pools(k_cache, v_cache)
+    _dev(q, "q", k_cache.dtype)
+    _dev(q_indptr, "q_indptr", torch.int32)
+    _dev(block_table, "block_table", torch.int32)
+    _dev(kv_lens, "kv_lens", torch.int32)
+    if q.dim() != 3 or q.shape[2] != desc.head_dim:
+        raise ValueError("q must be [sum C][H_q][D]")
+    batch = int(q_indptr.shape[0]) - 1
+    hq = int(q.shape[1])
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse_out is None:
+        lse_out = torch.empty((q.shape[0], hq), dtype=torch.float32, device=q.device)
+    ws_bytes = 0
+    if num_decode > 0:
+        _, ws_bytes = decode_plan(desc, num_decode, hq, max_kv_len, split_tokens)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pkv_paged_attn_mixed(
+        C.byref(desc), _p(k_cache), _p(v_cache), _p(q), _p(q_indptr), batch, int(num_decode), hq,
+        int(q.shape[0]), int(max_q_len), _p(block_table), int(block_table.shape[1]), _p(kv_lens),
+        int(max_kv_len), float(scale), int(split_tokens), _p(out), _p(lse_out), _p(workspace),
+        ws_len, _stream()))
     return (out, lse_out) if return_lse else out
 
 

@@ -49,6 +49,8 @@ struct PrefillArgs {
   int32_t max_q_len;
   int64_t total_q;              // rows of q / out
   int32_t m_tiles;              // query-row tiles per (b, kv head)
+  int32_t xcd_split;            // 1: tile ranges spread over the 8 XCDs (see prefill.hip)
+  int32_t m_tiles_x;            // ceil(m_tiles / 8): tiles per XCD and (b, kv head)
   float scale_log2;
   void* out;
   float* lse_out;

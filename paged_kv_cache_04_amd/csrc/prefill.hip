@@ -142,9 +142,24 @@ __global__ __launch_bounds__(NWP * 64, 2) void prefill_kernel(PrefillArgs a) {
   const int half = lane >> 5;     // which 32-lane half
   const int n = lane & 31;        // this lane's query row within the wave
 
+  // Workgroups are handed to the 8 XCDs round-robin (workgroup i to XCD
+  // i % 8), and each XCD has its own L2.  Default order: (b, kv head) fastest,
+  // so when there are at least 8 such pairs each XCD keeps whole pairs and all
+  // their query tiles share the K/V stream in its L2.  With xcd_split, XCD x
+  // takes the x-th eighth of the query tiles of every pair instead: every XCD
+  // gets the same share of long and short sequences, and the tiles of one
+  // pair on one XCD still read the same keys together.
   const int nbg = a.batch * a.num_kv_heads;
-  const int bg = blockIdx.x % nbg;
-  const int mt = blockIdx.x / nbg;
+  int bg, mt;
+  if (a.xcd_split) {
+    const int x = blockIdx.x % 8, j = blockIdx.x / 8;
+    bg = j % nbg;
+    mt = x * a.m_tiles_x + j / nbg;
+    if (mt >= a.m_tiles) return;     // padding of the last XCD's range
+  } else {
+    bg = blockIdx.x % nbg;
+    mt = blockIdx.x / nbg;
+  }
   const int b = bg / a.num_kv_heads;
   const int g = bg % a.num_kv_heads;
 
@@ -430,7 +445,8 @@ __global__ __launch_bounds__(NWP * 64, 2) void prefill_kernel(PrefillArgs a) {
 
 template <typename TT>
 hipError_t launch_t(int group, const PrefillArgs& a, hipStream_t stream) {
-  const int64_t blocks = (int64_t)a.batch * a.num_kv_heads * a.m_tiles;
+  const int64_t blocks = (int64_t)a.batch * a.num_kv_heads *
+                         (a.xcd_split ? 8 * (int64_t)a.m_tiles_x : (int64_t)a.m_tiles);
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)blocks), block(NWP * 64);
   switch (group) {

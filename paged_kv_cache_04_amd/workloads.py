@@ -65,6 +65,12 @@ CONFIGS: Dict[str, dict] = {
                    prefix=2048, suffix_range=(32, 512), append=False),
     "prefill": dict(kind="prefill", seed=5, batch=4, hq=32, hkv=8, d=128, dtype="bf16",
                     hist=32768, chunk=512),
+    # a chunked-prefill batch under page 1's token budget (section 4.1: at most
+    # 8192 batched tokens, up to 8 sequences at 128K): 6 sequences decoding one
+    # token each at contexts 8K..128K, then 2 prompts each contributing a
+    # 4093-row chunk (one at the start of its prompt, one after 64K tokens)
+    "mixed": dict(kind="mixed", seed=7, hq=16, hkv=2, d=128, dtype="f16", n_decode=6,
+                  decode_range=(8192, 131071), chunk_hist=[0, 65536], chunk=[4093, 4093]),
     # the 128K decode with an fp8 (e4m3) cache: page 1, section 4.1 recommends
     # that cache type for this deployment; f16 queries and outputs
     "llama70b_128k_fp8": dict(kind="decode", seed=6, batch=8, hq=16, hkv=2, d=128,
@@ -76,7 +82,7 @@ CONFIGS: Dict[str, dict] = {
 @dataclasses.dataclass
 class Workload:
     name: str
-    kind: str                      # "decode" or "prefill"
+    kind: str                      # "decode", "prefill" or "mixed" (decode-first ragged batch)
     dtype: str                     # "f32" | "f16" | "bf16": queries, outputs, new tokens
     num_pages: int
     page_size: int
@@ -304,6 +310,22 @@ def make_prefill(name: str, *, seed: int, batch: int, hq: int, hkv: int, d: int,
                               chunk_lens=list(chunk), seed=seed))
 
 
+def make_mixed(name: str, *, seed: int, hq: int, hkv: int, d: int, dtype: str,
+               decode_hist: List[int], chunk_hist: List[int], chunk: List[int],
+               pool_slack: float = 0.0, gen: Optional[torch.Generator] = None) -> Workload:
+    """A decode-first ragged batch: len(decode_hist) sequences with one new
+    token each (a chunk of one row), then the prompt chunks.  Same layout as a
+    prefill workload (every new row's K/V handed over for the append); meta
+    carries num_decode."""
+    w = make_prefill(name, seed=seed, batch=len(decode_hist) + len(chunk), hq=hq, hkv=hkv, d=d,
+                     dtype=dtype, hist=list(decode_hist) + list(chunk_hist),
+                     chunk=[1] * len(decode_hist) + list(chunk), pool_slack=pool_slack,
+                     gen=gen)
+    w.kind = "mixed"
+    w.meta["num_decode"] = len(decode_hist)
+    return w
+
+
 def make(name: str, seed: Optional[int] = None) -> Workload:
     """Build one of the named workloads with its fixed seed (or ``seed``)."""
     cfg = dict(CONFIGS[name])
@@ -311,6 +333,12 @@ def make(name: str, seed: Optional[int] = None) -> Workload:
     cfg.pop("seed", None)
     kind = cfg.pop("kind")
     gen = torch.Generator().manual_seed(seed)
+    if kind == "mixed":
+        lo, hi = cfg["decode_range"]
+        dec = torch.randint(lo, hi + 1, (cfg["n_decode"],), generator=gen).tolist()
+        return make_mixed(name, seed=seed, hq=cfg["hq"], hkv=cfg["hkv"], d=cfg["d"],
+                          dtype=cfg["dtype"], decode_hist=dec, chunk_hist=cfg["chunk_hist"],
+                          chunk=cfg["chunk"], gen=gen)
     if kind == "prefill":
         b = cfg["batch"]
         return make_prefill(name, seed=seed, batch=b, hq=cfg["hq"], hkv=cfg["hkv"],

@@ -209,3 +209,19 @@ def test_kv_append_quant_args(L):
 def test_fp8_elsewhere_rejected(L):
     assert _prefill(L, desc(dtype=3)) == -2
     assert L.pkv_merge_states(FAKE, FAKE, 4, 2, 128, 3, FAKE, None, None) == -2
+
+
+def _mixed(L, d, *, batch=4, nd=2, total=10, max_q=8, stride=8, max_kv=100):
+    return L.pkv_paged_attn_mixed(C.byref(d), FAKE, FAKE, FAKE, FAKE, batch, nd, 4, total, max_q,
+                                  FAKE, stride, FAKE, max_kv, 0.125, 0, FAKE, None, None, 0,
+                                  None)
+
+
+def test_mixed_args(L):
+    d = desc()
+    assert _mixed(L, d, nd=-1) == -1
+    assert _mixed(L, d, nd=5) == -1                       # more decode rows than sequences
+    assert _mixed(L, d, nd=3, total=2) == -1              # more decode rows than q rows
+    assert _mixed(L, d, nd=1, max_q=0) == -1              # chunks need max_q_len >= 1
+    assert _mixed(L, desc(dtype=0)) == -2                 # the chunk path is MFMA: f16/bf16
+    assert _mixed(L, d, batch=0, nd=0) == 0

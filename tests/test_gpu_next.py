@@ -221,3 +221,75 @@ def test_window_128k_sampled_rows():
     idx = torch.tensor(rows, device=DEV)
     assert_close(out.reshape(-1, w.head_dim)[idx], ref, w.dtype, "window 128K")
     assert_lse_close(lse.reshape(-1)[idx], ref_lse, w.dtype, "window 128K")
+
+
+# ------------------------------------------------------------ ragged mixed batch
+
+def mixed_run(w, d, split_tokens=0):
+    pkv.kv_append(d["k_cache"], d["v_cache"], d["k_new"], d["v_new"], d["slots"])
+    chunk = w.meta["chunk_lens"]
+    nd = w.meta["num_decode"]
+    max_q = max(chunk[nd:]) if len(chunk) > nd else 0
+    out, lse = pkv.paged_attn_mixed(d["q"], d["k_cache"], d["v_cache"], d["q_indptr"],
+                                    d["block_table"], d["context_lens"], nd, max_q,
+                                    w.max_context_len, w.scale, split_tokens=split_tokens,
+                                    return_lse=True)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def oracle_mixed(w, rows=None):
+    pkvref.kv_append(w.dtype, w.k_cache, w.v_cache, w.k_new, w.v_new, w.slots)
+    return pkvref.prefill(w.dtype, w.k_cache, w.v_cache, w.q, w.q_indptr, w.block_table,
+                          w.context_lens, w.scale, rows=rows, n_threads=host_threads())
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (8, 2), (16, 2)])
+@pytest.mark.parametrize("split", [0, 64])
+def test_mixed_batch_all_rows(dtype, hq, hkv, split):
+    """Decode rows (contexts from 1 key to several pages) before ragged
+    chunks; every output row and log-sum-exp against the oracle."""
+    w = W.make_mixed("mx", seed=hq + 3 * hkv, hq=hq, hkv=hkv, d=128, dtype=dtype,
+                     decode_hist=[0, 15, 16, 300, 1000], chunk_hist=[0, 37, 500],
+                     chunk=[7, 129, 64], pool_slack=0.2)
+    d = to_dev(w, DEV)
+    out, lse = mixed_run(w, d, split)
+    ref, ref_lse = oracle_mixed(w)
+    assert_close(out.reshape(ref.shape), ref, dtype, f"mixed {dtype} G{hq // hkv}")
+    assert_lse_close(lse.reshape(-1), ref_lse, dtype, f"mixed {dtype} G{hq // hkv}")
+
+
+@pytest.mark.parametrize("layout", ["decode only", "chunks only"])
+def test_mixed_batch_degenerate(layout):
+    if layout == "decode only":
+        dh, ch, c = [5, 100, 700], [], []
+    else:
+        dh, ch, c = [], [0, 90], [40, 3]
+    w = W.make_mixed("mxd", seed=9, hq=8, hkv=2, d=128, dtype="bf16", decode_hist=dh,
+                     chunk_hist=ch, chunk=c, pool_slack=0.2)
+    d = to_dev(w, DEV)
+    out, lse = mixed_run(w, d)
+    ref, ref_lse = oracle_mixed(w)
+    assert_close(out.reshape(ref.shape), ref, "bf16", layout)
+    assert_lse_close(lse.reshape(-1), ref_lse, "bf16", layout)
+
+
+def test_mixed_batch_full_size_sampled():
+    """The 8192-token batch: 6 decode rows at 8K..128K keys and two 4093-row
+    chunks (history 0 and 65536); every decode row and sampled chunk rows."""
+    w = W.make("mixed")
+    print("[mixed parity] 6 decode rows + 2 x 4093-row chunks", flush=True)
+    d = to_dev(w, DEV)
+    out, lse = mixed_run(w, d)
+    hq = w.num_q_heads
+    ind = w.q_indptr.tolist()
+    toks = list(range(6))
+    for b in (6, 7):
+        base = ind[b]
+        toks += [base + i for i in (0, 1, 15, 16, 17, 2047, 4091, 4092)]
+    rows = [t * hq + h for t in toks for h in (0, 5, 8, 15)]
+    ref, ref_lse = oracle_mixed(w, rows=rows)
+    idx = torch.tensor(rows, device=DEV)
+    assert_close(out.reshape(-1, w.head_dim)[idx], ref, w.dtype, "mixed full size")
+    assert_lse_close(lse.reshape(-1)[idx], ref_lse, w.dtype, "mixed full size")

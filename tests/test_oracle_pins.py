@@ -196,6 +196,31 @@ def test_dense_prefill_matches_sdpa(dtype):
     check_dense_prefill(dtype)
 
 
+def test_dense_mixed_batch_matches_sdpa():
+    """A decode-first ragged batch (one-row chunks, then longer chunks) is a
+    prefill batch: every row against dense SDPA with its bottom-right mask."""
+    w = W.make_mixed("m", seed=13, hq=4, hkv=2, d=16, dtype="f16", decode_hist=[0, 33, 16, 70],
+                     chunk_hist=[0, 19], chunk=[6, 17], pool_slack=0.2)
+    pkvref.kv_append("f16", w.k_cache, w.v_cache, w.k_new, w.v_new, w.slots)
+    out, lse = pkvref.prefill("f16", w.k_cache, w.v_cache, w.q, w.q_indptr, w.block_table,
+                              w.context_lens, w.scale)
+    G = w.num_q_heads // w.num_kv_heads
+    ind = w.q_indptr.tolist()
+    assert ind[:5] == [0, 1, 2, 3, 4] and w.meta["num_decode"] == 4
+    for b in range(w.batch):
+        kc, vc = W.contiguous_kv(w, b)
+        L, C = kc.shape[0], ind[b + 1] - ind[b]
+        kd = kc.double().permute(1, 0, 2).repeat_interleave(G, dim=0)
+        vd = vc.double().permute(1, 0, 2).repeat_interleave(G, dim=0)
+        qd = w.q[ind[b]:ind[b + 1]].double().permute(1, 0, 2)
+        mask = torch.zeros(C, L, dtype=torch.bool)
+        for i in range(C):
+            mask[i, : L - C + i + 1] = True
+        ref = _sdpa_rows(qd, kd, vd, w.scale, mask=mask).permute(1, 0, 2).reshape(C * w.num_q_heads, -1)
+        got = out[ind[b] * w.num_q_heads: ind[b + 1] * w.num_q_heads]
+        np.testing.assert_allclose(got, ref.numpy(), rtol=1e-10, atol=1e-11)
+
+
 # ----------------------------------------------------------------- brute force
 
 def _brute_decode_row(qv, ks, vs, scale):
