@@ -11,7 +11,15 @@ every input resident in HBM before the timed region.  `roofline` reports the
 partial-decode kernel: algorithmic KV bytes per launch over its mean launch
 time measured with HIP events on the stream it runs on.  `cpu_baseline` is
 the CPU oracle timed on this host's cores on a bounded sample of the same
-workload.  `--prefill` adds the chunked-prefill kernel's MFMA figure.
+workload.
+
+Extra objects (--extras, all by default) measure the other rows of the hot
+path on their own workloads, each with the roofline of its dominant kernel
+and a parity check of sampled rows against the oracle:
+  prefill_chunk  chunked prefill on the matrix cores (MFMA TFLOP/s)
+  fp8_decode     the 128K decode over fp8 (e4m3) pools (HBM GB/s)
+  window_decode  the 128K decode with a 4096-key window and a 128-key sink
+  mixed_batch    an 8192-token batch of decode rows and prefill chunks
 """
 from __future__ import annotations
 
@@ -41,6 +49,11 @@ WORKLOAD_TEXT = {
 }
 # Traffic factors measured for a plain copy kernel with the same counters
 # (FETCH_SIZE and WRITE_SIZE in KiB per dispatch versus known bytes).
+
+
+def progress(msg: str) -> None:
+    """One progress line on stderr (stdout carries only the JSON line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def host_cores() -> int:
@@ -73,8 +86,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="lower bound on the CPU oracle sample's wall time")
-    ap.add_argument("--prefill", action="store_true",
-                    help="also time the chunked-prefill kernel (batch 4, 32768 history + 512 chunk)")
+    ap.add_argument("--extras", default="prefill,fp8,window,mixed",
+                    help="comma-separated extra rows to measure: prefill, fp8, window, mixed "
+                         "('' or 'none' for none)")
+    ap.add_argument("--prefill", action="store_true", help="same as --extras prefill")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain copy of this many MiB first (counter calibration)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -111,6 +126,7 @@ def main():
         del src, dst
 
     t_gen = time.time()
+    progress(f"generating {args.config}")
     w = W.make(args.config)
     gen_s = time.time() - t_gen
     kc, vc = w.k_cache.to(dev), w.v_cache.to(dev)
@@ -145,6 +161,7 @@ def main():
             ev[1].record()
         call_merge()
 
+    progress(f"timing {args.steps} steps after {args.warmup} warm-up steps")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -164,7 +181,10 @@ def main():
     total_ms = t_begin.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
     kern_us = [e0.elapsed_time(e1) * 1e3 for e0, e1 in events]
-    kern_avg_us = float(np.mean(kern_us))
+    step_kern_us = float(np.mean(kern_us))
+    # the kernel's own duration: back-to-back launches between one event pair
+    # on its stream, so that the per-call event overhead does not count
+    kern_avg_us = _back_to_back_us(call_partials, args.steps)
 
     kv_bytes = A.decode_kv_bytes(w.context_lens.tolist(), w.num_kv_heads, w.head_dim, w.dtype)
     achieved = kv_bytes / (kern_avg_us * 1e-6) / 1e9
@@ -190,6 +210,7 @@ def main():
         got = out.float().cpu().double().numpy().reshape(w.batch * w.num_q_heads, w.head_dim)
         host_k, host_v = w.k_cache, w.v_cache
         cores = host_cores()
+        progress(f"CPU oracle baseline on {cores} threads")
         # CPU oracle on the same workload: one full step (append + decode of
         # every row), repeated until at least --cpu-seconds have passed.
         reps, t_cpu = 0, 0.0
@@ -235,15 +256,29 @@ def main():
                      "achieved": round(achieved, 1), "peak": A.HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / A.HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": kv_bytes,
-                     "kernel_avg_us": round(kern_avg_us, 2)},
+                     "kernel_avg_us": round(kern_avg_us, 2),
+                     "in_step_event_us": round(step_kern_us, 2)},
         "cpu_baseline": cpu,
         "parity": parity,
         "host_wall_s": round(wall, 4),
         "gen_s": round(gen_s, 1),
     }
 
-    if args.prefill:
-        line["prefill_chunk"] = bench_prefill(args, dev)
+    extras = [e for e in args.extras.split(",") if e and e != "none"]
+    if args.prefill and "prefill" not in extras:
+        extras.append("prefill")
+    sample = not args.no_cpu_baseline
+    if "window" in extras:
+        reuse = (w, (q, kc, vc, bt, cl)) if args.config == "llama70b_128k" else None
+        line["window_decode"] = bench_window(args, dev, sample, reuse)
+    del kc, vc, workspace
+    torch.cuda.empty_cache()
+    if "prefill" in extras:
+        line["prefill_chunk"] = bench_prefill(args, dev, sample)
+    if "fp8" in extras:
+        line["fp8_decode"] = bench_fp8(args, dev, sample)
+    if "mixed" in extras:
+        line["mixed_batch"] = bench_mixed(args, dev, sample)
 
     print(json.dumps(line), flush=True)
 
@@ -260,7 +295,68 @@ def _kernel_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def bench_prefill(args, dev):
+def _back_to_back_us(fn, n):
+    """Mean microseconds per call of n back-to-back calls of fn() bracketed by
+    one pair of HIP events on the current stream."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
+def _event_times(fn, n, warmup=3):
+    """Mean and median microseconds of fn() bracketed by HIP events on the
+    current stream (the stream the library enqueues on)."""
+    import numpy as np
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for e0, e1 in ev:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    us = [e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]
+    return float(np.mean(us)), float(np.median(us))
+
+
+def _parity(got, ref, dtype):
+    import numpy as np
+    err = np.abs(got - ref)
+    tol = 2e-2 + 1e-2 * np.abs(ref) if dtype != "f32" else 1e-5
+    return {"rows": int(ref.shape[0]), "max_abs_err": float(np.nanmax(err)),
+            "within_tolerance": bool(np.all(err <= tol))}
+
+
+def _hbm_roofline(kernel, nbytes, us):
+    from paged_kv_cache_04_amd import accounting as A
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "kernel": kernel, "achieved": round(gbps, 1),
+            "peak": A.HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / A.HBM_PEAK_GBPS, 4),
+            "algorithmic_bytes_per_launch": int(nbytes), "kernel_avg_us": round(us, 2)}
+
+
+def _mfma_roofline(kernel, flops, us, dtype):
+    from paged_kv_cache_04_amd import accounting as A
+    tf = flops / (us * 1e-6) / 1e12
+    peak = A.MFMA_PEAK_TFLOPS[dtype]
+    return {"bound": "mfma", "kernel": kernel, "achieved": round(tf, 1), "peak": peak,
+            "unit": "TFLOP/s", "frac": round(tf / peak, 4),
+            "algorithmic_flops_per_launch": int(flops), "kernel_avg_us": round(us, 2)}
+
+
+def bench_prefill(args, dev, sample):
+    progress("prefill_chunk")
     import numpy as np
     import torch
 
@@ -280,28 +376,199 @@ def bench_prefill(args, dev):
         pkv.paged_attn_prefill_chunk(q, kc, vc, qi, bt, kl, max(chunk), w.max_context_len,
                                      w.scale, out=out)
 
-    for _ in range(3):
-        run()
-    torch.cuda.synchronize()
-    ts = []
-    for _ in range(10):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        run()
-        e1.record()
-        torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1) * 1e3)
-    us = float(np.mean(ts))
+    us, us_med = _event_times(run, 10)
     flops = A.prefill_flops(w.context_lens.tolist(), chunk, w.num_q_heads, w.head_dim)
-    tf = flops / (us * 1e-6) / 1e12
-    return {"workload": "batch 4, 32768-token paged history + 512-row causal chunk, 32 q / 8 kv "
-                        "heads, head_dim 128, bf16",
-            "kernel_avg_us": round(us, 2), "query_tokens_per_s": round(sum(chunk) / (us * 1e-6), 1),
-            "roofline": {"bound": "mfma", "achieved": round(tf, 1),
-                         "peak": A.MFMA_PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
-                         "frac": round(tf / A.MFMA_PEAK_TFLOPS["bf16"], 4),
-                         "algorithmic_flops_per_launch": flops}}
+    res = {"workload": "batch 4, 32768-token paged history + 512-row causal chunk, 32 q / 8 kv "
+                       "heads, head_dim 128, bf16",
+           "kernel_avg_us": round(us, 2), "kernel_median_us": round(us_med, 2),
+           "query_tokens_per_s": round(sum(chunk) / (us * 1e-6), 1),
+           "roofline": _mfma_roofline("prefill_kernel", flops, us, "bf16")}
+    if sample:
+        from oracle import pkvref
+        hq = w.num_q_heads
+        toks = [int(w.q_indptr[b]) + i for b in range(w.batch) for i in (0, 255, 511)]
+        rows = [t * hq + h for t in toks for h in (0, 13, 31)]
+        pkvref.kv_append(w.dtype, w.k_cache, w.v_cache, w.k_new, w.v_new, w.slots)
+        ref, _ = pkvref.prefill(w.dtype, w.k_cache, w.v_cache, w.q, w.q_indptr, w.block_table,
+                                w.context_lens, w.scale, rows=rows, n_threads=host_cores())
+        got = out.float().cpu().double().numpy().reshape(-1, w.head_dim)[rows]
+        res["parity"] = _parity(got, ref, w.dtype)
+    return res
+
+
+def bench_fp8(args, dev, sample):
+    progress("fp8_decode")
+    import torch
+
+    import paged_kv_cache_04_amd as pkv
+    from paged_kv_cache_04_amd import workloads as W
+
+    w = W.make("llama70b_128k_fp8")
+    kc, vc = w.k_cache.to(dev), w.v_cache.to(dev)
+    q, bt, cl = w.q.to(dev), w.block_table.to(dev), w.context_lens.to(dev)
+    k_new, v_new, slots = w.k_new.to(dev), w.v_new.to(dev), w.slots.to(dev)
+    desc = pkv.cache_desc(kc)
+    opts = pkv.decode_opts(q.dtype, kc.dtype, w.k_scale, w.v_scale)
+    n_split, _ = pkv.decode_plan(desc, w.batch, w.num_q_heads, w.max_context_len, 0, opts)
+    _, total = pkv.binding.partials_bytes(w.batch, w.num_q_heads, n_split, w.head_dim)
+    ws = torch.empty(total, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    o_parts, l_parts, _ = pkv.paged_attn_decode_partials(
+        q, kc, vc, bt, cl, w.max_context_len, w.scale, workspace=ws, k_scale=w.k_scale,
+        v_scale=w.v_scale)
+    c_app = pkv.binding.prepare_kv_append_quant(kc, vc, k_new, v_new, slots, w.k_scale,
+                                                w.v_scale)
+    c_part = pkv.binding.prepare_decode_partials(q, kc, vc, bt, cl, w.max_context_len, w.scale,
+                                                 0, ws, w.k_scale, w.v_scale)
+    c_merge = pkv.binding.prepare_merge_states(o_parts, l_parts, out)
+
+    def step():
+        c_app()
+        c_part()
+        c_merge()
+
+    step_us, _ = _event_times(step, 30, warmup=10)
+    _, part_med = _event_times(c_part, 30)
+    part_us = _back_to_back_us(c_part, 30)
+    kv_bytes = sum(w.context_lens.tolist()) * 2 * w.num_kv_heads * w.head_dim * 1
+    res = {"workload": "Llama-3-70B per-GPU share at 128K over fp8 (OCP e4m3) pools with fp32 "
+                       "scales: batch 8, 16 q / 2 kv heads, head_dim 128, f16 queries, page 16, "
+                       "131072 keys per sequence (131071 stored + 1 quantized on append)",
+           "tokens_per_s": round(w.batch / (step_us * 1e-6), 1), "ms_per_step": round(
+               step_us / 1e3, 5), "n_split": n_split, "kernel_median_us": round(part_med, 2),
+           "roofline": _hbm_roofline("decode_kernel<f16 q, fp8 e4m3 cache> (split-KV partials)",
+                                     kv_bytes, part_us)}
+    if sample:
+        from oracle import pkvref
+        kq = torch.from_numpy(pkvref.quant_fp8(w.kv_dtype, w.dtype, w.k_new, w.k_scale))
+        vq = torch.from_numpy(pkvref.quant_fp8(w.kv_dtype, w.dtype, w.v_new, w.v_scale))
+        pkvref.kv_append(w.kv_dtype, w.k_cache, w.v_cache, kq.view(W.DTYPES[w.kv_dtype]),
+                         vq.view(W.DTYPES[w.kv_dtype]), w.slots)
+        rows = [b * w.num_q_heads + h for b in range(w.batch) for h in (0, 9)]
+        ref, _ = pkvref.decode_ex(w.dtype, w.kv_dtype, w.k_cache, w.v_cache, w.q, w.block_table,
+                                  w.context_lens, w.scale, k_scale=w.k_scale,
+                                  v_scale=w.v_scale, rows=rows, n_threads=host_cores())
+        got = out.float().cpu().double().numpy().reshape(-1, w.head_dim)[rows]
+        res["parity"] = _parity(got, ref, w.dtype)
+    return res
+
+
+def bench_window(args, dev, sample, reuse=None):
+    progress("window_decode")
+    import torch
+
+    import paged_kv_cache_04_amd as pkv
+    from paged_kv_cache_04_amd import workloads as W
+
+    window, sink = 4096, 128
+    if reuse is not None:      # the main 128K workload, its append already applied
+        w, (q, kc, vc, bt, cl) = reuse
+    else:
+        w = W.make("llama70b_128k")
+        kc, vc = w.k_cache.to(dev), w.v_cache.to(dev)
+        q, bt, cl = w.q.to(dev), w.block_table.to(dev), w.context_lens.to(dev)
+        pkv.kv_append(kc, vc, w.k_new.to(dev), w.v_new.to(dev), w.slots.to(dev))
+        if sample:
+            from oracle import pkvref
+            pkvref.kv_append(w.dtype, w.k_cache, w.v_cache, w.k_new, w.v_new, w.slots)
+    desc = pkv.cache_desc(kc)
+    opts = pkv.decode_opts(q.dtype, kc.dtype, window=window, sink=sink)
+    n_split, _ = pkv.decode_plan(desc, w.batch, w.num_q_heads, w.max_context_len, 0, opts)
+    _, total = pkv.binding.partials_bytes(w.batch, w.num_q_heads, n_split, w.head_dim)
+    ws = torch.empty(total, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    o_parts, l_parts, _ = pkv.paged_attn_decode_partials(
+        q, kc, vc, bt, cl, w.max_context_len, w.scale, workspace=ws, window=window, sink=sink)
+    c_part = pkv.binding.prepare_decode_partials(q, kc, vc, bt, cl, w.max_context_len, w.scale,
+                                                 0, ws, window=window, sink=sink)
+    c_merge = pkv.binding.prepare_merge_states(o_parts, l_parts, out)
+
+    def step():
+        c_part()
+        c_merge()
+
+    step_us, _ = _event_times(step, 30, warmup=10)
+    _, part_med = _event_times(c_part, 30)
+    part_us = _back_to_back_us(c_part, 30)
+    es = 4 if w.dtype == "f32" else 2
+    vis = [min(L, window) + min(sink, max(0, L - window)) for L in w.context_lens.tolist()]
+    kv_bytes = sum(vis) * 2 * w.num_kv_heads * w.head_dim * es
+    res = {"workload": "the 128K decode workload with a sliding window: each query sees its "
+                       "4096 most recent keys and the first 128 (page 4, section 2.3's local "
+                       "window + global tokens); pages wholly outside are not read",
+           "tokens_per_s": round(w.batch / (step_us * 1e-6), 1),
+           "ms_per_step": round(step_us / 1e3, 5), "n_split": n_split,
+           "kernel_median_us": round(part_med, 2),
+           "roofline": _hbm_roofline("decode_kernel (windowed split-KV partials)", kv_bytes,
+                                     part_us)}
+    if sample:
+        from oracle import pkvref
+        rows = [b * w.num_q_heads + h for b in range(w.batch) for h in (0, 15)]
+        ref, _ = pkvref.decode_ex(w.dtype, w.dtype, w.k_cache, w.v_cache, w.q, w.block_table,
+                                  w.context_lens, w.scale, window=window, sink=sink, rows=rows,
+                                  n_threads=host_cores())
+        got = out.float().cpu().double().numpy().reshape(-1, w.head_dim)[rows]
+        res["parity"] = _parity(got, ref, w.dtype)
+    return res
+
+
+def bench_mixed(args, dev, sample):
+    progress("mixed_batch")
+    import torch
+
+    import paged_kv_cache_04_amd as pkv
+    from paged_kv_cache_04_amd import accounting as A
+    from paged_kv_cache_04_amd import workloads as W
+
+    w = W.make("mixed")
+    kc, vc = w.k_cache.to(dev), w.v_cache.to(dev)
+    q, bt, kl, qi = w.q.to(dev), w.block_table.to(dev), w.context_lens.to(dev), w.q_indptr.to(dev)
+    pkv.kv_append(kc, vc, w.k_new.to(dev), w.v_new.to(dev), w.slots.to(dev))
+    nd = w.meta["num_decode"]
+    chunk = w.meta["chunk_lens"]
+    max_q = max(chunk[nd:])
+    _, ws_bytes = pkv.decode_plan(pkv.cache_desc(kc), nd, w.num_q_heads, w.max_context_len)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+
+    def run():
+        pkv.paged_attn_mixed(q, kc, vc, qi, bt, kl, nd, max_q, w.max_context_len, w.scale,
+                             out=out, workspace=ws)
+
+    us, us_med = _event_times(run, 10)
+    # the chunk part alone (the MFMA kernel) and the decode part alone
+    qi_c, bt_c, kl_c = qi[nd:].contiguous(), bt[nd:].contiguous(), kl[nd:].contiguous()
+    pf_us, _ = _event_times(lambda: pkv.paged_attn_prefill_chunk(
+        q, kc, vc, qi_c, bt_c, kl_c, max_q, w.max_context_len, w.scale, out=out), 10)
+    dec_us, _ = _event_times(lambda: pkv.paged_attn_decode(
+        q[:nd], kc, vc, bt[:nd].contiguous(), kl[:nd].contiguous(), w.max_context_len, w.scale,
+        out=out[:nd], workspace=ws), 10)
+    lens = w.context_lens.tolist()
+    flops = A.prefill_flops(lens[nd:], chunk[nd:], w.num_q_heads, w.head_dim)
+    dec_bytes = A.decode_kv_bytes(lens[:nd], w.num_kv_heads, w.head_dim, w.dtype)
+    res = {"workload": "one chunked-prefill batch under page 1's 8192-token budget: 6 sequences "
+                       "decoding at 8K..128K keys + two 4093-row prompt chunks (history 0 and "
+                       "65536), 16 q / 2 kv heads, head_dim 128, f16, decode rows first",
+           "query_tokens": int(sum(chunk)), "call_avg_us": round(us, 2),
+           "call_median_us": round(us_med, 2),
+           "query_tokens_per_s": round(sum(chunk) / (us * 1e-6), 1),
+           "roofline": _mfma_roofline("prefill_kernel (the batch's chunks)", flops, pf_us, "f16"),
+           "decode_rows": _hbm_roofline("decode_kernel + merge (the batch's decode rows)",
+                                        dec_bytes, dec_us)}
+    if sample:
+        from oracle import pkvref
+        hq = w.num_q_heads
+        ind = w.q_indptr.tolist()
+        toks = list(range(nd)) + [ind[b] + i for b in range(nd, w.batch) for i in (0, 2046, 4092)]
+        rows = [t * hq + h for t in toks for h in (0, 15)]
+        pkvref.kv_append(w.dtype, w.k_cache, w.v_cache, w.k_new, w.v_new, w.slots)
+        run()
+        torch.cuda.synchronize()
+        ref, _ = pkvref.prefill(w.dtype, w.k_cache, w.v_cache, w.q, w.q_indptr, w.block_table,
+                                w.context_lens, w.scale, rows=rows, n_threads=host_cores())
+        got = out.float().cpu().double().numpy().reshape(-1, w.head_dim)[rows]
+        res["parity"] = _parity(got, ref, w.dtype)
+    return res
 
 
 if __name__ == "__main__":

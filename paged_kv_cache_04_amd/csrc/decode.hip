@@ -176,7 +176,9 @@ struct PageRegs {
   uint32_t v[C::VT][C::VW];
 };
 
-template <typename QT, typename CT, int D, int G>
+// WIN: a sliding window is in force (the visited-page map and the hidden-key
+// test are compiled only then).
+template <typename QT, typename CT, int D, int G, bool WIN>
 __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeArgs a) {
   using C = DecodeCfg<QT, CT, D, G>;
   using TT = QT;
@@ -208,14 +210,14 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeArgs a) {
   const int n_pages = (L + P - 1) / P;
   // visible keys: t >= lo, and t < sink_n (without a window: all of them)
   int lo = 0, sink_n = 0;
-  if (a.window > 0) {
+  if (WIN && a.window > 0) {
     lo = max(0, L - a.window);
     sink_n = min(a.sink, L);
   }
   // visited pages: logical [0, sp) then [wp, n_pages); virtual page v is
   // logical page v (v < sp) or v + gap
-  const int sp = lo > 0 ? (sink_n + P - 1) / P : 0;
-  const int wp = max(sp, lo / P);
+  const int sp = WIN && lo > 0 ? (sink_n + P - 1) / P : 0;
+  const int wp = WIN ? max(sp, lo / P) : 0;
   const int gap = wp - sp;
   int n_vp = n_pages - gap;
   const int cover = a.n_split * a.pages_per_split;
@@ -225,7 +227,10 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeArgs a) {
   }
   const int p0 = ks * a.pages_per_split;
   const int p1 = min(n_vp, p0 + a.pages_per_split);
-  auto lpage = [&](int v) { return v < sp ? v : v + gap; };
+  auto lpage = [&](int v) {
+    if constexpr (WIN) return v < sp ? v : v + gap;
+    return v;
+  };
 
   if (p0 >= p1) {  // empty split: no keys, o = 0 and lse = -inf
     for (int idx = tid; idx < G * D; idx += NW * 64) {
@@ -322,12 +327,15 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeArgs a) {
 
   // Online-softmax update with the wave's i-th page held in r.
   // key t of a visited page is visible
-  auto vis = [&](int t) { return t < L && (t >= lo || t < sink_n); };
+  auto vis = [&](int t) {
+    if constexpr (WIN) return t < L && (t >= lo || t < sink_n);
+    return t < L;
+  };
   auto compute = [&](const PageRegs<QT, CT, D, G>& r, int i) {
     const int pi = lpage(p0 + w + NW * i);  // logical page index
     const int t0 = pi * P;
     // some key of the page is past the end or hidden by the window
-    const bool partial = t0 + P > L || max(t0, sink_n) < min(t0 + P, lo);
+    const bool partial = t0 + P > L || (WIN && max(t0, sink_n) < min(t0 + P, lo));
 
     float s[C::KP];
 #pragma unroll
@@ -508,19 +516,26 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeArgs a) {
   }
 }
 
+template <typename QT, typename CT, int D, bool WIN>
+hipError_t launch_w(int group, const dim3 grid, const DecodeArgs& a, hipStream_t stream) {
+  const dim3 block(NW * 64);
+  switch (group) {
+    case 1: hipLaunchKernelGGL((decode_kernel<QT, CT, D, 1, WIN>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<QT, CT, D, 2, WIN>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<QT, CT, D, 4, WIN>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((decode_kernel<QT, CT, D, 8, WIN>), grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <typename QT, typename CT, int D>
 hipError_t launch_g(int group, int batch, const DecodeArgs& a, hipStream_t stream) {
   const int64_t blocks = (int64_t)batch * a.num_kv_heads * a.n_split;
   if (blocks == 0) return hipSuccess;
-  const dim3 grid((unsigned)blocks), block(NW * 64);
-  switch (group) {
-    case 1: hipLaunchKernelGGL((decode_kernel<QT, CT, D, 1>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<QT, CT, D, 2>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<QT, CT, D, 4>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((decode_kernel<QT, CT, D, 8>), grid, block, 0, stream, a); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  const dim3 grid((unsigned)blocks);
+  if (a.window > 0) return launch_w<QT, CT, D, true>(group, grid, a, stream);
+  return launch_w<QT, CT, D, false>(group, grid, a, stream);
 }
 
 template <typename TT>
