@@ -252,7 +252,7 @@ def main():
                    "head_dim": w.head_dim, "page_size": w.page_size, "n_split": n_split,
                    "split_tokens": args.split_tokens},
         "kv_gbps": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-        "roofline": {"bound": "hbm", "kernel": "decode_kernel (split-KV partials)",
+        "roofline": {"bound": "hbm", "kernel": f"{_decode_kernel_name(w)} (split-KV partials)",
                      "achieved": round(achieved, 1), "peak": A.HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / A.HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": kv_bytes,
@@ -283,13 +283,22 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def _decode_kernel_name(w) -> str:
+    """The decode kernel the library runs for this workload: the matrix-core
+    kernel for 8 query heads per KV head (fp8 pools from 4), else the vector
+    kernel."""
+    g = w.num_q_heads // w.num_kv_heads
+    mfma = w.head_dim == 128 and w.dtype in ("f16", "bf16") and (g == 8 or (w.is_fp8 and g == 4))
+    return "decode_mfma_kernel" if mfma else "decode_kernel"
+
+
 def _kernel_sha() -> str:
     """Hash of the sources the partial-decode kernel is built from; a stored
     traffic figure is reported only while it matches."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_04_amd", "csrc")
-    for name in ("decode.hip", "pkv_device.h", "pkv_internal.h"):
+    for name in ("decode.hip", "decode_mfma.hip", "pkv_device.h", "pkv_internal.h"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -436,7 +445,7 @@ def bench_fp8(args, dev, sample):
                        "131072 keys per sequence (131071 stored + 1 quantized on append)",
            "tokens_per_s": round(w.batch / (step_us * 1e-6), 1), "ms_per_step": round(
                step_us / 1e3, 5), "n_split": n_split, "kernel_median_us": round(part_med, 2),
-           "roofline": _hbm_roofline("decode_kernel<f16 q, fp8 e4m3 cache> (split-KV partials)",
+           "roofline": _hbm_roofline("decode_mfma_kernel<f16 q, fp8 e4m3 cache> (split-KV partials)",
                                      kv_bytes, part_us)}
     if sample:
         from oracle import pkvref
@@ -499,7 +508,7 @@ def bench_window(args, dev, sample, reuse=None):
            "tokens_per_s": round(w.batch / (step_us * 1e-6), 1),
            "ms_per_step": round(step_us / 1e3, 5), "n_split": n_split,
            "kernel_median_us": round(part_med, 2),
-           "roofline": _hbm_roofline("decode_kernel (windowed split-KV partials)", kv_bytes,
+           "roofline": _hbm_roofline("decode_mfma_kernel (windowed split-KV partials)", kv_bytes,
                                      part_us)}
     if sample:
         from oracle import pkvref
@@ -553,7 +562,7 @@ def bench_mixed(args, dev, sample):
            "call_median_us": round(us_med, 2),
            "query_tokens_per_s": round(sum(chunk) / (us * 1e-6), 1),
            "roofline": _mfma_roofline("prefill_kernel (the batch's chunks)", flops, pf_us, "f16"),
-           "decode_rows": _hbm_roofline("decode_kernel + merge (the batch's decode rows)",
+           "decode_rows": _hbm_roofline("decode_mfma_kernel + merge (the batch's decode rows)",
                                         dec_bytes, dec_us)}
     if sample:
         from oracle import pkvref

@@ -84,8 +84,9 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 // Decode split plan.  Auto rule: aim for about 512 workgroups (two per CU
-// on a 256-CU device, one round of residency) and never less than 16 pages
-// (256 keys) per split.
+// on a 256-CU device, one round of residency) for the vector decode kernel,
+// 256 (one per CU) for the matrix-core kernel, whose workgroups each keep more
+// bytes in flight; never less than 16 pages (256 keys) per split.
 struct Plan {
   int32_t n_split;
   int32_t pages_per_split;
@@ -94,11 +95,12 @@ struct Plan {
 };
 
 constexpr int64_t kTargetWorkgroups = 512;
+constexpr int64_t kTargetWorkgroupsMfma = 256;
 constexpr int32_t kXcdSplitTiles = 64;    // prefill: query tiles per (b, kv head)
 constexpr int32_t kMinSplitPages = 16;
 
 int make_plan(const pkv_cache_desc* d, int32_t batch, int32_t num_q_heads,
-              int32_t max_context_len, int32_t split_tokens, Plan* plan) {
+              int32_t max_context_len, int32_t split_tokens, int q_dtype, Plan* plan) {
   const int P = d->page_size;
   const int64_t max_pages = ((int64_t)max_context_len + P - 1) / P;
   int64_t pps;
@@ -109,7 +111,11 @@ int make_plan(const pkv_cache_desc* d, int32_t batch, int32_t num_q_heads,
     pps = split_tokens / P;
   } else if (split_tokens == 0) {
     const int64_t units = (int64_t)batch * d->num_kv_heads;
-    int64_t want = units > 0 ? (kTargetWorkgroups + units - 1) / units : 1;
+    const int group = d->num_kv_heads > 0 ? num_q_heads / d->num_kv_heads : 1;
+    const int64_t target = pkv::decode_mfma_supported(d->dtype, q_dtype, d->head_dim, group)
+                               ? kTargetWorkgroupsMfma
+                               : kTargetWorkgroups;
+    int64_t want = units > 0 ? (target + units - 1) / units : 1;
     const int64_t cap = (max_pages + kMinSplitPages - 1) / kMinSplitPages;
     if (want > cap) want = cap;
     if (want < 1) want = 1;
@@ -200,7 +206,7 @@ int check_decode(const pkv_cache_desc* desc, const void* k_cache, const void* v_
   }
   if (int rc = make_plan(desc, batch, num_q_heads,
                          plan_len(max_context_len, dc->opts, desc->page_size), split_tokens,
-                         &dc->plan))
+                         dc->opts.q_dtype, &dc->plan))
     return rc;
   const int64_t blocks = (int64_t)batch * desc->num_kv_heads * dc->plan.n_split;
   if (blocks > 0x7fffffff) return fail(PKV_ERR_INVALID, "grid too large (%lld)", (long long)blocks);
@@ -231,6 +237,15 @@ pkv::DecodeArgs decode_args(const pkv_cache_desc* desc, const void* k_cache,
   return a;
 }
 
+// The decode kernel for these types and shapes: matrix cores for grouped
+// 16-bit queries (G >= 4, head_dim 128), the vector kernel otherwise.
+hipError_t launch_any_decode(const pkv_cache_desc* desc, int q_dtype, int group, int batch,
+                             const pkv::DecodeArgs& a, hipStream_t s) {
+  if (pkv::decode_mfma_supported(desc->dtype, q_dtype, desc->head_dim, group))
+    return pkv::launch_decode_mfma(desc->dtype, q_dtype, group, batch, a, s);
+  return pkv::launch_decode(desc->dtype, q_dtype, desc->head_dim, group, batch, a, s);
+}
+
 int decode_impl(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache,
                 const void* q, int32_t batch, int32_t num_q_heads, const int32_t* block_table,
                 int32_t block_table_stride, const int32_t* context_lens, int32_t max_context_len,
@@ -252,7 +267,7 @@ int decode_impl(const pkv_cache_desc* desc, const void* k_cache, const void* v_c
     a.out = out;
     a.lse_out = lse_out;
     return hip_status(
-        pkv::launch_decode(desc->dtype, qdt, desc->head_dim, dc.group, batch, a, s),
+        launch_any_decode(desc, qdt, dc.group, batch, a, s),
         "decode launch");
   }
   if (!workspace || workspace_bytes < dc.plan.ws_bytes)
@@ -263,7 +278,7 @@ int decode_impl(const pkv_cache_desc* desc, const void* k_cache, const void* v_c
   a.o_part = (float*)workspace;
   a.lse_part = (float*)((char*)workspace + dc.plan.o_bytes);
   if (int rc = hip_status(
-          pkv::launch_decode(desc->dtype, qdt, desc->head_dim, dc.group, batch, a, s),
+          launch_any_decode(desc, qdt, dc.group, batch, a, s),
           "decode launch"))
     return rc;
   return hip_status(pkv::launch_merge(qdt, desc->head_dim, a.o_part, a.lse_part,
@@ -292,8 +307,8 @@ int partials_impl(const pkv_cache_desc* desc, const void* k_cache, const void* v
   a.direct = 0;
   a.o_part = (float*)workspace;
   a.lse_part = (float*)((char*)workspace + dc.plan.o_bytes);
-  return hip_status(pkv::launch_decode(desc->dtype, dc.opts.q_dtype, desc->head_dim, dc.group,
-                                       batch, a, (hipStream_t)stream),
+  return hip_status(launch_any_decode(desc, dc.opts.q_dtype, dc.group, batch, a,
+                                     (hipStream_t)stream),
                     "decode launch");
 }
 
@@ -310,7 +325,8 @@ int plan_impl(const pkv_cache_desc* desc, int32_t batch, int32_t num_q_heads,
   if (!n_split || !workspace_bytes) return fail(PKV_ERR_INVALID, "NULL output pointer");
   Plan plan;
   if (int rc = make_plan(desc, batch, num_q_heads,
-                         plan_len(max_context_len, o, desc->page_size), split_tokens, &plan))
+                         plan_len(max_context_len, o, desc->page_size), split_tokens, o.q_dtype,
+                         &plan))
     return rc;
   *n_split = plan.n_split;
   *workspace_bytes = plan.n_split > 1 ? plan.ws_bytes : 0;

@@ -70,6 +70,12 @@ hipError_t launch_gather(int dtype, int head_dim, int num_kv_heads, int64_t num_
 hipError_t launch_decode(int kv_dtype, int q_dtype, int head_dim, int group, int batch,
                          const DecodeArgs& a, hipStream_t stream);
 
+// Decode on the matrix cores (16-bit queries, head_dim 128, G = 4 or 8, any
+// 16-bit or fp8 pool); same arguments and results as launch_decode.
+bool decode_mfma_supported(int kv_dtype, int q_dtype, int head_dim, int group);
+hipError_t launch_decode_mfma(int kv_dtype, int q_dtype, int group, int batch,
+                              const DecodeArgs& a, hipStream_t stream);
+
 // fp8 quantizing append from src_dtype (f32, f16, bf16) new tokens.
 hipError_t launch_kv_append_quant(int fp8_dtype, int src_dtype, int head_dim, int num_kv_heads,
                                   int64_t num_pages, void* k_cache, void* v_cache,

@@ -86,7 +86,8 @@ def test_decode_workspace_required_when_split(L):
 
 
 @pytest.mark.parametrize("name,batch,hq,hkv,max_len,want_split", [
-    ("llama70b_128k", 8, 16, 2, 131072, 32),
+    ("llama70b_128k", 8, 16, 2, 131072, 16),       # G 8: matrix-core kernel, 256 workgroups
+    ("llama70b_128k, G 4", 8, 8, 2, 131072, 32),   # G 4, 16-bit: vector kernel, 512
     ("tiny", 4, 8, 8, 511, 2),
     ("prefix", 256, 32, 8, 2560, 1),
 ])
@@ -182,7 +183,7 @@ def test_plan_ex_counts_window_pages_only(L):
     d = desc(hkv=2)
     n, ws = C.c_int32(), C.c_size_t()
     assert L.pkv_decode_plan_ex(C.byref(d), 8, 16, 131072, 0, None, C.byref(n), C.byref(ws)) == 0
-    assert n.value == 32
+    assert n.value == 16
     o = _opts(q_dtype=2, window=4096, sink=128)
     assert L.pkv_decode_plan_ex(C.byref(d), 8, 16, 131072, 0, C.byref(o), C.byref(n),
                                 C.byref(ws)) == 0
