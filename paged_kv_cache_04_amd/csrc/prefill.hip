@@ -9,12 +9,12 @@
 // section 2.2).  Keys are reached through the block table (page 3, section
 // 3.2).
 //
-// Work decomposition.  A workgroup (4 wavefronts) owns 128 query rows of one
-// (sequence, KV head): 128 / G chunk positions times the G query heads that
-// share the KV head (page 4, section 2.2, GQA), so the G heads reuse every
-// K/V tile.  Wave w owns rows 32w .. 32w+31.  Keys go in tiles of 64 (four
-// pages) through two LDS buffers: while the waves compute on one, direct
-// global-to-LDS loads (no registers) fill the other with the next tile.
+// Work decomposition.  A workgroup (8 wavefronts, one per CU) owns 256 query
+// rows of one (sequence, KV head): 256 / G chunk positions times the G query
+// heads that share the KV head (page 4, section 2.2, GQA), so the G heads
+// reuse every K/V tile.  Wave w owns rows 32w .. 32w+31.  Keys go in tiles of
+// 64 (four pages); direct global-to-LDS loads (no registers) bring each K and
+// V page into LDS once for all 256 rows, one tile ahead of its use.
 //
 // LDS layout: K and V tiles are stored as they sit in the pages, one 256-byte
 // row per key, with the sixteen 16-byte chunks of row r permuted by
@@ -23,15 +23,18 @@
 // Per tile and wave, on 32x32x16 MFMAs with fp32 accumulation:
 //   S^T (64 keys x 32 rows) = K x Q^T: K rows are read as 16-byte chunks, Q^T
 //       stays in registers.  The scores of a query row sit in one lane (16 per
-//       32-key block, the other 16 in lane + 32): the row max is an in-lane
-//       max and one exchange.
-//   online softmax in base 2 (log2 e folded into the scale); the reference
-//       max of a row moves only when a score exceeds it by more than 8 (in
-//       log2 units), so the accumulators are rescaled rarely (wave vote).
-//   O^T (128 x 32) += V^T x P^T: the probabilities are converted in place to
+//       32-key block, the other 16 in lane + 32).
+//   online softmax in base 2 (log2 e folded into the scale) against a lazy
+//       reference max: the weights exp2(c (s - m)) are formed with the current
+//       reference m, which moves to the running max (rescaling the
+//       accumulators) only when a weight could exceed 2^8 (its lane's sum
+//       does) or no reference is set yet.
+//   O^T (128 x 32) += V^T x P^T: the weights are converted in place to
 //       bf16/f16 (the S^T output layout is the P^T operand layout), and the
 //       V^T operand comes from transposing LDS reads (ds_read_b64_tr_b16) of
 //       the row-major V tile, with keys taken in the order P^T holds them.
+// The tiles are software-pipelined per wave: the MFMAs that form S of the
+// next tile run beside the vector work of this tile's weights.
 // Keys past the causal limit or the sequence end are selected out of S; V
 // rows past the sequence end are zeroed in LDS before use, so stale or NaN
 // slots in a partly filled last page never reach the products.
@@ -45,11 +48,11 @@ namespace {
 constexpr int P = kPageSize;
 constexpr int D = 128;           // head_dim of the MFMA kernel
 constexpr int BK = 64;           // keys per tile (4 pages)
-constexpr int NWP = 4;           // waves per workgroup
-constexpr int ROWS = 128;        // query rows per workgroup
+constexpr int NWP = 8;           // waves per workgroup
+constexpr int ROWS = 256;        // query rows per workgroup
 constexpr int ROWB = D * 2;      // bytes per key row (256)
 constexpr int TILEB = BK * ROWB; // bytes per K or V tile (16 KiB)
-constexpr float kLazyLog2 = 8.f; // rescale when a row max grows by > 2^8
+constexpr int kLazyLog2 = 8;     // weights stay below 2^(8 + POFF)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -127,7 +130,7 @@ __device__ __forceinline__ uint2 read_tr(const lds_u8* p) {
 }
 
 template <typename TT, int G>
-__global__ __launch_bounds__(NWP * 64, 2) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   using M = Mfma<TT>;
   constexpr int NPOS = ROWS / G;  // chunk positions per workgroup
   __shared__ __align__(1024) uint8_t k_lds0[TILEB];
@@ -210,14 +213,16 @@ __global__ __launch_bounds__(NWP * 64, 2) void prefill_kernel(PrefillArgs a) {
 
   if (tid == 0) bad_flag = bad ? 1 : 0;
 
-  // ---- staging: wave w copies page w of the tile (key rows 16w .. 16w+15)
-  // of K and V as four 1-KiB LDS chunks of four rows; lane i of a chunk fills
-  // row 4j + i/16, physical chunk i%16 with logical chunk (i%16) ^ swz(row).
-  // The page, its descriptor and the LDS destination are the same for the
-  // whole wave (scalar registers); each lane adds a fixed offset.  The page id
-  // of the next tile is loaded one tile ahead.
+  // ---- staging: waves 0-3 copy the K pages and waves 4-7 the V pages of a
+  // tile, wave w page w % 4 (key rows 16(w%4) .. +15), as four 1-KiB LDS
+  // chunks of four rows; lane i of a chunk fills row 4j + i/16, physical
+  // chunk i%16 with logical chunk (i%16) ^ swz(row).  The page, its
+  // descriptor and the LDS destination are the same for the whole wave
+  // (scalar registers); each lane adds a fixed offset.
   const int64_t head_block = (int64_t)P * D * 2;
   const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int wp = wu & 3;          // page of the tile this wave copies
+  const bool kwave = wu < 4;      // waves 0-3 copy K pages, waves 4-7 V pages
   uint32_t dma_off[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -225,25 +230,24 @@ __global__ __launch_bounds__(NWP * 64, 2) void prefill_kernel(PrefillArgs a) {
     dma_off[j] = (uint32_t)(r * ROWB + (((lane & 15) ^ swz(r)) * 16));
   }
   bool my_bad = false;
-  int pid_next = 0;
-  auto fetch_pid = [&](int it) {
-    const int pi = it * (BK / P) + wu;
-    pid_next = (it < n_tiles && pi < seq_pages) ? bt_row[pi] : 0;
+  // block-table entry of this wave's page of tile t (0 past the sequence)
+  auto load_pid = [&](int t) -> int {
+    const int pi = t * (BK / P) + wp;
+    return (t < n_tiles && pi < seq_pages) ? bt_row[pi] : 0;
   };
-  auto issue_tile = [&](int it, lds_u8* kdst, lds_u8* vdst) {
-    const int pi = it * (BK / P) + wu;
-    int pid = __builtin_amdgcn_readfirstlane(pid_next);
-    fetch_pid(it + 1);
-    if (pi < seq_pages && (pid < 0 || pid >= a.num_pages)) my_bad = true;
-    if (pid < 0 || pid >= a.num_pages) pid = 0;   // always a readable page
-    const int64_t base = ((int64_t)pid * a.num_kv_heads + g) * head_block;
-    const __amdgpu_buffer_rsrc_t kr = page_rsrc((const char*)a.k_cache + base);
-    const __amdgpu_buffer_rsrc_t vr = page_rsrc((const char*)a.v_cache + base);
+  // wave-uniform page id, flagged and replaced by page 0 when out of range
+  auto check_pid = [&](int t, int loaded) -> int {
+    const int pid = __builtin_amdgcn_readfirstlane(loaded);
+    const int pi = t * (BK / P) + wp;
+    const bool out = pid < 0 || pid >= a.num_pages;
+    if (pi < seq_pages && out) my_bad = true;
+    return out ? 0 : pid;
+  };
+  auto copy_page = [&](const void* pool, int pid, lds_u8* dst) {
+    const __amdgpu_buffer_rsrc_t r =
+        page_rsrc((const char*)pool + ((int64_t)pid * a.num_kv_heads + g) * head_block);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      dma16(kr, dma_off[j], kdst + (16 * wu + 4 * j) * ROWB);
-      dma16(vr, dma_off[j], vdst + (16 * wu + 4 * j) * ROWB);
-    }
+    for (int j = 0; j < 4; ++j) dma16(r, dma_off[j], dst + (16 * wp + 4 * j) * ROWB);
   };
   // V rows of keys past the sequence end become zero (edge tiles only)
   auto zero_tail = [&](int it, uint8_t* vdst) {
@@ -262,45 +266,10 @@ __global__ __launch_bounds__(NWP * 64, 2) void prefill_kernel(PrefillArgs a) {
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-  float m_run = -INFINITY;  // running max of the raw (unscaled) scores of this row
-  float l_run = 0.f;        // running sum of exp2(c * s - c * m_run) over this lane's keys
-
-  // Online-softmax update for one tile: running max, rescale, probabilities
-  // packed as the B operands of the PV MFMA (k-step ks = keys 16ks..16ks+15).
-  auto softmax_tile = [&](f32x16_t (&s)[2], u32x4_t (&pk)[4]) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    const bool grow = (m_run == -INFINITY) ? (mx > -INFINITY) : ((mx - m_run) * c > kLazyLog2);
-    if (__ballot(grow) != 0) {
-      __asm__ volatile("");   // keep this a branch: the rescale is rare
-      mx = fmaxf(mx, xor_f(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = (m_run == -INFINITY) ? 0.f : exp2_fast((m_run - m_new) * c);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-      m_run = m_new;
-    }
-    const float mc = (m_run == -INFINITY) ? 0.f : m_run * c - M::POFF;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = exp2_fast(fmaf(s[kb][8 * sub + e], c, -mc));   // masked: exp2(-inf) = 0
-          l_run += p[e];
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pk[2 * kb + sub][e] = M::pack(p[2 * e], p[2 * e + 1]);
-      }
-  };
+  // reference max of this row (raw scores): the running max at its last
+  // update; the accumulators hold weights exp2(c * (s - m_run)) * 2^POFF
+  float m_run = -INFINITY;
+  float l_run = 0.f;        // sum of this lane's weights (keys of its half)
 
   // Per-lane LDS byte offsets, the same for every tile: the K operand of
   // k-step ks (row n, logical chunk 2ks + half) and the V^T operand reads of
@@ -320,100 +289,214 @@ __global__ __launch_bounds__(NWP * 64, 2) void prefill_kernel(PrefillArgs a) {
     vb_off[db] = (key_a0 + 8) * ROWB + ((lc ^ swz(key_a0 + 8)) * 16) + sub8;
   }
 
-  // One tile from LDS buffers (kt, vt); MASKED tiles are the few that reach
-  // past some row's causal limit or the sequence end.
-  auto compute_tile = [&](int it, const lds_u8* kt, const lds_u8* vt, auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    // S^T = K Q^T for two 32-key blocks
-    f32x16_t s[2];
+  // S^T = K Q^T of one tile, two 32-key blocks: score i of block kb is key
+  // t0 + 32kb + 8(i/4) + 4half + i%4 of this lane's row.  Group g covers the
+  // k-steps 2g, 2g+1 of both blocks (four MFMAs).
+  typedef u32x4_t KOps[4];
+  auto k_read = [&](const lds_u8* kt, int g, KOps& ka) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+      ka[x] = *reinterpret_cast<const u32x4_t __attribute__((address_space(3)))*>(
+          kt + (x & 1) * 32 * ROWB + k_off[2 * g + (x >> 1)]);
+  };
+  auto s_group = [&](int g, const KOps& ka, f32x16_t (&s)[2]) {
     const f32x16_t zero16 = {};
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const u32x4_t av = *reinterpret_cast<const u32x4_t __attribute__((address_space(3)))*>(
-            kt + kb * 32 * ROWB + k_off[ks]);
-        s[kb] = M::run(av, qreg[ks], ks == 0 ? zero16 : s[kb]);
-      }
+    for (int x = 0; x < 4; ++x) {
+      const int ks = 2 * g + (x >> 1), kb = x & 1;
+      s[kb] = M::run(ka[x], qreg[ks], ks == 0 ? zero16 : s[kb]);
     }
-    // keys past this row's position (or the sequence end) are selected out:
-    // score i of block kb is key t0 + 32kb + 8(i/4) + 4half + i%4
-    const int t0 = it * BK;
-    if constexpr (MASKED) {
-      const int thr = min(apos, kvl - 1) - t0 - 4 * half;
+  };
+  auto s_tile = [&](const lds_u8* kt, f32x16_t (&s)[2]) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      KOps ka;
+      k_read(kt, g, ka);
+      s_group(g, ka, s);
+    }
+  };
+  // keys past this row's position (or the sequence end) are selected out
+  auto mask_tile = [&](int it, f32x16_t (&s)[2]) {
+    const int thr = min(apos, kvl - 1) - it * BK - 4 * half;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        s[kb][i] = (32 * kb + 8 * (i >> 2) + (i & 3) <= thr) ? s[kb][i] : -INFINITY;
+  };
+  // Weights of keys 16ks .. 16ks+15 against the reference max (mc = m_run *
+  // c - POFF), packed as the B operand of PV k-step ks; their fp32 sum goes
+  // into ls.
+  auto weights = [&](const f32x16_t (&s)[2], int ks, float mc, u32x4_t& pk, float& ls) {
+    const int kb = ks >> 1, sub = ks & 1;
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = exp2_fast(fmaf(s[kb][8 * sub + e], c, -mc));   // masked: exp2(-inf) = 0
+      ls += p[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pk[e] = M::pack(p[2 * e], p[2 * e + 1]);
+  };
+  // O^T += V^T P^T for k-step ks.  The 16-lane group q16 = lane / 16 covers
+  // head dims 32db + 16 (q16 & 1) .. +15 with key half h = q16 >> 1; source
+  // lane 4k + j of the group points at key (16ks + 4h + k) (+8 for slots
+  // 4..7), dims +4j .. +4j+3, so result lane i holds dim +i for keys k = 0..3.
+  // The swizzle of key 16ks + x equals that of key x, so k-step ks only adds
+  // 16 rows to the k-step 0 offsets.
+  typedef u32x4_t VOps[4];
+  auto v_read = [&](const lds_u8* vt, int ks, VOps& va) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const uint2 lo = read_tr(vt + ks * 16 * ROWB + va_off[db]);
+      const uint2 hi = read_tr(vt + ks * 16 * ROWB + vb_off[db]);
+      va[db][0] = lo.x;
+      va[db][1] = lo.y;
+      va[db][2] = hi.x;
+      va[db][3] = hi.y;
+    }
+  };
+  auto pv_step = [&](const VOps& va, const u32x4_t& pk) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[db] = M::run(va[db], pk, o[db]);
+  };
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+
+  // ---- software pipeline over key tiles.  Iteration j holds S(j) in
+  // registers, K(j+1) and V(j) in LDS, and:
+  //   copies K(j+2) into the buffer K(j) used (waves 0-3) and V(j+1) into the
+  //   other V buffer (waves 4-7); every wave finished with both buffers
+  //   before the last barrier;
+  //   computes S(j+1) on the matrix cores while the vector units form the
+  //   weights of S(j) against the current reference (the stream is fenced
+  //   into regions of four MFMAs, each with its K operand reads and the
+  //   weights of one 16-key step, which bounds the registers in flight);
+  //   checks the weights (rare fix-up, below);
+  //   O += P(j) V(j);
+  //   waits for its copies and meets the other waves.
+  // Tiles [0, n_full) lie wholly below every row's causal limit (and inside
+  // the sequence); only the rest need the mask and the V tail fill.  S(j+1)
+  // is formed even for the last tile (from a buffer that no copy targets;
+  // the result is unused) so that the stream has no branch.  The LDS
+  // buffers are named at compile time in each instance (even / odd j), which
+  // lets the compiler see that reads of one buffer never wait for the copy
+  // into another.
+  const float wmax = __builtin_ldexpf(1.f, kLazyLog2 + (int)M::POFF);
+  int pid_f = 0;      // block-table entry of the page this wave copies next
+  auto iteration = [&](int j, lds_u8* kd, const lds_u8* kc, uint8_t* vc_raw, lds_u8* vd,
+                       f32x16_t (&s_cur)[2], f32x16_t (&s_nxt)[2], auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const lds_u8* vc = (const lds_u8*)vc_raw;
+    if (kwave) {
+      if (j + 2 < n_tiles) copy_page(a.k_cache, check_pid(j + 2, pid_f), kd);
+      pid_f = load_pid(j + 3);
+    } else {
+      if (j + 1 < n_tiles) copy_page(a.v_cache, check_pid(j + 1, pid_f), vd);
+      pid_f = load_pid(j + 2);
+    }
+    if constexpr (MASKED) mask_tile(j, s_cur);
+    fence();
+
+    // S(j+1) beside the weights of S(j)
+    const float mc = (m_run == -INFINITY) ? 0.f : m_run * c - M::POFF;
+    u32x4_t pk[4];
+    float ls = 0.f;
+    KOps ka;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      k_read(kc, g, ka);
+      weights(s_cur, g, mc, pk[g], ls);
+      s_group(g, ka, s_nxt);
+      fence();
+    }
+    // A weight above 2^(8+POFF) shows in its lane's sum; so does a reference
+    // not set yet.  Then the reference moves to the running max (the wave
+    // votes; rare: scores seldom grow by more than 8 in log2 units), the
+    // accumulators are rescaled and the weights recomputed.  A NaN sum does
+    // not vote, so NaN reaches the output.
+    if (__ballot(ls > wmax || m_run == -INFINITY) != 0) {
+      __asm__ volatile("");   // keep this a branch: it is rare
+      float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          s[kb][i] = (32 * kb + 8 * (i >> 2) + (i & 3) <= thr) ? s[kb][i] : -INFINITY;
-    }
-    u32x4_t pk[4];
-    softmax_tile(s, pk);
-
-    // O^T += V^T P^T.  The 16-lane group q16 = lane / 16 covers head dims
-    // 32db + 16 (q16 & 1) .. +15 with key half h = q16 >> 1; source lane
-    // 4k + j of the group points at key (16ks + 4h + k) (+8 for slots 4..7),
-    // dims +4j .. +4j+3, so result lane i holds dim +i for keys k = 0..3.
-    // The swizzle of key 16ks + x equals that of key x, so k-step ks only
-    // adds 16 rows to the k-step 0 offsets.
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[kb][i]);
+      mx = fmaxf(mx, xor_f(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_run == -INFINITY) ? 0.f : exp2_fast((m_run - m_new) * c);
+      l_run *= alpha;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const uint2 lo = read_tr(vt + ks * 16 * ROWB + va_off[db]);
-        const uint2 hi = read_tr(vt + ks * 16 * ROWB + vb_off[db]);
-        u32x4_t av;
-        av[0] = lo.x;
-        av[1] = lo.y;
-        av[2] = hi.x;
-        av[3] = hi.y;
-        o[db] = M::run(av, pk[ks], o[db]);
-      }
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      m_run = m_new;
+      const float mc2 = (m_run == -INFINITY) ? 0.f : m_run * c - M::POFF;
+      ls = 0.f;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) weights(s_cur, g, mc2, pk[g], ls);
     }
+    fence();
+    if (MASKED && j * BK + BK > kvl) {
+      zero_tail(j, vc_raw);
+      __syncthreads();
+    }
+    VOps v0, v1;
+    v_read(vc, 0, v0);
+    v_read(vc, 1, v1);
+    pv_step(v0, pk[0]);
+    fence();
+    v_read(vc, 2, v0);
+    pv_step(v1, pk[1]);
+    fence();
+    v_read(vc, 3, v1);
+    pv_step(v0, pk[2]);
+    fence();
+    pv_step(v1, pk[3]);
+    l_run += ls;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   };
 
   lds_u8* kb0 = (lds_u8*)k_lds0;
   lds_u8* kb1 = (lds_u8*)k_lds1;
   lds_u8* vb0 = (lds_u8*)v_lds0;
   lds_u8* vb1 = (lds_u8*)v_lds1;
+  f32x16_t s0[2], s1[2];
 
-  // Tile it computes from buffer it % 2 while tile it + 1 loads into the
-  // other one.  Tiles [0, n_full) lie wholly below every row's causal limit
-  // (and inside the sequence); only the rest need the mask and the tail fill.
-  auto run_tile = [&](int it, auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    const bool odd = (it & 1) != 0;
-    if (MASKED && it * BK + BK > kvl) {
-      zero_tail(it, odd ? v_lds1 : v_lds0);
-      __syncthreads();
+  // prologue: K(0), V(0), K(1) in; S(0)
+  {
+    const int pid0 = check_pid(0, load_pid(0));
+    if (kwave) {
+      copy_page(a.k_cache, pid0, kb0);
+      if (n_tiles > 1) copy_page(a.k_cache, check_pid(1, load_pid(1)), kb1);
+      pid_f = load_pid(2);
+    } else {
+      copy_page(a.v_cache, pid0, vb0);
+      pid_f = load_pid(1);
     }
-    if (it + 1 < n_tiles) issue_tile(it + 1, odd ? kb0 : kb1, odd ? vb0 : vb1);
-    compute_tile(it, odd ? kb1 : kb0, odd ? vb1 : vb0, masked_tag);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-  };
-  const int n_full = min(n_tiles, (hist + pos0 + 1) / BK);
-
-  fetch_pid(0);
-  issue_tile(0, kb0, vb0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  // Unmasked tiles in pairs, so that each half names its LDS buffers at
-  // compile time (which lets the compiler see that the reads of one buffer
-  // never wait for the copy into the other).
-  int it = 0;
-  for (; it + 1 < n_full; it += 2) {
-    issue_tile(it + 1, kb1, vb1);
-    compute_tile(it, kb0, vb0, BoolTag<false>{});
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (it + 2 < n_tiles) issue_tile(it + 2, kb0, vb0);
-    compute_tile(it + 1, kb1, vb1, BoolTag<false>{});
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    s_tile(kb0, s0);
+    __syncthreads();   // every wave has read K(0): its buffer takes K(2)
   }
-  for (; it < n_full; ++it) run_tile(it, BoolTag<false>{});
-  for (; it < n_tiles; ++it) run_tile(it, BoolTag<true>{});
+  const int n_full = min(n_tiles, (hist + pos0 + 1) / BK);
+  int j = 0;
+  for (; j + 1 < n_full; j += 2) {
+    iteration(j, kb0, kb1, v_lds0, vb1, s0, s1, BoolTag<false>{});
+    iteration(j + 1, kb1, kb0, v_lds1, vb0, s1, s0, BoolTag<false>{});
+  }
+  if (j < n_full) {
+    iteration(j, kb0, kb1, v_lds0, vb1, s0, s1, BoolTag<false>{});
+    ++j;
+  }
+  if (j < n_tiles && (j & 1)) {
+    iteration(j, kb1, kb0, v_lds1, vb0, s1, s0, BoolTag<true>{});
+    ++j;
+  }
+  for (; j < n_tiles; j += 2) {
+    iteration(j, kb0, kb1, v_lds0, vb1, s0, s1, BoolTag<true>{});
+    if (j + 1 < n_tiles) iteration(j + 1, kb1, kb0, v_lds1, vb0, s1, s0, BoolTag<true>{});
+  }
 
   // ---- epilogue
   if (my_bad) bad_flag = 1;
