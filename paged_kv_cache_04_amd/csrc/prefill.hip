@@ -151,13 +151,16 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   // their query tiles share the K/V stream in its L2.  With xcd_split, XCD x
   // takes the x-th eighth of the query tiles of every pair instead: every XCD
   // gets the same share of long and short sequences, and the tiles of one
-  // pair on one XCD still read the same keys together.
+  // pair on one XCD still read the same keys together.  Each XCD walks the
+  // pairs one after another (pair-major), so that a long pair's workgroups
+  // start together instead of queueing, alternately with short ones, behind
+  // chains of short workgroups on the same CUs.
   const int nbg = a.batch * a.num_kv_heads;
   int bg, mt;
   if (a.xcd_split) {
     const int x = blockIdx.x % 8, j = blockIdx.x / 8;
-    bg = j % nbg;
-    mt = x * a.m_tiles_x + j / nbg;
+    bg = j / a.m_tiles_x;
+    mt = x * a.m_tiles_x + j % a.m_tiles_x;
     if (mt >= a.m_tiles) return;     // padding of the last XCD's range
   } else {
     bg = blockIdx.x % nbg;
