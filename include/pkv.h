@@ -28,7 +28,8 @@
  *     on the host before any HIP call; on error nothing is enqueued and
  *     pkv_last_error() gives a message (per calling thread).
  *   - Supported shapes: page_size 16; head_dim 64 or 128; dtype f32, f16,
- *     bf16; H_q a multiple of H_kv with G in {1, 2, 4, 8}; the prefill call
+ *     bf16; H_q a multiple of H_kv with G in {1, 2, 4, 8, 16} (decode at
+ *     G = 16 needs head_dim 128 and f16 or bf16 queries); the prefill call
  *     needs f16 or bf16 and head_dim 128.  fp8 caches (PKV_FP8_E4M3,
  *     PKV_FP8_E5M2) are read by the *_ex decode calls with head_dim 128 and
  *     f16 or bf16 queries; kv_append and gather_kv copy their bytes, and

@@ -1,5 +1,5 @@
-// Paged decode attention on the matrix cores, for grouped queries (G = 8; fp8
-// pools from G = 4).
+// Paged decode attention on the matrix cores, for grouped queries (G = 8 and
+// 16; fp8 pools from G = 4).
 //
 // Same operation and work decomposition as the vector decode kernel: out =
 // softmax(q K^T * scale) V for each query head over keys 0 .. len-1 of its
@@ -12,7 +12,7 @@
 // page: S^T (16 keys x G heads) = K Q^T and O^T (D x G) += V^T P^T.  On the
 // vector units that is 16 G D multiply-adds per page (256 packed dot products
 // per lane at G = 8); on the matrix cores it is a handful of 16x16x32 MFMAs
-// with the heads as the N dimension (padded to 16).  A wave takes two pages
+// with the heads as the N dimension (padded to 16 below G = 16).  A wave takes two pages
 // per step (32 keys, the K dimension of one MFMA) so that:
 //
 //   S^T:  per page, 4 MFMAs (K-dim 128 = 4 x 32) of K (16 keys x 32 dims,
@@ -126,8 +126,10 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_mfma_kernel(DecodeArgs a) {
   using M = Mf<QT>;
   constexpr int PAGEB = C::PAGEB;
   // per-slot V buffers, one object per slot so that the compiler sees that a
-  // read of one slot never depends on the copies into the others
-  __shared__ __align__(1024) uint8_t vb0[NW * 2 * PAGEB];
+  // read of one slot never depends on the copies into the others; the first
+  // also holds the cross-wave reduction of the accumulators at the end
+  constexpr int VB0 = NW * 2 * PAGEB > NW * G * D * 4 ? NW * 2 * PAGEB : NW * G * D * 4;
+  __shared__ __align__(1024) uint8_t vb0[VB0];
   __shared__ __align__(1024) uint8_t vb1[NW * 2 * PAGEB];
   __shared__ __align__(1024) uint8_t vb2[C::NB > 2 ? NW * 2 * PAGEB : 16];
   __shared__ int pid_lds[NW][64];
@@ -497,6 +499,7 @@ hipError_t launch_w(int group, const dim3 grid, const DecodeArgs& a, hipStream_t
   switch (group) {
     case 4: hipLaunchKernelGGL((decode_mfma_kernel<QT, CT, 4, WIN>), grid, block, 0, stream, a); break;
     case 8: hipLaunchKernelGGL((decode_mfma_kernel<QT, CT, 8, WIN>), grid, block, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL((decode_mfma_kernel<QT, CT, 16, WIN>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -529,12 +532,13 @@ hipError_t launch_q(int kv_dtype, int group, int batch, const DecodeArgs& a,
 // kernel's 256 packed dot products per page and lane are what limits a 16-bit
 // pool, and fp8 pages carry half the bytes for the same work, so fp8 pools use
 // this kernel from G = 4.  With 16-bit pools at G = 4 the vector kernel keeps
-// up with memory and its deeper per-wave pipeline wins.
+// up with memory and its deeper per-wave pipeline wins.  G = 16 (a full MFMA
+// N dimension) is built here only.
 bool decode_mfma_supported(int kv_dtype, int q_dtype, int head_dim, int group) {
   const bool q16 = q_dtype == 1 || q_dtype == 2;
   const bool fp8 = kv_dtype == 3 || kv_dtype == 4;
   if (!q16 || head_dim != D || !(fp8 || kv_dtype == q_dtype)) return false;
-  return group == 8 || (fp8 && group == 4);
+  return group == 8 || group == 16 || (fp8 && group == 4);
 }
 
 hipError_t launch_decode_mfma(int kv_dtype, int q_dtype, int group, int batch,

@@ -65,15 +65,24 @@ int check_desc(const pkv_cache_desc* d) {
   return PKV_OK;
 }
 
+// G = 16 is decoded on the matrix cores only.
+int check_decode_group(const pkv_cache_desc* d, int q_dtype, int group) {
+  if (group == 16 && !pkv::decode_mfma_supported(d->dtype, q_dtype, d->head_dim, 16))
+    return fail(PKV_ERR_UNSUPPORTED,
+                "16 query heads per KV head: decode is built for head_dim 128 with f16 or bf16 "
+                "queries only");
+  return PKV_OK;
+}
+
 int check_heads(const pkv_cache_desc* d, int32_t num_q_heads, int* group) {
   if (num_q_heads <= 0) return fail(PKV_ERR_INVALID, "num_q_heads %d <= 0", num_q_heads);
   if (num_q_heads % d->num_kv_heads != 0)
     return fail(PKV_ERR_INVALID, "num_q_heads %d is not a multiple of num_kv_heads %d",
                 num_q_heads, d->num_kv_heads);
   const int g = num_q_heads / d->num_kv_heads;
-  if (g != 1 && g != 2 && g != 4 && g != 8)
-    return fail(PKV_ERR_UNSUPPORTED, "query heads per KV head %d: only 1, 2, 4, 8 are built",
-                g);
+  if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16)
+    return fail(PKV_ERR_UNSUPPORTED,
+                "query heads per KV head %d: only 1, 2, 4, 8, 16 are built", g);
   *group = g;
   return PKV_OK;
 }
@@ -192,6 +201,7 @@ int check_decode(const pkv_cache_desc* desc, const void* k_cache, const void* v_
   if (int rc = check_desc(desc)) return rc;
   if (int rc = resolve_opts(desc, opts, &dc->opts)) return rc;
   if (int rc = check_heads(desc, num_q_heads, &dc->group)) return rc;
+  if (int rc = check_decode_group(desc, dc->opts.q_dtype, dc->group)) return rc;
   if (batch < 0) return fail(PKV_ERR_INVALID, "batch %d < 0", batch);
   if (stride <= 0) return fail(PKV_ERR_INVALID, "block_table_stride %d <= 0", stride);
   if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)stride * desc->page_size)
@@ -320,6 +330,7 @@ int plan_impl(const pkv_cache_desc* desc, int32_t batch, int32_t num_q_heads,
   if (int rc = resolve_opts(desc, opts, &o)) return rc;
   int group = 0;
   if (int rc = check_heads(desc, num_q_heads, &group)) return rc;
+  if (int rc = check_decode_group(desc, o.q_dtype, group)) return rc;
   if (batch < 0) return fail(PKV_ERR_INVALID, "batch %d < 0", batch);
   if (max_context_len < 0) return fail(PKV_ERR_INVALID, "max_context_len %d < 0", max_context_len);
   if (!n_split || !workspace_bytes) return fail(PKV_ERR_INVALID, "NULL output pointer");

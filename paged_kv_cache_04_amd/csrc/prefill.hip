@@ -540,6 +540,7 @@ hipError_t launch_t(int group, const PrefillArgs& a, hipStream_t stream) {
     case 2: hipLaunchKernelGGL((prefill_kernel<TT, 2>), grid, block, 0, stream, a); break;
     case 4: hipLaunchKernelGGL((prefill_kernel<TT, 4>), grid, block, 0, stream, a); break;
     case 8: hipLaunchKernelGGL((prefill_kernel<TT, 8>), grid, block, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL((prefill_kernel<TT, 16>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

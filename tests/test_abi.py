@@ -62,7 +62,10 @@ def _decode(L, d, *, batch=2, hq=4, stride=8, max_len=100, split=0, ws=None, ws_
 def test_decode_args(L):
     d = desc()
     assert _decode(L, d, hq=3) == -1                       # not a multiple of H_kv
-    assert _decode(L, d, hq=32) == -2                      # G = 16 not built
+    assert _decode(L, d, hq=64) == -2                      # G = 32 not built
+    assert _decode(L, desc(d=64), hq=32) == -2             # G = 16: head_dim 128 only
+    assert "16 query heads" in err(L)
+    assert _decode(L, desc(dtype=0), hq=32) == -2          # G = 16: 16-bit queries only
     assert _decode(L, d, max_len=8 * 16 + 1) == -1         # beyond stride * P
     assert _decode(L, d, batch=-1) == -1
     assert _decode(L, d, split=24) == -1                   # not a multiple of P
@@ -98,6 +101,16 @@ def test_auto_plan(L, name, batch, hq, hkv, max_len, want_split):
     assert L.pkv_decode_plan(C.byref(d), batch, hq, max_len, 0, C.byref(n), C.byref(ws)) == 0
     assert n.value == want_split
     assert (ws.value == 0) == (n.value == 1)
+
+
+def test_plan_group_16(L):
+    """G = 16 plans on the matrix-core decode (head_dim 128, 16-bit queries)."""
+    n = C.c_int32()
+    ws = C.c_size_t()
+    assert L.pkv_decode_plan(C.byref(desc()), 8, 32, 131072, 0, C.byref(n), C.byref(ws)) == 0
+    assert n.value == 16
+    assert L.pkv_decode_plan(C.byref(desc(dtype=0)), 8, 32, 4096, 0, C.byref(n),
+                             C.byref(ws)) == -2
 
 
 def test_merge_args(L):

@@ -64,8 +64,9 @@ def test_decode_llama70b_128k_parity():
     ("f32", 64, 2, 2), ("f32", 128, 8, 1), ("f32", 64, 8, 1), ("f32", 128, 4, 2),
     ("f16", 64, 4, 2), ("f16", 128, 2, 1), ("f16", 64, 8, 1), ("f16", 128, 1, 1),
     ("bf16", 64, 16, 2), ("bf16", 128, 6, 3), ("bf16", 64, 1, 1), ("bf16", 128, 16, 16),
-    # G = 8 at head_dim 128: the matrix-core kernel
-    ("f16", 128, 16, 2), ("bf16", 128, 8, 1), ("bf16", 128, 32, 4),
+    # G = 8 and 16 at head_dim 128: the matrix-core kernel
+    ("f16", 128, 16, 2), ("bf16", 128, 8, 1), ("bf16", 128, 32, 4), ("f16", 128, 32, 2),
+    ("bf16", 128, 16, 1),
 ])
 def test_decode_shapes(dtype, d, hq, hkv):
     """Every (dtype, head_dim, group) kernel variant, ragged lengths spanning
@@ -97,11 +98,11 @@ def test_empty_context_rows():
 # --------------------------------------------------------------- indexing
 
 @pytest.mark.parametrize("dtype,group", [("f32", 4), ("f16", 4), ("bf16", 4), ("f16", 8),
-                                         ("bf16", 8)])
+                                         ("bf16", 8), ("f16", 16)])
 def test_one_hot_key_bit_exact(dtype, group):
     """K = 0 except the target token's key, whose score is >= 200: every other
     weight underflows to exactly 0, so the output is V[target] bit for bit.
-    Targets sweep page boundaries and the last token (G = 8: matrix cores)."""
+    Targets sweep page boundaries and the last token (G = 8, 16: matrix cores)."""
     L = 300
     targets = [0, 15, 16, 17, 31, 32, 150, 255, 256, 298, 299]
     w = W.make_decode("onehot", seed=5, batch=len(targets), hq=2 * group, hkv=2, d=128,
@@ -241,7 +242,7 @@ def test_merge_states_matches_oracle():
 
 # ------------------------------------------------ broken preconditions
 
-@pytest.mark.parametrize("hq", [8, 16])
+@pytest.mark.parametrize("hq", [8, 16, 32])
 def test_bad_page_id_and_length_poison_only_their_row(hq):
     w = W.make_decode("bad", seed=15, batch=4, hq=hq, hkv=2, d=128, dtype="bf16",
                       hist_lens=[300, 300, 300, 300], append=False, pool_slack=0.2)

@@ -121,7 +121,7 @@ def check_ex(w, split_tokens=0, window=0, sink=0, what=""):
 
 @pytest.mark.parametrize("fp8", FP8)
 @pytest.mark.parametrize("qd", ["f16", "bf16"])
-@pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 2), (8, 2), (16, 2)])
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 2), (8, 2), (16, 2), (32, 2)])
 def test_fp8_decode_shapes(fp8, qd, hq, hkv):
     """Every fp8 kernel variant (format x query type x group), ragged lengths
     with partial last pages, one split and several."""
@@ -154,7 +154,8 @@ WINDOWS = [(1, 0), (5, 0), (16, 0), (17, 3), (40, 17), (64, 16), (100, 1), (1000
 
 
 @pytest.mark.parametrize("dtype,d,hq,hkv", [("f32", 64, 4, 2), ("f16", 128, 16, 2),
-                                            ("bf16", 128, 8, 2), ("fp8_e4m3", 128, 8, 1)])
+                                            ("bf16", 128, 8, 2), ("fp8_e4m3", 128, 8, 1),
+                                            ("bf16", 128, 32, 2)])
 def test_window_decode(dtype, d, hq, hkv):
     """Window and sink sizes around page boundaries, windows wider than the
     context, one split and several."""
@@ -245,7 +246,7 @@ def oracle_mixed(w, rows=None):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (8, 2), (16, 2)])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (8, 2), (16, 2), (32, 2)])
 @pytest.mark.parametrize("split", [0, 64])
 def test_mixed_batch_all_rows(dtype, hq, hkv, split):
     """Decode rows (contexts from 1 key to several pages) before ragged

@@ -63,9 +63,9 @@ def test_prefill_config_sampled_rows():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (8, 2), (16, 2)])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (8, 2), (16, 2), (32, 2)])
 def test_prefill_shapes_all_rows(dtype, hq, hkv):
-    """Every row of ragged chunks over ragged histories, G = 1, 2, 4, 8."""
+    """Every row of ragged chunks over ragged histories, G = 1, 2, 4, 8, 16."""
     hist = [0, 1, 15, 100, 1000, 37]
     chunk = [1, 33, 128, 200, 5, 129]
     w = W.make_prefill("shape", seed=hq + hkv, batch=len(hist), hq=hq, hkv=hkv, d=128,

@@ -59,7 +59,7 @@ def scale_keys(w, factor, limit=None):
 
 @pytest.mark.parametrize("shape", ["ramp", "spikes"])
 @pytest.mark.parametrize("dtype,hq,hkv", [("bf16", 16, 2), ("f16", 16, 2), ("bf16", 8, 2),
-                                          ("f16", 8, 8)])
+                                          ("f16", 8, 8), ("bf16", 32, 2)])
 def test_prefill_growing_max(shape, dtype, hq, hkv):
     w = W.make_prefill("grow", seed=31 + hq + hkv, batch=3, hq=hq, hkv=hkv, d=128,
                        dtype=dtype, hist=[300, 1000, 1480], chunk=[40, 130, 64],
@@ -84,7 +84,7 @@ def test_prefill_growing_max(shape, dtype, hq, hkv):
 @pytest.mark.parametrize("split", [0, 64])
 @pytest.mark.parametrize("shape", ["ramp", "spikes"])
 @pytest.mark.parametrize("dtype,hq,hkv", [("bf16", 16, 2), ("f16", 16, 2), ("f16", 8, 2),
-                                          ("f32", 8, 2), ("bf16", 4, 4)])
+                                          ("f32", 8, 2), ("bf16", 4, 4), ("f16", 32, 2)])
 def test_decode_growing_max(split, shape, dtype, hq, hkv):
     w = W.make_decode("grow", seed=41 + hq, batch=3, hq=hq, hkv=hkv, d=128, dtype=dtype,
                       hist_lens=[333, 1000, 2000], append=False, pool_slack=0.1)
@@ -102,9 +102,9 @@ def test_decode_growing_max(split, shape, dtype, hq, hkv):
 
 
 @pytest.mark.parametrize("split", [0, 64])
-@pytest.mark.parametrize("hq", [16, 8])
+@pytest.mark.parametrize("hq", [32, 16, 8])
 def test_decode_fp8_growing_max(split, hq):
-    """fp8 (e4m3) keys growing fourfold along the sequence, G = 8 and 4."""
+    """fp8 (e4m3) keys growing fourfold along the sequence, G = 16, 8 and 4."""
     k_scale, v_scale = 0.0625, 0.03125
     w = W.make_decode("grow8", seed=51 + hq, batch=3, hq=hq, hkv=2, d=128, dtype="f16",
                       hist_lens=[333, 1000, 2000], append=False, pool_slack=0.1,
