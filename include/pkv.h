@@ -39,6 +39,13 @@
  *     buffers described by the arguments even when a precondition is broken;
  *     a decode or prefill row whose table entries or length are out of range
  *     is written as NaN.  pkv_validate_tables() checks host copies.
+ *   - Debugging: with the environment variable PKV_CHECK set (to anything but
+ *     "" or "0"; read at every call), each call that reads device tables
+ *     (slots, block table, lengths, q_indptr) first copies them to the host
+ *     on its stream, which synchronises the stream, and returns
+ *     PKV_ERR_INVALID with a "PKV_CHECK: ..." message instead of launching
+ *     when one of the preconditions above is broken.  A windowed decode
+ *     checks only the pages it reads.
  */
 #ifndef PKV_H
 #define PKV_H

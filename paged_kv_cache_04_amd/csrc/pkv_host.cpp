@@ -6,8 +6,11 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <string>
 #include <unordered_set>
+#include <vector>
 
 #include "pkv_internal.h"
 
@@ -90,6 +93,120 @@ int check_heads(const pkv_cache_desc* d, int32_t num_q_heads, int* group) {
 int hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
+}
+
+// ---- PKV_CHECK: device-table checks for debugging.  With the environment
+// variable PKV_CHECK set (to anything but "" or "0", read at every call), a
+// call that reads device tables first copies them to the host on its stream
+// (which synchronises the stream), checks the preconditions the kernels
+// otherwise only report as NaN rows, and returns PKV_ERR_INVALID with a
+// "PKV_CHECK: ..." message instead of launching when one is broken.
+
+bool check_mode() {
+  const char* e = std::getenv("PKV_CHECK");
+  return e && *e && std::strcmp(e, "0") != 0;
+}
+
+int fetch_i32(const int32_t* dev, int64_t n, std::vector<int32_t>* out, hipStream_t s) {
+  out->assign((size_t)(n > 0 ? n : 0), 0);
+  if (n <= 0) return PKV_OK;
+  hipError_t e = hipMemcpyAsync(out->data(), dev, (size_t)n * sizeof(int32_t),
+                                hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "PKV_CHECK copy: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+// Page ids of logical pages [first, last) of table row b.
+int check_pages(const pkv_cache_desc* d, const std::vector<int32_t>& bt, int32_t stride,
+                int32_t b, int64_t first, int64_t last, const char* what) {
+  for (int64_t i = first; i < last; ++i) {
+    const int32_t pg = bt[(size_t)((int64_t)b * stride + i)];
+    if (pg < 0 || pg >= d->num_pages)
+      return fail(PKV_ERR_INVALID, "PKV_CHECK: %s block_table[%d][%lld] = %d outside [0, %d)",
+                  what, b, (long long)i, pg, d->num_pages);
+  }
+  return PKV_OK;
+}
+
+// Decode: lengths within [0, max_len] and the pages the kernel reads valid
+// (with a window, only the sink's pages and the window's).
+int debug_check_decode(const pkv_cache_desc* d, const int32_t* block_table, int32_t stride,
+                       const int32_t* lens, int32_t batch, int32_t max_len, int32_t window,
+                       int32_t sink, hipStream_t s) {
+  std::vector<int32_t> bt, ln;
+  if (int rc = fetch_i32(lens, batch, &ln, s)) return rc;
+  if (int rc = fetch_i32(block_table, (int64_t)batch * stride, &bt, s)) return rc;
+  const int P = d->page_size;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t L = ln[(size_t)b];
+    if (L < 0 || L > max_len)
+      return fail(PKV_ERR_INVALID, "PKV_CHECK: decode context_lens[%d] = %lld outside [0, %d]",
+                  b, (long long)L, max_len);
+    const int64_t pages = (L + P - 1) / P;
+    if (window > 0 && L > window) {
+      const int64_t sink_pages = ((int64_t)(sink < L ? sink : L) + P - 1) / P;
+      if (int rc = check_pages(d, bt, stride, b, 0, sink_pages, "decode")) return rc;
+      if (int rc = check_pages(d, bt, stride, b, (L - window) / P, pages, "decode")) return rc;
+    } else if (int rc = check_pages(d, bt, stride, b, 0, pages, "decode")) {
+      return rc;
+    }
+  }
+  return PKV_OK;
+}
+
+// Chunked prefill over sequences [0, batch): q_indptr non-decreasing from >= 0
+// and ending <= total_rows, chunk lengths <= max_q_len and <= kv_lens <=
+// max_kv_len, the pages of every kv_len valid.  With num_decode > 0 the first
+// num_decode sequences must be one-row chunks at rows 0 .. num_decode-1.
+int debug_check_prefill(const pkv_cache_desc* d, const int32_t* q_indptr,
+                        const int32_t* block_table, int32_t stride, const int32_t* kv_lens,
+                        int32_t batch, int32_t total_rows, int32_t max_q_len,
+                        int32_t max_kv_len, int32_t num_decode, hipStream_t s) {
+  std::vector<int32_t> ip, bt, ln;
+  if (int rc = fetch_i32(q_indptr, (int64_t)batch + 1, &ip, s)) return rc;
+  if (int rc = fetch_i32(kv_lens, batch, &ln, s)) return rc;
+  if (int rc = fetch_i32(block_table, (int64_t)batch * stride, &bt, s)) return rc;
+  const int P = d->page_size;
+  if (ip[0] < 0) return fail(PKV_ERR_INVALID, "PKV_CHECK: q_indptr[0] = %d < 0", ip[0]);
+  if (ip[(size_t)batch] > total_rows)
+    return fail(PKV_ERR_INVALID, "PKV_CHECK: q_indptr[%d] = %d > total_q_rows %d", batch,
+                ip[(size_t)batch], total_rows);
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t C = (int64_t)ip[(size_t)b + 1] - ip[(size_t)b];
+    const int64_t L = ln[(size_t)b];
+    if (b < num_decode && (ip[(size_t)b] != b || C != 1))
+      return fail(PKV_ERR_INVALID,
+                  "PKV_CHECK: decode row %d: q_indptr[%d..%d] = %d..%d, want %d..%d", b, b,
+                  b + 1, ip[(size_t)b], ip[(size_t)b + 1], b, b + 1);
+    if (b >= num_decode && (C < 0 || C > max_q_len))
+      return fail(PKV_ERR_INVALID, "PKV_CHECK: chunk %d has %lld rows, outside [0, %d]", b,
+                  (long long)C, max_q_len);
+    if (L < C || L > max_kv_len)
+      return fail(PKV_ERR_INVALID, "PKV_CHECK: kv_lens[%d] = %lld outside [%lld, %d]", b,
+                  (long long)L, (long long)C, max_kv_len);
+    if (int rc = check_pages(d, bt, stride, b, 0, (L + P - 1) / P, "prefill")) return rc;
+  }
+  return PKV_OK;
+}
+
+// Append: slots below num_pages * page_size, each used once (negative: skip).
+int debug_check_slots(const pkv_cache_desc* d, const int32_t* slots, int32_t n, hipStream_t s) {
+  std::vector<int32_t> sl;
+  if (int rc = fetch_i32(slots, n, &sl, s)) return rc;
+  const int64_t total = (int64_t)d->num_pages * d->page_size;
+  std::unordered_set<int32_t> seen;
+  seen.reserve((size_t)n * 2);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t v = sl[(size_t)i];
+    if (v < 0) continue;
+    if (v >= total)
+      return fail(PKV_ERR_INVALID, "PKV_CHECK: slot[%d] = %d >= num_pages * page_size = %lld",
+                  i, v, (long long)total);
+    if (!seen.insert(v).second)
+      return fail(PKV_ERR_INVALID, "PKV_CHECK: slot %d repeats (index %d)", v, i);
+  }
+  return PKV_OK;
 }
 
 // Decode split plan.  Auto rule: aim for about 512 workgroups (two per CU
@@ -268,6 +385,11 @@ int decode_impl(const pkv_cache_desc* desc, const void* k_cache, const void* v_c
     return rc;
   if (batch == 0) return ok();
   if (!out) return fail(PKV_ERR_INVALID, "out is NULL");
+  if (check_mode())
+    if (int rc = debug_check_decode(desc, block_table, block_table_stride, context_lens, batch,
+                                    max_context_len, dc.opts.window, dc.opts.sink,
+                                    (hipStream_t)stream))
+      return rc;
   pkv::DecodeArgs a = decode_args(desc, k_cache, v_cache, q, num_q_heads, block_table,
                                   block_table_stride, context_lens, scale, dc);
   hipStream_t s = (hipStream_t)stream;
@@ -312,6 +434,11 @@ int partials_impl(const pkv_cache_desc* desc, const void* k_cache, const void* v
     return fail(PKV_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes,
                 dc.plan.ws_bytes);
   if (!aligned16(workspace)) return fail(PKV_ERR_INVALID, "workspace must be 16-byte aligned");
+  if (check_mode())
+    if (int rc = debug_check_decode(desc, block_table, block_table_stride, context_lens, batch,
+                                    max_context_len, dc.opts.window, dc.opts.sink,
+                                    (hipStream_t)stream))
+      return rc;
   pkv::DecodeArgs a = decode_args(desc, k_cache, v_cache, q, num_q_heads, block_table,
                                   block_table_stride, context_lens, scale, dc);
   a.direct = 0;
@@ -362,6 +489,8 @@ int pkv_kv_append(const pkv_cache_desc* desc, void* k_cache, void* v_cache, cons
     return fail(PKV_ERR_INVALID, "NULL pointer");
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
     return fail(PKV_ERR_INVALID, "cache and new-token buffers must be 16-byte aligned");
+  if (check_mode())
+    if (int rc = debug_check_slots(desc, slot_mapping, n_tokens, (hipStream_t)stream)) return rc;
   return hip_status(pkv::launch_kv_append(desc->dtype, desc->head_dim, desc->num_kv_heads,
                                           desc->num_pages, k_cache, v_cache, k_new, v_new,
                                           slot_mapping, n_tokens, (hipStream_t)stream),
@@ -378,6 +507,12 @@ int pkv_gather_kv(const pkv_cache_desc* desc, const void* k_cache, const void* v
     return fail(PKV_ERR_INVALID, "NULL pointer");
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_out) || !aligned16(v_out))
     return fail(PKV_ERR_INVALID, "buffers must be 16-byte aligned");
+  if (check_mode()) {
+    std::vector<int32_t> row;
+    const int64_t pages = ((int64_t)len + desc->page_size - 1) / desc->page_size;
+    if (int rc = fetch_i32(table_row, pages, &row, (hipStream_t)stream)) return rc;
+    if (int rc = check_pages(desc, row, (int32_t)pages, 0, 0, pages, "gather")) return rc;
+  }
   return hip_status(pkv::launch_gather(desc->dtype, desc->head_dim, desc->num_kv_heads,
                                        desc->num_pages, k_cache, v_cache, table_row, len, k_out,
                                        v_out, (hipStream_t)stream),
@@ -460,6 +595,8 @@ int pkv_kv_append_quant(const pkv_cache_desc* desc, void* k_cache, void* v_cache
     return fail(PKV_ERR_INVALID, "NULL pointer");
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
     return fail(PKV_ERR_INVALID, "cache and new-token buffers must be 16-byte aligned");
+  if (check_mode())
+    if (int rc = debug_check_slots(desc, slot_mapping, n_tokens, (hipStream_t)stream)) return rc;
   return hip_status(pkv::launch_kv_append_quant(desc->dtype, src_dtype, desc->head_dim,
                                                 desc->num_kv_heads, desc->num_pages, k_cache,
                                                 v_cache, k_new, v_new, k_scale, v_scale,
@@ -565,6 +702,11 @@ int pkv_paged_attn_prefill_chunk(const pkv_cache_desc* desc, const void* k_cache
     return fail(PKV_ERR_INVALID, "NULL pointer");
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q) || !aligned16(out))
     return fail(PKV_ERR_INVALID, "k_cache, v_cache, q and out must be 16-byte aligned");
+  if (check_mode())
+    if (int rc = debug_check_prefill(desc, q_indptr, block_table, block_table_stride, kv_lens,
+                                     batch, total_q_rows, max_q_len, max_kv_len, 0,
+                                     (hipStream_t)stream))
+      return rc;
   return prefill_launch(desc, group, k_cache, v_cache, q, q_indptr, batch, num_q_heads,
                         total_q_rows, max_q_len, block_table, block_table_stride, kv_lens,
                         scale, out, lse_out, (hipStream_t)stream);
@@ -592,6 +734,11 @@ int pkv_paged_attn_mixed(const pkv_cache_desc* desc, const void* k_cache, const 
   const int32_t n_chunk = batch - num_decode;
   if (n_chunk > 0 && max_q_len == 0)
     return fail(PKV_ERR_INVALID, "max_q_len 0 with %d chunk sequences", n_chunk);
+  if (check_mode())
+    if (int rc = debug_check_prefill(desc, q_indptr, block_table, block_table_stride, kv_lens,
+                                     batch, total_q_rows, max_q_len, max_kv_len, num_decode,
+                                     (hipStream_t)stream))
+      return rc;
   if (num_decode > 0) {
     // decode rows: q rows and out rows 0 .. num_decode-1, i.e. [num_decode][H_q][D]
     if (int rc = decode_impl(desc, k_cache, v_cache, q, num_decode, num_q_heads, block_table,

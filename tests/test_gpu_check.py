@@ -1,0 +1,158 @@
+"""PKV_CHECK: the debugging mode that checks device tables on the host before
+a launch.  Valid inputs give bit-identical results with and without it;
+each broken precondition becomes a PkvError naming the bad entry, raised
+before anything is launched."""
+import pytest
+import torch
+
+import paged_kv_cache_04_amd as pkv
+from paged_kv_cache_04_amd import workloads as W
+from paged_kv_cache_04_amd.binding import PkvError
+
+from helpers import bits, to_dev
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture
+def check_on(monkeypatch):
+    monkeypatch.setenv("PKV_CHECK", "1")
+
+
+def decode(w, d, split=64, **kw):
+    out, lse = pkv.paged_attn_decode(d["q"], d["k_cache"], d["v_cache"], d["block_table"],
+                                     d["context_lens"], w.max_context_len, w.scale,
+                                     split_tokens=split, return_lse=True, **kw)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def prefill(w, d):
+    out, lse = pkv.paged_attn_prefill_chunk(d["q"], d["k_cache"], d["v_cache"], d["q_indptr"],
+                                            d["block_table"], d["context_lens"],
+                                            max(w.meta["chunk_lens"]), w.max_context_len,
+                                            w.scale, return_lse=True)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def test_valid_inputs_same_bits(monkeypatch):
+    wd = W.make_decode("ck", seed=61, batch=3, hq=16, hkv=2, d=128, dtype="bf16",
+                       hist_lens=[40, 333, 1000], append=True, pool_slack=0.2)
+    wp = W.make_prefill("ckp", seed=62, batch=2, hq=8, hkv=2, d=128, dtype="f16",
+                        hist=[100, 0], chunk=[50, 70], pool_slack=0.2)
+    results = []
+    for mode in ("0", "1"):
+        monkeypatch.setenv("PKV_CHECK", mode)
+        dd, dp = to_dev(wd, DEV), to_dev(wp, DEV)
+        pkv.kv_append(dd["k_cache"], dd["v_cache"], dd["k_new"], dd["v_new"], dd["slots"])
+        pkv.kv_append(dp["k_cache"], dp["v_cache"], dp["k_new"], dp["v_new"], dp["slots"])
+        o1, l1 = decode(wd, dd)
+        o2, l2 = decode(wd, dd, split=0)
+        o3, l3 = prefill(wp, dp)
+        kg, vg = pkv.gather_kv(dd["k_cache"], dd["v_cache"], dd["block_table"][2], 1001)
+        torch.cuda.synchronize()
+        results.append([bits(x) for x in (o1, l1, o2, l2, o3, l3, kg, vg)])
+    for a, b in zip(*results):
+        assert torch.equal(a, b)
+
+
+def test_decode_bad_page(check_on):
+    w = W.make_decode("ck", seed=63, batch=3, hq=8, hkv=2, d=128, dtype="bf16",
+                      hist_lens=[100, 300, 200], append=False, pool_slack=0.2)
+    w.block_table[1, 3] = w.num_pages + 5
+    d = to_dev(w, DEV)
+    with pytest.raises(PkvError, match=r"PKV_CHECK: decode block_table\[1\]\[3\]"):
+        decode(w, d)
+    with pytest.raises(PkvError, match="PKV_CHECK"):
+        decode(w, d, split=0)
+
+
+def test_decode_length_over_bound(check_on):
+    w = W.make_decode("ck", seed=64, batch=2, hq=8, hkv=2, d=128, dtype="bf16",
+                      hist_lens=[100, 300], append=False, pool_slack=0.5)
+    d = to_dev(w, DEV)
+    with pytest.raises(PkvError, match=r"context_lens\[1\] = 300 outside \[0, 299\]"):
+        pkv.paged_attn_decode(d["q"], d["k_cache"], d["v_cache"], d["block_table"],
+                              d["context_lens"], 299, w.scale)
+
+
+def test_window_checks_only_read_pages(monkeypatch):
+    """A sliding-window server may drop the pages between the sink and the
+    window: with their table entries set to -1 the check passes and the
+    result is that of the intact table."""
+    w = W.make_decode("ckw", seed=65, batch=2, hq=16, hkv=2, d=128, dtype="f16",
+                      hist_lens=[1000, 700], append=False, pool_slack=0.2)
+    d = to_dev(w, DEV)
+    ref, ref_lse = decode(w, d, window=200, sink=20)
+    bt = d["block_table"].clone()
+    bt[0, 2:50] = -1        # keys 32 .. 799: neither sink (< 20) nor window (>= 800)
+    bt[1, 2:31] = -1        # keys 32 .. 495: window starts at 500
+    d2 = dict(d, block_table=bt)
+    monkeypatch.setenv("PKV_CHECK", "1")
+    out, lse = decode(w, d2, window=200, sink=20)
+    assert torch.equal(bits(out), bits(ref)) and torch.equal(bits(lse), bits(ref_lse))
+    bt[0, 50] = -1          # keys 800 .. 815: the window's first page
+    with pytest.raises(PkvError, match=r"block_table\[0\]\[50\]"):
+        decode(w, dict(d, block_table=bt), window=200, sink=20)
+
+
+def test_append_bad_slots(check_on):
+    w = W.make_decode("cka", seed=66, batch=2, hq=8, hkv=2, d=128, dtype="bf16",
+                      hist_lens=[10, 20], append=True, pool_slack=0.2)
+    d = to_dev(w, DEV)
+    before = bits(d["k_cache"]).clone()
+    dup = d["slots"].clone()
+    dup[1] = dup[0]
+    with pytest.raises(PkvError, match="repeats"):
+        pkv.kv_append(d["k_cache"], d["v_cache"], d["k_new"], d["v_new"], dup)
+    big = d["slots"].clone()
+    big[0] = w.num_pages * w.page_size
+    with pytest.raises(PkvError, match=r"slot\[0\]"):
+        pkv.kv_append(d["k_cache"], d["v_cache"], d["k_new"], d["v_new"], big)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(d["k_cache"]), before)     # nothing was launched
+
+
+def test_prefill_bad_tables(check_on):
+    w = W.make_prefill("ckp", seed=67, batch=2, hq=8, hkv=2, d=128, dtype="bf16",
+                       hist=[100, 30], chunk=[50, 20], pool_slack=0.2)
+    d = to_dev(w, DEV)
+    pkv.kv_append(d["k_cache"], d["v_cache"], d["k_new"], d["v_new"], d["slots"])
+    short = d["context_lens"].clone()
+    short[1] = 10                                      # fewer keys than chunk rows
+    with pytest.raises(PkvError, match=r"kv_lens\[1\] = 10 outside \[20, "):
+        prefill(w, dict(d, context_lens=short))
+    bt = d["block_table"].clone()
+    bt[0, 9] = -1                                      # keys 144 .. 149 of sequence 0
+    with pytest.raises(PkvError, match=r"prefill block_table\[0\]\[9\]"):
+        prefill(w, dict(d, block_table=bt))
+
+
+def test_mixed_decode_rows_are_one_row(check_on):
+    w = W.make_mixed("ckm", seed=68, hq=16, hkv=2, d=128, dtype="f16", decode_hist=[10, 40],
+                     chunk_hist=[0, 64], chunk=[7, 30], pool_slack=0.2)
+    d = to_dev(w, DEV)
+    pkv.kv_append(d["k_cache"], d["v_cache"], d["k_new"], d["v_new"], d["slots"])
+    nd = w.meta["num_decode"]
+    out = pkv.paged_attn_mixed(d["q"], d["k_cache"], d["v_cache"], d["q_indptr"],
+                               d["block_table"], d["context_lens"], nd, 30,
+                               w.max_context_len, w.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    # claim three decode rows: sequence 2 is a 7-row chunk
+    with pytest.raises(PkvError, match="PKV_CHECK: decode row 2"):
+        pkv.paged_attn_mixed(d["q"], d["k_cache"], d["v_cache"], d["q_indptr"],
+                             d["block_table"], d["context_lens"], nd + 1, 30,
+                             w.max_context_len, w.scale)
+
+
+def test_gather_bad_page(check_on):
+    w = W.make_decode("ckg", seed=69, batch=1, hq=4, hkv=2, d=64, dtype="f32",
+                      hist_lens=[100], append=False, pool_slack=0.2)
+    d = to_dev(w, DEV)
+    row = d["block_table"][0].clone()
+    row[6] = -3
+    with pytest.raises(PkvError, match=r"gather block_table\[0\]\[6\]"):
+        pkv.gather_kv(d["k_cache"], d["v_cache"], row, 100)
