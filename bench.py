@@ -320,6 +320,27 @@ def _back_to_back_us(fn, n):
     return e0.elapsed_time(e1) * 1e3 / n
 
 
+def _cold_event_us(fn, n, scratch_bytes=1 << 30):
+    """Mean microseconds of fn() bracketed by HIP events, each call preceded
+    (untimed) by a read of a 1 GiB scratch buffer on the same stream, which
+    evicts L2 and the 256 MB Infinity Cache and leaves them holding clean
+    lines (a write would leave dirty ones to be written back during fn)."""
+    import torch
+    scratch = torch.ones(scratch_bytes // 4, dtype=torch.float32, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    fn()
+    for i, (e0, e1) in enumerate(ev):
+        scratch.sum()
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    us = [e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]
+    del scratch
+    return sum(us) / len(us)
+
+
 def _event_times(fn, n, warmup=3):
     """Mean and median microseconds of fn() bracketed by HIP events on the
     current stream (the stream the library enqueues on)."""
@@ -499,6 +520,7 @@ def bench_window(args, dev, sample, reuse=None):
     step_us, _ = _event_times(step, 30, warmup=10)
     _, part_med = _event_times(c_part, 30)
     part_us = _back_to_back_us(c_part, 30)
+    cold_us = _cold_event_us(c_part, 20)
     es = 4 if w.dtype == "f32" else 2
     vis = [min(L, window) + min(sink, max(0, L - window)) for L in w.context_lens.tolist()]
     kv_bytes = sum(vis) * 2 * w.num_kv_heads * w.head_dim * es
@@ -509,7 +531,11 @@ def bench_window(args, dev, sample, reuse=None):
            "ms_per_step": round(step_us / 1e3, 5), "n_split": n_split,
            "kernel_median_us": round(part_med, 2),
            "roofline": _hbm_roofline("decode_mfma_kernel (windowed split-KV partials)", kv_bytes,
-                                     part_us)}
+                                     part_us),
+           # the visible K/V (35 MB) fits in the 256 MB Infinity Cache: the same kernel with
+           # L2 and that cache evicted before each launch (its own event pair per launch)
+           "cold_cache": {"kernel_us": round(cold_us, 2),
+                          "achieved_gbps": round(kv_bytes / (cold_us * 1e-6) / 1e9, 1)}}
     if sample:
         from oracle import pkvref
         rows = [b * w.num_q_heads + h for b in range(w.batch) for h in (0, 15)]
