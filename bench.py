@@ -7,7 +7,10 @@ is Llama-3-70B's per-GPU head share at 128K context: batch 8, 16 query / 2 KV
 heads, head_dim 128, fp16 K/V in 16-token pages, 131072 keys per sequence.
 
 Prints one JSON line.  `value` is decode tokens/s (batch / step time) with
-every input resident in HBM before the timed region.  `roofline` reports the
+every input resident in HBM before the timed region.  Steps are eager
+launches; with --graph the step's calls are captured once in a HIP graph and
+the timed steps are graph replays (on this stack no faster: the graph
+launches each kernel node at about the cost of an eager launch).  `roofline` reports the
 partial-decode kernel: algorithmic KV bytes per launch over its mean launch
 time measured with HIP events on the stream it runs on.  `cpu_baseline` is
 the CPU oracle timed on this host's cores on a bounded sample of the same
@@ -90,6 +93,8 @@ def parse():
                     help="comma-separated extra rows to measure: prefill, fp8, window, mixed "
                          "('' or 'none' for none)")
     ap.add_argument("--prefill", action="store_true", help="same as --extras prefill")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the steps as HIP graph replays instead of eager launches")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain copy of this many MiB first (counter calibration)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -179,7 +184,18 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = t_begin.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
+    eager_ms_per_step = total_ms / args.steps
+    ms_per_step = eager_ms_per_step
+    if args.graph:
+        # the same three calls per step, replayed as one HIP graph: no launch gaps
+        def issue_step():
+            if has_append:
+                pkv.binding.prepare_kv_append(kc, vc, k_new, v_new, slots)()
+            pkv.binding.prepare_decode_partials(*dargs, args.split_tokens, workspace)()
+            pkv.binding.prepare_merge_states(o_parts, l_parts, out, lse)()
+        t0 = time.perf_counter()
+        ms_per_step = _graph_us(issue_step, args.steps, args.warmup) / 1e3
+        wall = time.perf_counter() - t0
     kern_us = [e0.elapsed_time(e1) * 1e3 for e0, e1 in events]
     step_kern_us = float(np.mean(kern_us))
     # the kernel's own duration: back-to-back launches between one event pair
@@ -241,6 +257,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "step_launch": "hip graph" if args.graph else "eager",
+        "eager_ms_per_step": round(eager_ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -285,10 +303,11 @@ def main():
 
 def _decode_kernel_name(w) -> str:
     """The decode kernel the library runs for this workload: the matrix-core
-    kernel for 8 query heads per KV head (fp8 pools from 4), else the vector
-    kernel."""
+    kernel for 8 or 16 query heads per KV head (fp8 pools from 4), else the
+    vector kernel."""
     g = w.num_q_heads // w.num_kv_heads
-    mfma = w.head_dim == 128 and w.dtype in ("f16", "bf16") and (g == 8 or (w.is_fp8 and g == 4))
+    mfma = (w.head_dim == 128 and w.dtype in ("f16", "bf16")
+            and (g in (8, 16) or (w.is_fp8 and g == 4)))
     return "decode_mfma_kernel" if mfma else "decode_kernel"
 
 
@@ -315,6 +334,27 @@ def _back_to_back_us(fn, n):
     e0.record()
     for _ in range(n):
         fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
+def _graph_us(issue, n, warmup=5):
+    """Mean microseconds per replay of a HIP graph that holds one issue() --
+    the step's library calls, prepared and made on torch's capture stream --
+    over n back-to-back replays between one event pair."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        issue()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        g.replay()
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / n
@@ -457,7 +497,15 @@ def bench_fp8(args, dev, sample):
         c_part()
         c_merge()
 
-    step_us, _ = _event_times(step, 30, warmup=10)
+    def issue_step():
+        pkv.binding.prepare_kv_append_quant(kc, vc, k_new, v_new, slots, w.k_scale,
+                                            w.v_scale)()
+        pkv.binding.prepare_decode_partials(q, kc, vc, bt, cl, w.max_context_len, w.scale, 0, ws,
+                                            w.k_scale, w.v_scale)()
+        pkv.binding.prepare_merge_states(o_parts, l_parts, out)()
+
+    eager_us, _ = _event_times(step, 30, warmup=10)
+    step_us = _graph_us(issue_step, 30) if args.graph else eager_us
     _, part_med = _event_times(c_part, 30)
     part_us = _back_to_back_us(c_part, 30)
     kv_bytes = sum(w.context_lens.tolist()) * 2 * w.num_kv_heads * w.head_dim * 1
@@ -465,7 +513,8 @@ def bench_fp8(args, dev, sample):
                        "scales: batch 8, 16 q / 2 kv heads, head_dim 128, f16 queries, page 16, "
                        "131072 keys per sequence (131071 stored + 1 quantized on append)",
            "tokens_per_s": round(w.batch / (step_us * 1e-6), 1), "ms_per_step": round(
-               step_us / 1e3, 5), "n_split": n_split, "kernel_median_us": round(part_med, 2),
+               step_us / 1e3, 5), "eager_ms_per_step": round(eager_us / 1e3, 5),
+           "n_split": n_split, "kernel_median_us": round(part_med, 2),
            "roofline": _hbm_roofline("decode_mfma_kernel<f16 q, fp8 e4m3 cache> (split-KV partials)",
                                      kv_bytes, part_us)}
     if sample:
@@ -517,7 +566,13 @@ def bench_window(args, dev, sample, reuse=None):
         c_part()
         c_merge()
 
-    step_us, _ = _event_times(step, 30, warmup=10)
+    def issue_step():
+        pkv.binding.prepare_decode_partials(q, kc, vc, bt, cl, w.max_context_len, w.scale, 0, ws,
+                                            window=window, sink=sink)()
+        pkv.binding.prepare_merge_states(o_parts, l_parts, out)()
+
+    eager_us, _ = _event_times(step, 30, warmup=10)
+    step_us = _graph_us(issue_step, 30) if args.graph else eager_us
     _, part_med = _event_times(c_part, 30)
     part_us = _back_to_back_us(c_part, 30)
     cold_us = _cold_event_us(c_part, 20)
@@ -528,7 +583,8 @@ def bench_window(args, dev, sample, reuse=None):
                        "4096 most recent keys and the first 128 (page 4, section 2.3's local "
                        "window + global tokens); pages wholly outside are not read",
            "tokens_per_s": round(w.batch / (step_us * 1e-6), 1),
-           "ms_per_step": round(step_us / 1e3, 5), "n_split": n_split,
+           "ms_per_step": round(step_us / 1e3, 5), "eager_ms_per_step": round(eager_us / 1e3, 5),
+           "n_split": n_split,
            "kernel_median_us": round(part_med, 2),
            "roofline": _hbm_roofline("decode_mfma_kernel (windowed split-KV partials)", kv_bytes,
                                      part_us),
@@ -570,7 +626,8 @@ def bench_mixed(args, dev, sample):
         pkv.paged_attn_mixed(q, kc, vc, qi, bt, kl, nd, max_q, w.max_context_len, w.scale,
                              out=out, workspace=ws)
 
-    us, us_med = _event_times(run, 10)
+    eager_us, us_med = _event_times(run, 10)
+    us = _graph_us(run, 10) if args.graph else eager_us
     # the chunk part alone (the MFMA kernel) and the decode part alone
     qi_c, bt_c, kl_c = qi[nd:].contiguous(), bt[nd:].contiguous(), kl[nd:].contiguous()
     pf_us, _ = _event_times(lambda: pkv.paged_attn_prefill_chunk(
@@ -585,7 +642,7 @@ def bench_mixed(args, dev, sample):
                        "decoding at 8K..128K keys + two 4093-row prompt chunks (history 0 and "
                        "65536), 16 q / 2 kv heads, head_dim 128, f16, decode rows first",
            "query_tokens": int(sum(chunk)), "call_avg_us": round(us, 2),
-           "call_median_us": round(us_med, 2),
+           "eager_call_avg_us": round(eager_us, 2), "eager_call_median_us": round(us_med, 2),
            "query_tokens_per_s": round(sum(chunk) / (us * 1e-6), 1),
            "roofline": _mfma_roofline("prefill_kernel (the batch's chunks)", flops, pf_us, "f16"),
            "decode_rows": _hbm_roofline("decode_mfma_kernel + merge (the batch's decode rows)",
