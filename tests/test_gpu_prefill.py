@@ -73,6 +73,19 @@ def test_prefill_shapes_all_rows(dtype, hq, hkv):
     check_prefill(w, what=f"{dtype} G{hq // hkv}")
 
 
+@pytest.mark.parametrize("dtype,hq,hkv", [("bf16", 8, 8), ("f16", 8, 4), ("bf16", 32, 2)])
+def test_prefill_workgroup_and_tile_boundaries(dtype, hq, hkv):
+    """A workgroup holds 256 / G chunk positions and keys go in 64-key tiles:
+    chunks one below, at and one above multiples of 256 / G, over histories
+    one below, at and one above multiples of 64, every row."""
+    npos = 256 // (hq // hkv)
+    chunk = [npos - 1, npos, npos + 1, 2 * npos + 1]
+    hist = [63, 64, 65, 127]
+    w = W.make_prefill("edge", seed=hq * 7 + hkv, batch=4, hq=hq, hkv=hkv, d=128, dtype=dtype,
+                       hist=hist, chunk=chunk, pool_slack=0.2)
+    check_prefill(w, what=f"{dtype} G{hq // hkv} edges")
+
+
 def test_prefill_one_row_chunk_matches_decode():
     """A chunk of one row is a decode step: same oracle, both GPU paths."""
     w = W.make_prefill("one", seed=21, batch=3, hq=16, hkv=2, d=128, dtype="f16",
