@@ -618,13 +618,17 @@ def bench_mixed(args, dev, sample):
     nd = w.meta["num_decode"]
     chunk = w.meta["chunk_lens"]
     max_q = max(chunk[nd:])
-    _, ws_bytes = pkv.decode_plan(pkv.cache_desc(kc), nd, w.num_q_heads, w.max_context_len)
+    # the scheduler knows the decode rows' lengths: split them by the batch's pages
+    split = pkv.decode_split_for_lens(pkv.cache_desc(kc), w.num_q_heads,
+                                      w.context_lens[:nd].tolist())
+    _, ws_bytes = pkv.decode_plan(pkv.cache_desc(kc), nd, w.num_q_heads, w.max_context_len,
+                                  split)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
 
     def run():
         pkv.paged_attn_mixed(q, kc, vc, qi, bt, kl, nd, max_q, w.max_context_len, w.scale,
-                             out=out, workspace=ws)
+                             split_tokens=split, out=out, workspace=ws)
 
     eager_us, us_med = _event_times(run, 10)
     us = _graph_us(run, 10) if args.graph else eager_us
@@ -632,16 +636,28 @@ def bench_mixed(args, dev, sample):
     qi_c, bt_c, kl_c = qi[nd:].contiguous(), bt[nd:].contiguous(), kl[nd:].contiguous()
     pf_us, _ = _event_times(lambda: pkv.paged_attn_prefill_chunk(
         q, kc, vc, qi_c, bt_c, kl_c, max_q, w.max_context_len, w.scale, out=out), 10)
-    dec_us, _ = _event_times(lambda: pkv.paged_attn_decode(
-        q[:nd], kc, vc, bt[:nd].contiguous(), kl[:nd].contiguous(), w.max_context_len, w.scale,
-        out=out[:nd], workspace=ws), 10)
+    # the decode part alone: its two kernels, prepared and launched back to back
+    q_d, bt_d, kl_d = q[:nd].contiguous(), bt[:nd].contiguous(), kl[:nd].contiguous()
+    o_d = torch.empty_like(q_d)
+    o_parts, l_parts, _ = pkv.paged_attn_decode_partials(
+        q_d, kc, vc, bt_d, kl_d, w.max_context_len, w.scale, split_tokens=split, workspace=ws)
+    c_part = pkv.binding.prepare_decode_partials(q_d, kc, vc, bt_d, kl_d, w.max_context_len,
+                                                 w.scale, split, ws)
+    c_merge = pkv.binding.prepare_merge_states(o_parts, l_parts, o_d)
+
+    def dec():
+        c_part()
+        c_merge()
+
+    dec_us = _back_to_back_us(dec, 20)
     lens = w.context_lens.tolist()
     flops = A.prefill_flops(lens[nd:], chunk[nd:], w.num_q_heads, w.head_dim)
     dec_bytes = A.decode_kv_bytes(lens[:nd], w.num_kv_heads, w.head_dim, w.dtype)
     res = {"workload": "one chunked-prefill batch under page 1's 8192-token budget: 6 sequences "
                        "decoding at 8K..128K keys + two 4093-row prompt chunks (history 0 and "
                        "65536), 16 q / 2 kv heads, head_dim 128, f16, decode rows first",
-           "query_tokens": int(sum(chunk)), "call_avg_us": round(us, 2),
+           "query_tokens": int(sum(chunk)), "decode_split_tokens": split,
+           "call_avg_us": round(us, 2),
            "eager_call_avg_us": round(eager_us, 2), "eager_call_median_us": round(us_med, 2),
            "query_tokens_per_s": round(sum(chunk) / (us * 1e-6), 1),
            "roofline": _mfma_roofline("prefill_kernel (the batch's chunks)", flops, pf_us, "f16"),

@@ -20,7 +20,8 @@
  * Conventions for every entry point:
  *   - Pointers named "device" are HIP device pointers; "host" ones are CPU
  *     memory.  The caller owns every buffer.  The library allocates no device
- *     memory, keeps no pointer after returning, and never synchronises.
+ *     memory, keeps no pointer after returning, and never synchronises
+ *     (outside the PKV_CHECK debug mode below).
  *   - stream: a hipStream_t passed as void*; NULL is the null stream.  All
  *     device work is enqueued on it asynchronously.
  *   - Base pointers of device buffers must be 16-byte aligned.
@@ -221,6 +222,30 @@ int pkv_paged_attn_decode_partials(const pkv_cache_desc* desc, const void* k_cac
 int pkv_decode_plan_ex(const pkv_cache_desc* desc, int32_t batch, int32_t num_q_heads,
                        int32_t max_context_len, int32_t split_tokens,
                        const pkv_decode_opts* opts, int32_t* n_split, size_t* workspace_bytes);
+
+/*
+ * decode_split_for_lens -- a split size for a batch whose lengths the caller
+ * holds on the host, as a batching scheduler does (page 2, section 4.2:
+ * continuous batching mixes requests of every length).  decode_plan's
+ * automatic rule sizes every sequence by max_context_len, one or two
+ * workgroups per CU; with unequal lengths those workgroups end at different
+ * times and leave CUs idle.  This rule counts the pages the batch actually
+ * visits (lens_host[b] keys of sequence b, window-aware under opts): when
+ * every sequence visits as many pages it returns the automatic split;
+ * otherwise a split that spreads them over about 1024 workgroups (four per
+ * CU, balanced by the hardware), with at least 32 pages per split, adjusted
+ * so that the decode runs an odd number of splits when its max_context_len is
+ * the largest length (the XCDs then share the short sequences' work evenly).
+ *   lens_host    : host int32 [batch], the lengths the decode will see
+ *   opts         : as for decode_plan_ex (may be NULL)
+ *   split_tokens : out, a multiple of P, to pass to decode_plan(_ex) and to
+ *                  the decode calls
+ * Host-only; no HIP call.  Errors: as decode_plan_ex, plus a negative length
+ * or a NULL pointer (PKV_ERR_INVALID).
+ */
+int pkv_decode_split_for_lens(const pkv_cache_desc* desc, int32_t batch, int32_t num_q_heads,
+                              const int32_t* lens_host, const pkv_decode_opts* opts,
+                              int32_t* split_tokens);
 
 int pkv_paged_attn_decode_ex(const pkv_cache_desc* desc, const void* k_cache,
                              const void* v_cache, const void* q, int32_t batch,

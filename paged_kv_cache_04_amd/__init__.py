@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     cache_desc,
     decode_opts,
     decode_plan,
+    decode_split_for_lens,
     gather_kv,
     kv_append,
     kv_append_quant,

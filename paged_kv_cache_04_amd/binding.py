@@ -78,12 +78,13 @@ def lib():
         L.pkv_kv_append_quant.argtypes = [dp, vp, vp, vp, vp, i32, f32, f32, vp, i32, vp]
         L.pkv_paged_attn_mixed.argtypes = [dp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32,
                                            vp, i32, f32, i32, vp, vp, vp, sz, vp]
+        L.pkv_decode_split_for_lens.argtypes = [dp, i32, i32, vp, op, C.POINTER(i32)]
         for name in ("pkv_kv_append", "pkv_gather_kv", "pkv_decode_plan", "pkv_paged_attn_decode",
                      "pkv_paged_attn_decode_partials", "pkv_merge_states",
                      "pkv_paged_attn_prefill_chunk", "pkv_validate_tables",
                      "pkv_decode_plan_ex", "pkv_paged_attn_decode_ex",
                      "pkv_paged_attn_decode_partials_ex", "pkv_kv_append_quant",
-                     "pkv_paged_attn_mixed"):
+                     "pkv_paged_attn_mixed", "pkv_decode_split_for_lens"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -205,6 +206,19 @@ def decode_plan(desc: CacheDesc, batch: int, num_q_heads: int, max_context_len: 
                                         int(max_context_len), int(split_tokens), C.byref(opts),
                                         C.byref(n), C.byref(ws)))
     return int(n.value), int(ws.value)
+
+
+def decode_split_for_lens(desc: CacheDesc, num_q_heads: int, lens,
+                          opts: Optional[DecodeOpts] = None) -> int:
+    """pkv_decode_split_for_lens: split_tokens for a batch of known lengths
+    (a sequence of ints or a CPU int tensor)."""
+    ln = torch.as_tensor(lens, dtype=torch.int32).contiguous().cpu()
+    out = C.c_int32(0)
+    _check(lib().pkv_decode_split_for_lens(C.byref(desc), int(ln.numel()), int(num_q_heads),
+                                           _p(ln) if ln.numel() else None,
+                                           C.byref(opts) if opts is not None else None,
+                                           C.byref(out)))
+    return int(out.value)
 
 
 def partials_bytes(batch: int, num_q_heads: int, n_split: int, head_dim: int) -> Tuple[int, int]:

@@ -224,6 +224,11 @@ constexpr int64_t kTargetWorkgroups = 512;
 constexpr int64_t kTargetWorkgroupsMfma = 256;
 constexpr int32_t kXcdSplitTiles = 64;    // prefill: query tiles per (b, kv head)
 constexpr int32_t kMinSplitPages = 16;
+// Splits for batches of unequal lengths (pkv_decode_split_for_lens): small
+// enough that about 1024 workgroups (four per CU) carry the batch, so that the
+// hardware balances the uneven tails, and at least 32 pages each.
+constexpr int64_t kUnevenWorkgroups = 1024;
+constexpr int64_t kUnevenMinPages = 32;
 
 int make_plan(const pkv_cache_desc* d, int32_t batch, int32_t num_q_heads,
               int32_t max_context_len, int32_t split_tokens, int q_dtype, Plan* plan) {
@@ -531,6 +536,66 @@ int pkv_decode_plan_ex(const pkv_cache_desc* desc, int32_t batch, int32_t num_q_
                        const pkv_decode_opts* opts, int32_t* n_split, size_t* workspace_bytes) {
   return plan_impl(desc, batch, num_q_heads, max_context_len, split_tokens, opts, n_split,
                    workspace_bytes);
+}
+
+int pkv_decode_split_for_lens(const pkv_cache_desc* desc, int32_t batch, int32_t num_q_heads,
+                              const int32_t* lens_host, const pkv_decode_opts* opts,
+                              int32_t* split_tokens) {
+  if (int rc = check_desc(desc)) return rc;
+  pkv_decode_opts o;
+  if (int rc = resolve_opts(desc, opts, &o)) return rc;
+  int group = 0;
+  if (int rc = check_heads(desc, num_q_heads, &group)) return rc;
+  if (int rc = check_decode_group(desc, o.q_dtype, group)) return rc;
+  if (batch < 0) return fail(PKV_ERR_INVALID, "batch %d < 0", batch);
+  if (!split_tokens || (batch > 0 && !lens_host)) return fail(PKV_ERR_INVALID, "NULL pointer");
+  const int P = desc->page_size;
+  // pages the decode visits (and the split plan counts) for each sequence
+  int64_t total = 0, lo = -1, hi = -1;
+  int32_t max_len = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t L = lens_host[b];
+    if (L < 0) return fail(PKV_ERR_INVALID, "lens[%d] = %lld < 0", b, (long long)L);
+    if (L > max_len) max_len = (int32_t)L;
+    const int64_t pages = (L + P - 1) / P;
+    int64_t v = pages;
+    if (o.window > 0 && L > o.window) {
+      const int64_t sink_pages = ((o.sink < L ? (int64_t)o.sink : L) + P - 1) / P;
+      const int64_t first = (L - o.window) / P;
+      v = sink_pages + (pages - (first > sink_pages ? first : sink_pages));
+    }
+    total += v;
+    lo = (lo < 0 || v < lo) ? v : lo;
+    hi = v > hi ? v : hi;
+  }
+  int64_t pps;
+  if (lo == hi) {
+    // equal sequences divide evenly: the automatic split
+    Plan plan;
+    if (int rc = make_plan(desc, batch, num_q_heads, plan_len(max_len, o, P), 0, o.q_dtype,
+                           &plan))
+      return rc;
+    pps = plan.pages_per_split;
+  } else {
+    pps = (total * desc->num_kv_heads + kUnevenWorkgroups - 1) / kUnevenWorkgroups;
+    if (pps < kUnevenMinPages) pps = kUnevenMinPages;
+    // An odd number of splits: workgroup i runs on XCD i % 8 and a unit's
+    // splits are consecutive workgroups, so with n splits the first split of
+    // unit u lands on XCD (u * n) % 8; an odd n spreads the units' first
+    // splits -- all a short sequence has -- over every XCD, where an even n
+    // would stack them on a few.
+    const int64_t max_pages = ((int64_t)plan_len(max_len, o, P) + P - 1) / P;   // as make_plan
+    for (int64_t p = pps; p > kUnevenMinPages / 2; --p) {
+      const int64_t n = (max_pages + p - 1) / p;
+      if (n == 1 || (n & 1)) {
+        pps = p;
+        break;
+      }
+    }
+  }
+  if (pps * P > 0x7fffffff) return fail(PKV_ERR_INVALID, "split out of range");
+  *split_tokens = (int32_t)(pps * P);
+  return ok();
 }
 
 int pkv_paged_attn_decode(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache,

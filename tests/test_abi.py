@@ -2,6 +2,7 @@
 header declares, and every invalid-argument path returns its status before
 any HIP call (fake, aligned device addresses are never dereferenced)."""
 import ctypes as C
+import math
 
 import pytest
 import torch
@@ -111,6 +112,43 @@ def test_plan_group_16(L):
     assert n.value == 16
     assert L.pkv_decode_plan(C.byref(desc(dtype=0)), 8, 32, 4096, 0, C.byref(n),
                              C.byref(ws)) == -2
+
+
+def test_split_for_lens(L):
+    """The lengths-aware split: equal lengths give the automatic split; an
+    uneven batch spreads its visited pages over ~1024 workgroups of at least
+    32 pages; a window counts only the pages it visits."""
+    d = desc(num_pages=65537, dtype=1)
+    out = C.c_int32()
+
+    def split(lens, hq=16, opts=None):
+        arr = (C.c_int32 * len(lens))(*lens)
+        rc = L.pkv_decode_split_for_lens(C.byref(d), len(lens), hq, arr,
+                                         C.byref(opts) if opts else None, C.byref(out))
+        return rc, out.value
+
+    assert split([131072] * 8) == (0, 8192)                 # the automatic 16 splits
+    lens = [8192, 40000, 70000, 100000, 131071, 20000]
+    rc, s = split(lens)
+    assert rc == 0 and s % 16 == 0
+    pps = s // 16
+    active = 2 * sum(math.ceil(math.ceil(n / 16) / pps) for n in lens)   # x 2 KV heads
+    assert 0.95 * 1024 <= active <= 1024 + 2 * len(lens)    # split size rounds up
+    opts = binding.DecodeOpts(1, 1.0, 1.0, 4096, 128)
+    assert split([131072] * 8, opts=opts) == (0, 272)       # 17 of the window's 265 pages
+    # both visit 264 pages: the automatic split of that batch (17 splits of 16 pages)
+    n, ws = C.c_int32(), C.c_size_t()
+    assert L.pkv_decode_plan_ex(C.byref(d), 2, 16, 131072, 0, C.byref(opts), C.byref(n),
+                                C.byref(ws)) == 0
+    assert split([131072, 100000], opts=opts) == (0, 16 * math.ceil(265 / n.value))
+    assert split([100, 200])[1] == 32 * 16                  # at least 32 pages per split
+    assert L.pkv_decode_plan(C.byref(d), 64, 32, 4096, 0, C.byref(n), C.byref(ws)) == 0
+    assert split([4096] * 64, hq=32) == (0, 16 * math.ceil(256 / n.value))   # equal: automatic
+    assert split([5, -1])[0] == -1
+    assert split([5], hq=5)[0] == -1
+    assert L.pkv_decode_split_for_lens(C.byref(d), 1, 16, None, None, C.byref(out)) == -1
+    assert L.pkv_decode_split_for_lens(C.byref(desc(dtype=0)), 1, 32,
+                                       (C.c_int32 * 1)(5), None, C.byref(out)) == -2
 
 
 def test_merge_args(L):

@@ -222,6 +222,33 @@ def test_split_sweep_and_partials_path():
             assert torch.equal(bits(lse2.view_as(lse)), bits(lse))
 
 
+@pytest.mark.parametrize("dtype,hq,hkv,window", [("f16", 16, 2, 0), ("bf16", 8, 2, 0),
+                                                 ("bf16", 32, 4, 700), ("f32", 4, 2, 0)])
+def test_uneven_batch_with_split_for_lens(dtype, hq, hkv, window):
+    """Lengths from 1 key to 20K in one batch, decoded with the lengths-aware
+    split (many splits for the long rows, one for the short)."""
+    lens = [1, 5, 100, 3000, 20000, 777]
+    d_ = 64 if dtype == "f32" else 128
+    w = W.make_decode("uneven", seed=121 + hq, batch=len(lens), hq=hq, hkv=hkv, d=d_,
+                      dtype=dtype, hist_lens=lens, append=False, pool_slack=0.1)
+    d = to_dev(w, DEV)
+    desc = pkv.cache_desc(d["k_cache"])
+    opts = pkv.decode_opts(d["q"].dtype, d["k_cache"].dtype, window=window, sink=16)
+    split = pkv.decode_split_for_lens(desc, hq, lens, opts)
+    n_split, _ = pkv.decode_plan(desc, w.batch, hq, w.max_context_len, split, opts)
+    assert n_split > 1
+    out, lse = pkv.paged_attn_decode(d["q"], d["k_cache"], d["v_cache"], d["block_table"],
+                                     d["context_lens"], w.max_context_len, w.scale,
+                                     split_tokens=split, return_lse=True, window=window,
+                                     sink=16 if window else 0)
+    torch.cuda.synchronize()
+    ref, ref_lse = pkvref.decode_ex(dtype, dtype, w.k_cache, w.v_cache, w.q, w.block_table,
+                                    w.context_lens, w.scale, window=window,
+                                    sink=16 if window else 0, n_threads=host_threads())
+    assert_close(out.reshape(ref.shape), ref, dtype, f"uneven {dtype} G{hq // hkv}")
+    assert_lse_close(lse.reshape(-1), ref_lse, dtype, f"uneven {dtype} G{hq // hkv}")
+
+
 def test_merge_states_matches_oracle():
     gen = torch.Generator().manual_seed(14)
     rows, n, dd = 37, 70, 128
