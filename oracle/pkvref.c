@@ -28,7 +28,8 @@
  *   - Merging partial results over disjoint key sets by their log-sum-exp,
  *     the same recursion that the pages' online softmax rests on.
  *   - An fp8 KV cache (page 1, section 4.1 and page 4, section 3.2 name the
- *     e4m3 and e5m2 cache types; page 4, chapter 6 calls fp8 the most
+ *     e4m3 and e5m2 cache types, the latter in a serving setup that also
+ *     prefills in chunks; page 4, chapter 6 calls fp8 the most
  *     cost-effective saving): element = per-tensor fp32 scale times the
  *     OCP 8-bit float value; a new token is stored as the code nearest to
  *     x / scale (x / scale taken in fp32, ties to the even code), clipped to
@@ -397,20 +398,25 @@ int pkvref_decode(int dtype, int32_t num_pages, int32_t page_size, int32_t num_k
 }
 
 /*
- * prefill chunk: q packed [sum_b C_b][H_q][D] with q_indptr [B+1] (host);
- * kv_lens[b] counts history plus chunk.  rows: indices r = tok * H_q + h
- * (tok indexes the packed query tokens), or NULL for all.  out [n_rows][D],
- * lse [n_rows].
+ * prefill_ex: chunked prefill, q packed [sum_b C_b][H_q][D] of q_dtype with
+ * q_indptr [B+1] (host); kv_lens[b] counts history plus chunk.  The pools hold
+ * kv_dtype (for fp8, element = k_scale or v_scale times the code's value;
+ * otherwise the scales must be 1 and kv_dtype == q_dtype).  rows: indices
+ * r = tok * H_q + h (tok indexes the packed query tokens), or NULL for all.
+ * out [n_rows][D], lse [n_rows].
  */
-int pkvref_prefill(int dtype, int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
-                   int32_t head_dim, const void* k_cache, const void* v_cache, const void* q,
-                   const int32_t* q_indptr, int32_t batch, int32_t num_q_heads,
-                   const int32_t* block_table, int32_t stride, const int32_t* kv_lens,
-                   float scale, const int64_t* rows, int64_t n_rows, double* out, double* lse,
-                   int32_t n_threads) {
-  if (!elem_bytes(dtype) || is_fp8(dtype) || page_size <= 0 || num_kv_heads <= 0 ||
-      head_dim <= 0 || batch < 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
-      stride <= 0)
+int pkvref_prefill_ex(int q_dtype, int kv_dtype, int32_t num_pages, int32_t page_size,
+                      int32_t num_kv_heads, int32_t head_dim, const void* k_cache,
+                      const void* v_cache, float k_scale, float v_scale, const void* q,
+                      const int32_t* q_indptr, int32_t batch, int32_t num_q_heads,
+                      const int32_t* block_table, int32_t stride, const int32_t* kv_lens,
+                      float scale, const int64_t* rows, int64_t n_rows, double* out, double* lse,
+                      int32_t n_threads) {
+  if (!elem_bytes(q_dtype) || is_fp8(q_dtype) || !elem_bytes(kv_dtype) || page_size <= 0 ||
+      num_kv_heads <= 0 || head_dim <= 0 || batch < 0 || num_q_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || stride <= 0)
+    return -1;
+  if (!is_fp8(kv_dtype) && (kv_dtype != q_dtype || k_scale != 1.0f || v_scale != 1.0f))
     return -1;
   if (q_indptr[0] != 0) return -1;
   for (int32_t b = 0; b < batch; ++b) {
@@ -447,15 +453,29 @@ int pkvref_prefill(int dtype, int32_t num_pages, int32_t page_size, int32_t num_
         s_cap = n_keys;
         s = (double*)malloc(sizeof(double) * s_cap);
       }
-      for (int32_t d = 0; d < head_dim; ++d) qd[d] = load_elem(q, r * head_dim + d, dtype);
-      err |= attend_row(dtype, num_pages, page_size, num_kv_heads, head_dim, k_cache, v_cache,
-                        1.0, 1.0, block_table + (int64_t)b * stride, n_keys, 0, 0, h / group,
-                        qd, (double)scale, s, out + i * head_dim, lse + i);
+      for (int32_t d = 0; d < head_dim; ++d) qd[d] = load_elem(q, r * head_dim + d, q_dtype);
+      err |= attend_row(kv_dtype, num_pages, page_size, num_kv_heads, head_dim, k_cache,
+                        v_cache, (double)k_scale, (double)v_scale,
+                        block_table + (int64_t)b * stride, n_keys, 0, 0, h / group, qd,
+                        (double)scale, s, out + i * head_dim, lse + i);
     }
     free(s);
     free(qd);
   }
   return err ? -1 : 0;
+}
+
+/* prefill chunk: prefill_ex with one element type and unit scales. */
+int pkvref_prefill(int dtype, int32_t num_pages, int32_t page_size, int32_t num_kv_heads,
+                   int32_t head_dim, const void* k_cache, const void* v_cache, const void* q,
+                   const int32_t* q_indptr, int32_t batch, int32_t num_q_heads,
+                   const int32_t* block_table, int32_t stride, const int32_t* kv_lens,
+                   float scale, const int64_t* rows, int64_t n_rows, double* out, double* lse,
+                   int32_t n_threads) {
+  if (is_fp8(dtype)) return -1;
+  return pkvref_prefill_ex(dtype, dtype, num_pages, page_size, num_kv_heads, head_dim, k_cache,
+                           v_cache, 1.0f, 1.0f, q, q_indptr, batch, num_q_heads, block_table,
+                           stride, kv_lens, scale, rows, n_rows, out, lse, n_threads);
 }
 
 /*

@@ -34,11 +34,14 @@ def _configure(L):
                                  i32, vp, f32, vp, i64, vp, vp, i32]
     L.pkvref_decode_ex.argtypes = [C.c_int, C.c_int, i32, i32, i32, i32, vp, vp, f32, f32, vp,
                                    i32, i32, vp, i32, vp, f32, i32, i32, vp, i64, vp, vp, i32]
+    L.pkvref_prefill_ex.argtypes = [C.c_int, C.c_int, i32, i32, i32, i32, vp, vp, f32, f32, vp,
+                                    vp, i32, i32, vp, i32, vp, f32, vp, i64, vp, vp, i32]
     L.pkvref_merge.argtypes = [vp, vp, i64, i32, i32, vp, vp]
     L.pkvref_to_double.argtypes = [C.c_int, vp, i64, vp]
     L.pkvref_quant_fp8.argtypes = [C.c_int, C.c_int, vp, i64, f32, vp]
     for fn in ("pkvref_kv_append", "pkvref_gather", "pkvref_decode", "pkvref_prefill",
-               "pkvref_merge", "pkvref_to_double", "pkvref_decode_ex", "pkvref_quant_fp8"):
+               "pkvref_merge", "pkvref_to_double", "pkvref_decode_ex", "pkvref_quant_fp8",
+               "pkvref_prefill_ex"):
         getattr(L, fn).restype = C.c_int
     return L
 
@@ -179,6 +182,15 @@ def prefill(dtype: str, k_cache, v_cache, q, q_indptr, block_table, kv_lens, sca
     """Chunked-prefill attention over the cache.  q packed [sum C][H_q][D].
     Returns (out [n_rows][D], lse [n_rows]) in float64; rows are indices
     tok * H_q + h (default: all)."""
+    return prefill_ex(dtype, dtype, k_cache, v_cache, q, q_indptr, block_table, kv_lens, scale,
+                      rows=rows, n_threads=n_threads)
+
+
+def prefill_ex(q_dtype: str, kv_dtype: str, k_cache, v_cache, q, q_indptr, block_table, kv_lens,
+               scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+               rows: Optional[Sequence[int]] = None, n_threads: int = 0):
+    """Chunked prefill over a cache type apart from the query type (fp8 pools
+    with per-tensor scales).  Returns (out, lse) in float64 as prefill()."""
     num_pages, hkv, p, d = k_cache.shape
     n_tok, hq, dq = q.shape
     assert dq == d
@@ -190,10 +202,11 @@ def prefill(dtype: str, k_cache, v_cache, q, q_indptr, block_table, kv_lens, sca
     n = n_tok * hq if r is None else int(r.shape[0])
     out = np.zeros((n, d), dtype=np.float64)
     lse = np.zeros((n,), dtype=np.float64)
-    _check(lib().pkvref_prefill(DTYPE_CODES[dtype], num_pages, p, hkv, d, _ptr(k_cache),
-                                _ptr(v_cache), _ptr(q), _ptr(qi), batch, hq, _ptr(bt),
-                                int(bt.shape[1]), _ptr(kl), float(scale), _ptr(r), n, _ptr(out),
-                                _ptr(lse), int(n_threads)), "prefill")
+    _check(lib().pkvref_prefill_ex(DTYPE_CODES[q_dtype], DTYPE_CODES[kv_dtype], num_pages, p,
+                                   hkv, d, _ptr(k_cache), _ptr(v_cache), float(k_scale),
+                                   float(v_scale), _ptr(q), _ptr(qi), batch, hq, _ptr(bt),
+                                   int(bt.shape[1]), _ptr(kl), float(scale), _ptr(r), n,
+                                   _ptr(out), _ptr(lse), int(n_threads)), "prefill_ex")
     return out, lse
 
 

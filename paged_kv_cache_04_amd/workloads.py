@@ -259,13 +259,21 @@ def make_decode(name: str, *, seed: int, batch: int, hq: int, hkv: int, d: int, 
 
 def make_prefill(name: str, *, seed: int, batch: int, hq: int, hkv: int, d: int, dtype: str,
                  hist: List[int], chunk: List[int], pool_slack: float = 0.0,
-                 page_size: int = PAGE_SIZE, gen: Optional[torch.Generator] = None) -> Workload:
+                 page_size: int = PAGE_SIZE, gen: Optional[torch.Generator] = None,
+                 kv_dtype: Optional[str] = None, k_scale: float = 1.0,
+                 v_scale: float = 1.0) -> Workload:
     """Chunked-prefill workload (page 4, section 3.1: the prompt is processed
     in chunks that reuse the KV cache).  hist[b] tokens are stored; chunk[b]
     new query rows follow.  The chunk's own K/V are handed over as k_new/v_new
     with slots at positions hist[b] .. hist[b]+chunk[b]-1; the caller appends
     them before the prefill call, which then attends to hist + chunk tokens.
+    ``kv_dtype`` (default: dtype) sets the cache type; fp8 pools carry
+    k_scale / v_scale and the chunk's K/V arrive in dtype, to be quantized
+    into the cache.
     """
+    kv_dtype = kv_dtype or dtype
+    if kv_dtype not in FP8:
+        assert kv_dtype == dtype and k_scale == 1.0 and v_scale == 1.0
     if gen is None:
         gen = torch.Generator().manual_seed(seed)
     total = [h + c for h, c in zip(hist, chunk)]
@@ -283,8 +291,8 @@ def make_prefill(name: str, *, seed: int, batch: int, hq: int, hkv: int, d: int,
 
     n_q = sum(chunk)
     q = _normal(gen, (n_q, hq, d), dtype)
-    k_cache = _normal(gen, (num_pages, hkv, page_size, d), dtype)
-    v_cache = _normal(gen, (num_pages, hkv, page_size, d), dtype)
+    k_cache = _normal_kv(gen, (num_pages, hkv, page_size, d), kv_dtype, k_scale)
+    v_cache = _normal_kv(gen, (num_pages, hkv, page_size, d), kv_dtype, v_scale)
     valid = _valid_mask(num_pages, page_lists, hist, page_size)
     _poison(k_cache, valid)
     _poison(v_cache, valid)
@@ -307,12 +315,15 @@ def make_prefill(name: str, *, seed: int, batch: int, hq: int, hkv: int, d: int,
                     q_indptr=torch.tensor(indptr, dtype=torch.int32),
                     poison_page=poison_page,
                     meta=dict(page_lists=page_lists, hist_lens=list(hist),
-                              chunk_lens=list(chunk), seed=seed))
+                              chunk_lens=list(chunk), seed=seed),
+                    kv_dtype=kv_dtype, k_scale=float(k_scale), v_scale=float(v_scale))
 
 
 def make_mixed(name: str, *, seed: int, hq: int, hkv: int, d: int, dtype: str,
                decode_hist: List[int], chunk_hist: List[int], chunk: List[int],
-               pool_slack: float = 0.0, gen: Optional[torch.Generator] = None) -> Workload:
+               pool_slack: float = 0.0, gen: Optional[torch.Generator] = None,
+               kv_dtype: Optional[str] = None, k_scale: float = 1.0,
+               v_scale: float = 1.0) -> Workload:
     """A decode-first ragged batch: len(decode_hist) sequences with one new
     token each (a chunk of one row), then the prompt chunks.  Same layout as a
     prefill workload (every new row's K/V handed over for the append); meta
@@ -320,7 +331,7 @@ def make_mixed(name: str, *, seed: int, hq: int, hkv: int, d: int, dtype: str,
     w = make_prefill(name, seed=seed, batch=len(decode_hist) + len(chunk), hq=hq, hkv=hkv, d=d,
                      dtype=dtype, hist=list(decode_hist) + list(chunk_hist),
                      chunk=[1] * len(decode_hist) + list(chunk), pool_slack=pool_slack,
-                     gen=gen)
+                     gen=gen, kv_dtype=kv_dtype, k_scale=k_scale, v_scale=v_scale)
     w.kind = "mixed"
     w.meta["num_decode"] = len(decode_hist)
     return w

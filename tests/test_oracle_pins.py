@@ -12,7 +12,8 @@
 - fp8 caches: every OCP e4m3 / e5m2 code widened as torch's own float8 types
   widen it (and e5m2 as the top byte of an IEEE half, by numpy), the
   quantizer against torch's float8 rounding of the clipped fp32 quotient, and
-  decode over fp8 pools against dense attention on the dequantized rows,
+  decode and chunked prefill over fp8 pools against dense attention on the
+  dequantized rows,
 - sliding window: the last row of the pages' mixed local/global attention
   mask (page 4, section 2.3) computed densely, a window of one key returning
   that key's V row exactly, and pages outside the window never read,
@@ -582,6 +583,45 @@ def test_dense_decode_fp8(kv_dtype):
     check_dense_decode_fp8(kv_dtype)
 
 
+def check_dense_prefill_fp8(kv_dtype, qd="f16"):
+    """Chunked prefill over fp8 pools (the chunk quantized in by the oracle's
+    append) against SDPA in float64 on the dequantized rows with the
+    bottom-right causal mask."""
+    w = W.make_prefill("f8p", seed=52, batch=3, hq=8, hkv=2, d=32, dtype=qd,
+                       hist=[0, 21, 40], chunk=[5, 16, 9], pool_slack=0.2, kv_dtype=kv_dtype,
+                       k_scale=0.046875, v_scale=0.0234375)
+    f8 = W.DTYPES[kv_dtype]
+    kq = torch.from_numpy(pkvref.quant_fp8(kv_dtype, qd, w.k_new, w.k_scale)).view(f8)
+    vq = torch.from_numpy(pkvref.quant_fp8(kv_dtype, qd, w.v_new, w.v_scale)).view(f8)
+    pkvref.kv_append(kv_dtype, w.k_cache, w.v_cache, kq, vq, w.slots)
+    out, lse = pkvref.prefill_ex(qd, kv_dtype, w.k_cache, w.v_cache, w.q, w.q_indptr,
+                                 w.block_table, w.context_lens, w.scale, k_scale=w.k_scale,
+                                 v_scale=w.v_scale)
+    G = w.num_q_heads // w.num_kv_heads
+    ind = w.q_indptr.tolist()
+    for b in range(w.batch):
+        kc, vc = W.contiguous_kv(w, b)
+        L, C = kc.shape[0], ind[b + 1] - ind[b]
+        kd = (kc.to(torch.float64) * w.k_scale).permute(1, 0, 2).repeat_interleave(G, dim=0)
+        vd = (vc.to(torch.float64) * w.v_scale).permute(1, 0, 2).repeat_interleave(G, dim=0)
+        q = w.q[ind[b]:ind[b + 1]].double().permute(1, 0, 2)
+        mask = torch.zeros(C, L, dtype=torch.bool)
+        for i in range(C):
+            mask[i, : L - C + i + 1] = True
+        ref = _sdpa_rows(q, kd, vd, w.scale, mask=mask).permute(1, 0, 2).reshape(C * w.num_q_heads, -1)
+        rows = slice(ind[b] * w.num_q_heads, ind[b + 1] * w.num_q_heads)
+        np.testing.assert_allclose(out[rows], ref.numpy(), rtol=1e-10, atol=1e-11)
+        scores = (torch.matmul(q, kd.transpose(1, 2)) * float(w.scale)).masked_fill(
+            ~mask, float("-inf"))
+        ref_lse = torch.logsumexp(scores, dim=-1).permute(1, 0).reshape(-1).numpy()
+        np.testing.assert_allclose(lse[rows], ref_lse, rtol=1e-11, atol=1e-11)
+
+
+@pytest.mark.parametrize("kv_dtype,qd", [("fp8_e4m3", "f16"), ("fp8_e5m2", "bf16")])
+def test_dense_prefill_fp8(kv_dtype, qd):
+    check_dense_prefill_fp8(kv_dtype, qd)
+
+
 def _listing_mask_last_row(n, window_size, global_tokens):
     """Row n-1 of the mixed local/global mask of page 4, section 2.3: row i
     sees columns [i - window_size // 2, i + window_size // 2] clipped to the
@@ -690,6 +730,9 @@ MUTATIONS = [
     ("quantiser ties to odd", "(d == best_d && (c & 1) == 0)", "(d == best_d && (c & 1) == 1)"),
     ("quantiser without saturation", "int best = max_code;", "int best = 0;"),
     ("k scale dropped", "q_row[d] * (k_scale * load_elem", "q_row[d] * (load_elem"),
+    ("prefill k scale dropped",
+     "v_cache, (double)k_scale, (double)v_scale,\n                        block_table + (int64_t)b",
+     "v_cache, 1.0, (double)v_scale,\n                        block_table + (int64_t)b"),
     ("v scale dropped", "w * (v_scale * load_elem", "w * (1.0 * load_elem"),
     ("window one key short", "lo = n_keys - window > 0 ? n_keys - window : 0;",
      "lo = n_keys - window + 1 > 0 ? n_keys - window + 1 : 0;"),
@@ -711,6 +754,7 @@ def _battery():
     check_fp8_quant()
     for kv in FP8:
         check_dense_decode_fp8(kv)
+        check_dense_prefill_fp8(kv)
     check_window_listing()
 
 
