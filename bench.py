@@ -20,6 +20,7 @@ Extra objects (--extras, all by default) measure the other rows of the hot
 path on their own workloads, each with the roofline of its dominant kernel
 and a parity check of sampled rows against the oracle:
   prefill_chunk  chunked prefill on the matrix cores (MFMA TFLOP/s)
+  fp8_prefill    the same prefill over fp8 (e5m2) pools (MFMA TFLOP/s)
   fp8_decode     the 128K decode over fp8 (e4m3) pools (HBM GB/s)
   window_decode  the 128K decode with a 4096-key window and a 128-key sink
   mixed_batch    an 8192-token batch of decode rows and prefill chunks
@@ -89,9 +90,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="lower bound on the CPU oracle sample's wall time")
-    ap.add_argument("--extras", default="prefill,fp8,window,mixed",
-                    help="comma-separated extra rows to measure: prefill, fp8, window, mixed "
-                         "('' or 'none' for none)")
+    ap.add_argument("--extras", default="prefill,fp8prefill,fp8,window,mixed",
+                    help="comma-separated extra rows to measure: prefill, fp8prefill, fp8, "
+                         "window, mixed ('' or 'none' for none)")
     ap.add_argument("--prefill", action="store_true", help="same as --extras prefill")
     ap.add_argument("--graph", action="store_true",
                     help="time the steps as HIP graph replays instead of eager launches")
@@ -299,6 +300,8 @@ def main():
     torch.cuda.empty_cache()
     if "prefill" in extras:
         line["prefill_chunk"] = bench_prefill(args, dev, sample)
+    if "fp8prefill" in extras:
+        line["fp8_prefill"] = bench_prefill(args, dev, sample, "prefill_fp8")
     if "fp8" in extras:
         line["fp8_decode"] = bench_fp8(args, dev, sample)
     if "mixed" in extras:
@@ -431,8 +434,9 @@ def _mfma_roofline(kernel, flops, us, dtype):
             "algorithmic_flops_per_launch": int(flops), "kernel_avg_us": round(us, 2)}
 
 
-def bench_prefill(args, dev, sample):
-    progress("prefill_chunk")
+def bench_prefill(args, dev, sample, config="prefill"):
+    fp8 = config == "prefill_fp8"
+    progress("fp8_prefill" if fp8 else "prefill_chunk")
     import numpy as np
     import torch
 
@@ -440,33 +444,49 @@ def bench_prefill(args, dev, sample):
     from paged_kv_cache_04_amd import accounting as A
     from paged_kv_cache_04_amd import workloads as W
 
-    w = W.make("prefill")
+    w = W.make(config)
     kc, vc = w.k_cache.to(dev), w.v_cache.to(dev)
     q, bt, kl = w.q.to(dev), w.block_table.to(dev), w.context_lens.to(dev)
     qi = w.q_indptr.to(dev)
-    pkv.kv_append(kc, vc, w.k_new.to(dev), w.v_new.to(dev), w.slots.to(dev))
+    sc = dict(k_scale=w.k_scale, v_scale=w.v_scale) if fp8 else {}
+    if fp8:
+        pkv.kv_append_quant(kc, vc, w.k_new.to(dev), w.v_new.to(dev), w.slots.to(dev), **sc)
+    else:
+        pkv.kv_append(kc, vc, w.k_new.to(dev), w.v_new.to(dev), w.slots.to(dev))
     out = torch.empty_like(q)
     chunk = w.meta["chunk_lens"]
 
     def run():
         pkv.paged_attn_prefill_chunk(q, kc, vc, qi, bt, kl, max(chunk), w.max_context_len,
-                                     w.scale, out=out)
+                                     w.scale, out=out, **sc)
 
     us, us_med = _event_times(run, 10)
     flops = A.prefill_flops(w.context_lens.tolist(), chunk, w.num_q_heads, w.head_dim)
-    res = {"workload": "batch 4, 32768-token paged history + 512-row causal chunk, 32 q / 8 kv "
-                       "heads, head_dim 128, bf16",
+    text = ("batch 4, 32768-token paged history + 512-row causal chunk, 32 q / 8 kv heads, "
+            "head_dim 128, bf16")
+    if fp8:
+        text += (" queries over fp8 e5m2 pools with fp32 scales (page 4, section 3.1's "
+                 "serving setup), each page widened exactly to bf16 in the kernel")
+    res = {"workload": text,
            "kernel_avg_us": round(us, 2), "kernel_median_us": round(us_med, 2),
            "query_tokens_per_s": round(sum(chunk) / (us * 1e-6), 1),
-           "roofline": _mfma_roofline("prefill_kernel", flops, us, "bf16")}
+           "roofline": _mfma_roofline("prefill_kernel" + ("<bf16 q, fp8 e5m2 cache>" if fp8 else ""),
+                                      flops, us, "bf16")}
     if sample:
         from oracle import pkvref
         hq = w.num_q_heads
         toks = [int(w.q_indptr[b]) + i for b in range(w.batch) for i in (0, 255, 511)]
         rows = [t * hq + h for t in toks for h in (0, 13, 31)]
-        pkvref.kv_append(w.dtype, w.k_cache, w.v_cache, w.k_new, w.v_new, w.slots)
-        ref, _ = pkvref.prefill(w.dtype, w.k_cache, w.v_cache, w.q, w.q_indptr, w.block_table,
-                                w.context_lens, w.scale, rows=rows, n_threads=host_cores())
+        if fp8:
+            f8 = W.DTYPES[w.kv_dtype]
+            kq = torch.from_numpy(pkvref.quant_fp8(w.kv_dtype, w.dtype, w.k_new, w.k_scale))
+            vq = torch.from_numpy(pkvref.quant_fp8(w.kv_dtype, w.dtype, w.v_new, w.v_scale))
+            pkvref.kv_append(w.kv_dtype, w.k_cache, w.v_cache, kq.view(f8), vq.view(f8), w.slots)
+        else:
+            pkvref.kv_append(w.dtype, w.k_cache, w.v_cache, w.k_new, w.v_new, w.slots)
+        ref, _ = pkvref.prefill_ex(w.dtype, w.kv_dtype, w.k_cache, w.v_cache, w.q, w.q_indptr,
+                                   w.block_table, w.context_lens, w.scale, rows=rows,
+                                   n_threads=host_cores(), **sc)
         got = out.float().cpu().double().numpy().reshape(-1, w.head_dim)[rows]
         res["parity"] = _parity(got, ref, w.dtype)
     return res

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define PKV_VERSION 2
+#define PKV_VERSION 3
 
 /*
  * Element types.  The fp8 types are the OCP 8-bit floats (E4M3 without
@@ -93,8 +93,8 @@ typedef struct pkv_cache_desc {
 } pkv_cache_desc;
 
 /*
- * Options of the *_ex decode calls.  NULL options mean: q_dtype = the cache
- * dtype, unit scales, no window.
+ * Options of the *_ex decode, prefill and mixed-batch calls.  NULL options
+ * mean: q_dtype = the cache dtype, unit scales, no window.
  *   q_dtype  : pkv_dtype of q and out.  Must equal desc->dtype for f32, f16
  *              and bf16 caches; PKV_F16 or PKV_BF16 for fp8 caches.
  *   k_scale, v_scale : fp8 caches only (1 otherwise): a K (V) element is
@@ -110,6 +110,8 @@ typedef struct pkv_cache_desc {
  *              entries are not looked at.
  *   sink     : >= 0; ignored when window == 0.
  */
+/* The prefill and mixed-batch calls take q_dtype and the scales; their
+ * window and sink must be 0. */
 typedef struct pkv_decode_opts {
   int32_t q_dtype;
   float k_scale;
@@ -315,8 +317,8 @@ int pkv_merge_states(const float* o_parts, const float* lse_parts, int32_t rows,
  *   max_kv_len   : host bound >= every kv_lens[b], <= stride * P.
  *   lse_out      : device float [total_q_rows][H_q] or NULL.
  * QK^T and PV run on the matrix cores (MFMA, fp32 accumulation); the
- * probabilities enter the PV product rounded to the K/V type.  Needs f16 or
- * bf16 and head_dim 128.
+ * probabilities enter the PV product rounded to the query type.  Needs f16
+ * or bf16 pools and head_dim 128 (fp8 pools: the _ex form).
  */
 int pkv_paged_attn_prefill_chunk(const pkv_cache_desc* desc, const void* k_cache,
                                  const void* v_cache, const void* q, const int32_t* q_indptr,
@@ -325,6 +327,27 @@ int pkv_paged_attn_prefill_chunk(const pkv_cache_desc* desc, const void* k_cache
                                  int32_t block_table_stride, const int32_t* kv_lens,
                                  int32_t max_kv_len, float scale, void* out, float* lse_out,
                                  void* stream);
+
+/*
+ * paged_attn_prefill_chunk_ex -- paged_attn_prefill_chunk with options, for
+ * fp8 pools (page 4, section 3.1 prefills in chunks over an fp8_e5m2 cache;
+ * page 1, section 4.1 names e4m3).  opts: q_dtype PKV_F16 or PKV_BF16 for
+ * fp8 pools (q and out of that type), k_scale / v_scale as for decode;
+ * window and sink must be 0 (PKV_ERR_INVALID otherwise).  The chunk's K/V go
+ * in with pkv_kv_append_quant first.  Each fp8 page is widened exactly to
+ * q_dtype inside the kernel; the K scale multiplies the softmax scale, the V
+ * scale the output.  NULL opts: as paged_attn_prefill_chunk (fp8 pools then
+ * fail with PKV_ERR_INVALID).
+ */
+int pkv_paged_attn_prefill_chunk_ex(const pkv_cache_desc* desc, const void* k_cache,
+                                    const void* v_cache, const void* q,
+                                    const int32_t* q_indptr, int32_t batch,
+                                    int32_t num_q_heads, int32_t total_q_rows,
+                                    int32_t max_q_len, const int32_t* block_table,
+                                    int32_t block_table_stride, const int32_t* kv_lens,
+                                    int32_t max_kv_len, float scale,
+                                    const pkv_decode_opts* opts, void* out, float* lse_out,
+                                    void* stream);
 
 /*
  * paged_attn_mixed -- one call for a ragged batch that mixes decode rows and
@@ -344,7 +367,8 @@ int pkv_paged_attn_prefill_chunk(const pkv_cache_desc* desc, const void* k_cache
  *   max_q_len  : host bound >= C_b of every chunk sequence (>= 1 if any).
  *   workspace  : >= the workspace_bytes of pkv_decode_plan(desc, num_decode,
  *                num_q_heads, max_kv_len, split_tokens); may be NULL when 0.
- * Other arguments as for paged_attn_prefill_chunk (f16 or bf16, head_dim 128).
+ * Other arguments as for paged_attn_prefill_chunk (f16 or bf16, head_dim 128;
+ * fp8 pools: the _ex form).
  */
 int pkv_paged_attn_mixed(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache,
                          const void* q, const int32_t* q_indptr, int32_t batch,
@@ -353,6 +377,22 @@ int pkv_paged_attn_mixed(const pkv_cache_desc* desc, const void* k_cache, const 
                          int32_t block_table_stride, const int32_t* kv_lens, int32_t max_kv_len,
                          float scale, int32_t split_tokens, void* out, float* lse_out,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * paged_attn_mixed_ex -- paged_attn_mixed with options (fp8 pools): opts as
+ * for paged_attn_prefill_chunk_ex, used for both the decode rows and the
+ * chunks; the workspace is that of pkv_decode_plan_ex(desc, num_decode,
+ * num_q_heads, max_kv_len, split_tokens, opts).
+ */
+int pkv_paged_attn_mixed_ex(const pkv_cache_desc* desc, const void* k_cache,
+                            const void* v_cache, const void* q, const int32_t* q_indptr,
+                            int32_t batch, int32_t num_decode, int32_t num_q_heads,
+                            int32_t total_q_rows, int32_t max_q_len,
+                            const int32_t* block_table, int32_t block_table_stride,
+                            const int32_t* kv_lens, int32_t max_kv_len, float scale,
+                            int32_t split_tokens, const pkv_decode_opts* opts, void* out,
+                            float* lse_out, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /*
  * validate_tables -- host-side check of host copies of the tables (no HIP

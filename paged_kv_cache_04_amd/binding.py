@@ -79,12 +79,17 @@ def lib():
         L.pkv_paged_attn_mixed.argtypes = [dp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, i32,
                                            vp, i32, f32, i32, vp, vp, vp, sz, vp]
         L.pkv_decode_split_for_lens.argtypes = [dp, i32, i32, vp, op, C.POINTER(i32)]
+        L.pkv_paged_attn_prefill_chunk_ex.argtypes = [dp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                                      vp, i32, vp, i32, f32, op, vp, vp, vp]
+        L.pkv_paged_attn_mixed_ex.argtypes = [dp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp,
+                                              i32, vp, i32, f32, i32, op, vp, vp, vp, sz, vp]
         for name in ("pkv_kv_append", "pkv_gather_kv", "pkv_decode_plan", "pkv_paged_attn_decode",
                      "pkv_paged_attn_decode_partials", "pkv_merge_states",
                      "pkv_paged_attn_prefill_chunk", "pkv_validate_tables",
                      "pkv_decode_plan_ex", "pkv_paged_attn_decode_ex",
                      "pkv_paged_attn_decode_partials_ex", "pkv_kv_append_quant",
-                     "pkv_paged_attn_mixed", "pkv_decode_split_for_lens"):
+                     "pkv_paged_attn_mixed", "pkv_decode_split_for_lens",
+                     "pkv_paged_attn_prefill_chunk_ex", "pkv_paged_attn_mixed_ex"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -323,12 +328,23 @@ def merge_states(o_parts, lse_parts, out_dtype=torch.float32, out=None, lse_out=
     return (out, lse_out) if return_lse else out
 
 
+def _query_type(q, k_cache):
+    if k_cache.dtype in _FP8:
+        _dev(q, "q")
+        if q.dtype not in (torch.float16, torch.bfloat16):
+            raise TypeError("queries over an fp8 cache must be float16 or bfloat16")
+    else:
+        _dev(q, "q", k_cache.dtype)
+
+
 def paged_attn_prefill_chunk(q, k_cache, v_cache, q_indptr, block_table, kv_lens,
                              max_q_len: int, max_kv_len: int, scale: float, out=None,
-                             lse_out=None, return_lse: bool = False):
-    """pkv_paged_attn_prefill_chunk.  q packed [sum C][H_q][D]."""
+                             lse_out=None, return_lse: bool = False, k_scale: float = 1.0,
+                             v_scale: float = 1.0):
+    """pkv_paged_attn_prefill_chunk (pkv_paged_attn_prefill_chunk_ex for an fp8
+    cache and its scales).  q packed [sum C][H_q][D]."""
     desc = _check_pools(k_cache, v_cache)
-    _dev(q, "q", k_cache.dtype)
+    _query_type(q, k_cache)
     _dev(q_indptr, "q_indptr", torch.int32)
     _dev(block_table, "block_table", torch.int32)
     _dev(kv_lens, "kv_lens", torch.int32)
@@ -340,21 +356,27 @@ def paged_attn_prefill_chunk(q, k_cache, v_cache, q_indptr, block_table, kv_lens
         lse_out = torch.empty((q.shape[0], hq), dtype=torch.float32, device=q.device)
     if q.dim() != 3 or q.shape[2] != desc.head_dim:
         raise ValueError("q must be [sum C][H_q][D]")
-    _check(lib().pkv_paged_attn_prefill_chunk(
-        C.byref(desc), _p(k_cache), _p(v_cache), _p(q), _p(q_indptr), batch, hq,
-        int(q.shape[0]), int(max_q_len), _p(block_table), int(block_table.shape[1]), _p(kv_lens),
-        int(max_kv_len), float(scale), _p(out), _p(lse_out), _stream()))
+    opts = decode_opts(q.dtype, k_cache.dtype, k_scale, v_scale)
+    args = (C.byref(desc), _p(k_cache), _p(v_cache), _p(q), _p(q_indptr), batch, hq,
+            int(q.shape[0]), int(max_q_len), _p(block_table), int(block_table.shape[1]),
+            _p(kv_lens), int(max_kv_len), float(scale))
+    tail = (_p(out), _p(lse_out), _stream())
+    if opts is None:
+        _check(lib().pkv_paged_attn_prefill_chunk(*args, *tail))
+    else:
+        _check(lib().pkv_paged_attn_prefill_chunk_ex(*args, C.byref(opts), *tail))
     return (out, lse_out) if return_lse else out
 
 
 def paged_attn_mixed(q, k_cache, v_cache, q_indptr, block_table, kv_lens, num_decode: int,
                      max_q_len: int, max_kv_len: int, scale: float, split_tokens: int = 0,
-                     out=None, lse_out=None, workspace=None, return_lse: bool = False):
-    """pkv_paged_attn_mixed: a decode-first ragged batch (sequences
-    0 .. num_decode-1 one row each, then prefill chunks), q packed
-    [sum C][H_q][D]."""
+                     out=None, lse_out=None, workspace=None, return_lse: bool = False,
+                     k_scale: float = 1.0, v_scale: float = 1.0):
+    """pkv_paged_attn_mixed (pkv_paged_attn_mixed_ex for an fp8 cache and its
+    scales): a decode-first ragged batch (sequences 0 .. num_decode-1 one row
+    each, then prefill chunks), q packed [sum C][H_q][D]."""
     desc = _check_pools(k_cache, v_cache)
-    _dev(q, "q", k_cache.dtype)
+    _query_type(q, k_cache)
     _dev(q_indptr, "q_indptr", torch.int32)
     _dev(block_table, "block_table", torch.int32)
     _dev(kv_lens, "kv_lens", torch.int32)
@@ -366,17 +388,21 @@ def paged_attn_mixed(q, k_cache, v_cache, q_indptr, block_table, kv_lens, num_de
         out = torch.empty_like(q)
     if return_lse and lse_out is None:
         lse_out = torch.empty((q.shape[0], hq), dtype=torch.float32, device=q.device)
+    opts = decode_opts(q.dtype, k_cache.dtype, k_scale, v_scale)
     ws_bytes = 0
     if num_decode > 0:
-        _, ws_bytes = decode_plan(desc, num_decode, hq, max_kv_len, split_tokens)
+        _, ws_bytes = decode_plan(desc, num_decode, hq, max_kv_len, split_tokens, opts)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().pkv_paged_attn_mixed(
-        C.byref(desc), _p(k_cache), _p(v_cache), _p(q), _p(q_indptr), batch, int(num_decode), hq,
-        int(q.shape[0]), int(max_q_len), _p(block_table), int(block_table.shape[1]), _p(kv_lens),
-        int(max_kv_len), float(scale), int(split_tokens), _p(out), _p(lse_out), _p(workspace),
-        ws_len, _stream()))
+    args = (C.byref(desc), _p(k_cache), _p(v_cache), _p(q), _p(q_indptr), batch, int(num_decode),
+            hq, int(q.shape[0]), int(max_q_len), _p(block_table), int(block_table.shape[1]),
+            _p(kv_lens), int(max_kv_len), float(scale), int(split_tokens))
+    tail = (_p(out), _p(lse_out), _p(workspace), ws_len, _stream())
+    if opts is None:
+        _check(lib().pkv_paged_attn_mixed(*args, *tail))
+    else:
+        _check(lib().pkv_paged_attn_mixed_ex(*args, C.byref(opts), *tail))
     return (out, lse_out) if return_lse else out
 
 

@@ -689,17 +689,24 @@ int pkv_merge_states(const float* o_parts, const float* lse_parts, int32_t rows,
 namespace {
 
 // Checks and launch of the chunked-prefill kernel for sequences
-// [0, batch) of the given (already offset) tables.
+// [0, batch) of the given (already offset) tables.  opts (nullable): the
+// query type and fp8 pool scales; window and sink must be 0.
 int prefill_checks(const pkv_cache_desc* desc, int32_t num_q_heads, int32_t batch,
                    int32_t total_q_rows, int32_t max_q_len, int32_t block_table_stride,
-                   int32_t max_kv_len, float scale, int* group) {
+                   int32_t max_kv_len, float scale, const pkv_decode_opts* opts,
+                   pkv_decode_opts* o, int* group) {
   if (int rc = check_desc(desc)) return rc;
+  if (int rc = resolve_opts(desc, opts, o)) return rc;
   if (int rc = check_heads(desc, num_q_heads, group)) return rc;
-  if (desc->dtype != PKV_F16 && desc->dtype != PKV_BF16)
-    return fail(PKV_ERR_UNSUPPORTED, "prefill runs on the matrix cores: f16 or bf16 only");
+  if (desc->dtype != PKV_F16 && desc->dtype != PKV_BF16 && !is_fp8(desc->dtype))
+    return fail(PKV_ERR_UNSUPPORTED,
+                "prefill runs on the matrix cores: f16, bf16 or fp8 pools only");
   if (desc->head_dim != 128)
     return fail(PKV_ERR_UNSUPPORTED, "prefill is built for head_dim 128 (got %d)",
                 desc->head_dim);
+  if (o->window != 0 || o->sink != 0)
+    return fail(PKV_ERR_INVALID, "window and sink apply to decode only (got %d, %d)", o->window,
+                o->sink);
   if (batch < 0) return fail(PKV_ERR_INVALID, "batch %d < 0", batch);
   if (total_q_rows < 0) return fail(PKV_ERR_INVALID, "total_q_rows %d < 0", total_q_rows);
   if (max_q_len < 0) return fail(PKV_ERR_INVALID, "max_q_len %d < 0", max_q_len);
@@ -713,12 +720,12 @@ int prefill_checks(const pkv_cache_desc* desc, int32_t num_q_heads, int32_t batc
   return PKV_OK;
 }
 
-int prefill_launch(const pkv_cache_desc* desc, int group, const void* k_cache,
-                   const void* v_cache, const void* q, const int32_t* q_indptr, int32_t batch,
-                   int32_t num_q_heads, int32_t total_q_rows, int32_t max_q_len,
-                   const int32_t* block_table, int32_t block_table_stride,
-                   const int32_t* kv_lens, float scale, void* out, float* lse_out,
-                   hipStream_t stream) {
+int prefill_launch(const pkv_cache_desc* desc, int group, const pkv_decode_opts& o,
+                   const void* k_cache, const void* v_cache, const void* q,
+                   const int32_t* q_indptr, int32_t batch, int32_t num_q_heads,
+                   int32_t total_q_rows, int32_t max_q_len, const int32_t* block_table,
+                   int32_t block_table_stride, const int32_t* kv_lens, float scale, void* out,
+                   float* lse_out, hipStream_t stream) {
   pkv::PrefillArgs a{};
   a.k_cache = k_cache;
   a.v_cache = v_cache;
@@ -739,28 +746,28 @@ int prefill_launch(const pkv_cache_desc* desc, int group, const void* k_cache,
   // are enough of them (>= 8 per XCD) to keep sharing the K/V stream in L2.
   a.xcd_split = a.m_tiles >= kXcdSplitTiles ? 1 : 0;
   a.m_tiles_x = (a.m_tiles + 7) / 8;
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634 * (double)o.k_scale);
+  a.v_scale = o.v_scale;
   a.out = out;
   a.lse_out = lse_out;
   const int64_t blocks = (int64_t)batch * desc->num_kv_heads *
                          (a.xcd_split ? 8 * (int64_t)a.m_tiles_x : (int64_t)a.m_tiles);
   if (blocks > 0x7fffffff) return fail(PKV_ERR_INVALID, "grid too large");
-  return hip_status(pkv::launch_prefill(desc->dtype, desc->head_dim, group, a, stream),
-                    "prefill launch");
+  return hip_status(
+      pkv::launch_prefill(desc->dtype, o.q_dtype, desc->head_dim, group, a, stream),
+      "prefill launch");
 }
 
-}  // namespace
-
-int pkv_paged_attn_prefill_chunk(const pkv_cache_desc* desc, const void* k_cache,
-                                 const void* v_cache, const void* q, const int32_t* q_indptr,
-                                 int32_t batch, int32_t num_q_heads, int32_t total_q_rows,
-                                 int32_t max_q_len, const int32_t* block_table,
-                                 int32_t block_table_stride, const int32_t* kv_lens,
-                                 int32_t max_kv_len, float scale, void* out, float* lse_out,
-                                 void* stream) {
+int prefill_impl(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache,
+                 const void* q, const int32_t* q_indptr, int32_t batch, int32_t num_q_heads,
+                 int32_t total_q_rows, int32_t max_q_len, const int32_t* block_table,
+                 int32_t block_table_stride, const int32_t* kv_lens, int32_t max_kv_len,
+                 float scale, const pkv_decode_opts* opts, void* out, float* lse_out,
+                 void* stream) {
   int group = 0;
+  pkv_decode_opts o;
   if (int rc = prefill_checks(desc, num_q_heads, batch, total_q_rows, max_q_len,
-                              block_table_stride, max_kv_len, scale, &group))
+                              block_table_stride, max_kv_len, scale, opts, &o, &group))
     return rc;
   if (batch == 0 || max_q_len == 0 || total_q_rows == 0) return ok();
   if (!k_cache || !v_cache || !q || !q_indptr || !block_table || !kv_lens || !out)
@@ -772,21 +779,22 @@ int pkv_paged_attn_prefill_chunk(const pkv_cache_desc* desc, const void* k_cache
                                      batch, total_q_rows, max_q_len, max_kv_len, 0,
                                      (hipStream_t)stream))
       return rc;
-  return prefill_launch(desc, group, k_cache, v_cache, q, q_indptr, batch, num_q_heads,
+  return prefill_launch(desc, group, o, k_cache, v_cache, q, q_indptr, batch, num_q_heads,
                         total_q_rows, max_q_len, block_table, block_table_stride, kv_lens,
                         scale, out, lse_out, (hipStream_t)stream);
 }
 
-int pkv_paged_attn_mixed(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache,
-                         const void* q, const int32_t* q_indptr, int32_t batch,
-                         int32_t num_decode, int32_t num_q_heads, int32_t total_q_rows,
-                         int32_t max_q_len, const int32_t* block_table,
-                         int32_t block_table_stride, const int32_t* kv_lens, int32_t max_kv_len,
-                         float scale, int32_t split_tokens, void* out, float* lse_out,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+int mixed_impl(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache,
+               const void* q, const int32_t* q_indptr, int32_t batch, int32_t num_decode,
+               int32_t num_q_heads, int32_t total_q_rows, int32_t max_q_len,
+               const int32_t* block_table, int32_t block_table_stride, const int32_t* kv_lens,
+               int32_t max_kv_len, float scale, int32_t split_tokens,
+               const pkv_decode_opts* opts, void* out, float* lse_out, void* workspace,
+               size_t workspace_bytes, void* stream) {
   int group = 0;
+  pkv_decode_opts o;
   if (int rc = prefill_checks(desc, num_q_heads, batch, total_q_rows, max_q_len,
-                              block_table_stride, max_kv_len, scale, &group))
+                              block_table_stride, max_kv_len, scale, opts, &o, &group))
     return rc;
   if (num_decode < 0 || num_decode > batch || num_decode > total_q_rows)
     return fail(PKV_ERR_INVALID, "num_decode %d outside [0, min(batch %d, total_q_rows %d)]",
@@ -807,16 +815,72 @@ int pkv_paged_attn_mixed(const pkv_cache_desc* desc, const void* k_cache, const 
   if (num_decode > 0) {
     // decode rows: q rows and out rows 0 .. num_decode-1, i.e. [num_decode][H_q][D]
     if (int rc = decode_impl(desc, k_cache, v_cache, q, num_decode, num_q_heads, block_table,
-                             block_table_stride, kv_lens, max_kv_len, scale, split_tokens,
-                             nullptr, out, lse_out, workspace, workspace_bytes, stream))
+                             block_table_stride, kv_lens, max_kv_len, scale, split_tokens, opts,
+                             out, lse_out, workspace, workspace_bytes, stream))
       return rc;
   }
   if (n_chunk == 0) return ok();
-  return prefill_launch(desc, group, k_cache, v_cache, q, q_indptr + num_decode, n_chunk,
+  return prefill_launch(desc, group, o, k_cache, v_cache, q, q_indptr + num_decode, n_chunk,
                         num_q_heads, total_q_rows, max_q_len,
                         block_table + (int64_t)num_decode * block_table_stride,
                         block_table_stride, kv_lens + num_decode, scale, out, lse_out,
                         (hipStream_t)stream);
+}
+
+}  // namespace
+
+int pkv_paged_attn_prefill_chunk(const pkv_cache_desc* desc, const void* k_cache,
+                                 const void* v_cache, const void* q, const int32_t* q_indptr,
+                                 int32_t batch, int32_t num_q_heads, int32_t total_q_rows,
+                                 int32_t max_q_len, const int32_t* block_table,
+                                 int32_t block_table_stride, const int32_t* kv_lens,
+                                 int32_t max_kv_len, float scale, void* out, float* lse_out,
+                                 void* stream) {
+  return prefill_impl(desc, k_cache, v_cache, q, q_indptr, batch, num_q_heads, total_q_rows,
+                      max_q_len, block_table, block_table_stride, kv_lens, max_kv_len, scale,
+                      nullptr, out, lse_out, stream);
+}
+
+int pkv_paged_attn_prefill_chunk_ex(const pkv_cache_desc* desc, const void* k_cache,
+                                    const void* v_cache, const void* q,
+                                    const int32_t* q_indptr, int32_t batch,
+                                    int32_t num_q_heads, int32_t total_q_rows,
+                                    int32_t max_q_len, const int32_t* block_table,
+                                    int32_t block_table_stride, const int32_t* kv_lens,
+                                    int32_t max_kv_len, float scale,
+                                    const pkv_decode_opts* opts, void* out, float* lse_out,
+                                    void* stream) {
+  return prefill_impl(desc, k_cache, v_cache, q, q_indptr, batch, num_q_heads, total_q_rows,
+                      max_q_len, block_table, block_table_stride, kv_lens, max_kv_len, scale,
+                      opts, out, lse_out, stream);
+}
+
+int pkv_paged_attn_mixed(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache,
+                         const void* q, const int32_t* q_indptr, int32_t batch,
+                         int32_t num_decode, int32_t num_q_heads, int32_t total_q_rows,
+                         int32_t max_q_len, const int32_t* block_table,
+                         int32_t block_table_stride, const int32_t* kv_lens, int32_t max_kv_len,
+                         float scale, int32_t split_tokens, void* out, float* lse_out,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  return mixed_impl(desc, k_cache, v_cache, q, q_indptr, batch, num_decode, num_q_heads,
+                    total_q_rows, max_q_len, block_table, block_table_stride, kv_lens,
+                    max_kv_len, scale, split_tokens, nullptr, out, lse_out, workspace,
+                    workspace_bytes, stream);
+}
+
+int pkv_paged_attn_mixed_ex(const pkv_cache_desc* desc, const void* k_cache,
+                            const void* v_cache, const void* q, const int32_t* q_indptr,
+                            int32_t batch, int32_t num_decode, int32_t num_q_heads,
+                            int32_t total_q_rows, int32_t max_q_len,
+                            const int32_t* block_table, int32_t block_table_stride,
+                            const int32_t* kv_lens, int32_t max_kv_len, float scale,
+                            int32_t split_tokens, const pkv_decode_opts* opts, void* out,
+                            float* lse_out, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  return mixed_impl(desc, k_cache, v_cache, q, q_indptr, batch, num_decode, num_q_heads,
+                    total_q_rows, max_q_len, block_table, block_table_stride, kv_lens,
+                    max_kv_len, scale, split_tokens, opts, out, lse_out, workspace,
+                    workspace_bytes, stream);
 }
 
 int pkv_validate_tables(const pkv_cache_desc* desc, const int32_t* block_table_host,

@@ -51,7 +51,8 @@ struct PrefillArgs {
   int32_t m_tiles;              // query-row tiles per (b, kv head)
   int32_t xcd_split;            // 1: tile ranges spread over the 8 XCDs (see prefill.hip)
   int32_t m_tiles_x;            // ceil(m_tiles / 8): tiles per XCD and (b, kv head)
-  float scale_log2;
+  float scale_log2;             // softmax scale * log2(e) (* k_scale for fp8 pools)
+  float v_scale;                // fp8 pools: V element = v_scale * code; 1 otherwise
   void* out;
   float* lse_out;
 };
@@ -88,8 +89,10 @@ hipError_t launch_merge(int out_dtype, int head_dim, const float* o_parts,
                         const float* lse_parts, int32_t rows, int32_t n_parts, void* out,
                         float* lse_out, hipStream_t stream);
 
-hipError_t launch_prefill(int dtype, int head_dim, int group, const PrefillArgs& a,
-                          hipStream_t stream);
+// kv_dtype: element type of the pools (f16, bf16, or fp8 with q_dtype f16 /
+// bf16); q_dtype: of q and out.
+hipError_t launch_prefill(int kv_dtype, int q_dtype, int head_dim, int group,
+                          const PrefillArgs& a, hipStream_t stream);
 
 // Rows of query positions one prefill workgroup covers (per KV head group).
 int prefill_rows_per_tile(int group);

@@ -38,6 +38,16 @@
 // Keys past the causal limit or the sequence end are selected out of S; V
 // rows past the sequence end are zeroed in LDS before use, so stale or NaN
 // slots in a partly filled last page never reach the products.
+//
+// fp8 pools (OCP E4M3 / E5M2 with one fp32 scale per pool, queries f16 or
+// bf16; page 4, section 3.1 prefills in chunks over an e5m2 cache): a page
+// block is 2 KiB.  The wave that copies a page brings it into a staging
+// buffer of its own, waits for its own copy and widens the page exactly to
+// the query type into the same swizzled tile the 16-bit pools use (every fp8
+// value is exact in f16 and in bf16); from there the tile loop is the same.
+// Each element is widened once per workgroup, not once per wave that reads
+// it.  The K scale is folded into the softmax scale, the V scale into the
+// final normalisation.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -58,6 +68,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
@@ -115,10 +126,10 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, l
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)lds_base,
                                            16, voff, 0, 0, 0);
 }
-// Descriptor of one 4-KiB (page, head) block: base address, no stride, range
-// 4096 bytes, 32-bit data format.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const char* base) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, P * D * 2, 0x00020000);
+// Descriptor of one (page, head) block of `bytes` bytes (4 KiB at 16 bits, 2
+// KiB in fp8): base address, no stride, 32-bit data format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const char* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
 }
 
 // Transposing LDS read: in each group of 16 lanes, lane i receives element
@@ -129,14 +140,20 @@ __device__ __forceinline__ uint2 read_tr(const lds_u8* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
-template <typename TT, int G>
+// TT: type of q, out and the tiles' elements; CT: type of the pools (TT, or
+// an fp8 type).
+template <typename TT, typename CT, int G>
 __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   using M = Mfma<TT>;
+  constexpr bool F8 = CT::is_fp8;
+  constexpr int PAGEB = P * D * CT::bytes;  // bytes of one (page, head) block
   constexpr int NPOS = ROWS / G;  // chunk positions per workgroup
   __shared__ __align__(1024) uint8_t k_lds0[TILEB];
   __shared__ __align__(1024) uint8_t k_lds1[TILEB];
   __shared__ __align__(1024) uint8_t v_lds0[TILEB];
   __shared__ __align__(1024) uint8_t v_lds1[TILEB];
+  // fp8: one staging page per wave (the page it copies, before widening)
+  __shared__ __align__(1024) uint8_t stg[F8 ? NWP * PAGEB : 16];
   __shared__ int bad_flag;
 
   const int tid = threadIdx.x;
@@ -221,8 +238,10 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   // chunks of four rows; lane i of a chunk fills row 4j + i/16, physical
   // chunk i%16 with logical chunk (i%16) ^ swz(row).  The page, its
   // descriptor and the LDS destination are the same for the whole wave
-  // (scalar registers); each lane adds a fixed offset.
-  const int64_t head_block = (int64_t)P * D * 2;
+  // (scalar registers); each lane adds a fixed offset.  fp8: the page goes
+  // unpermuted into the wave's staging buffer as two 1-KiB chunks, and
+  // widen_page() fills the tile rows.
+  const int64_t head_block = (int64_t)PAGEB;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int wp = wu & 3;          // page of the tile this wave copies
   const bool kwave = wu < 4;      // waves 0-3 copy K pages, waves 4-7 V pages
@@ -246,11 +265,38 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
     if (pi < seq_pages && out) my_bad = true;
     return out ? 0 : pid;
   };
+  lds_u8* my_stg = (lds_u8*)(stg + (F8 ? wu * PAGEB : 0));
   auto copy_page = [&](const void* pool, int pid, lds_u8* dst) {
     const __amdgpu_buffer_rsrc_t r =
-        page_rsrc((const char*)pool + ((int64_t)pid * a.num_kv_heads + g) * head_block);
+        page_rsrc((const char*)pool + ((int64_t)pid * a.num_kv_heads + g) * head_block, PAGEB);
+    if constexpr (F8) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(r, dma_off[j], dst + (16 * wp + 4 * j) * ROWB);
+      for (int j = 0; j < PAGEB / 1024; ++j) dma16(r, (uint32_t)(j * 1024 + 16 * lane), my_stg + j * 1024);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma16(r, dma_off[j], dst + (16 * wp + 4 * j) * ROWB);
+    }
+  };
+  // fp8: widen the staged page (after this wave's own copy has landed) into
+  // rows 16wp .. 16wp+15 of tile dst: lane i takes the 8-element chunks
+  // i, i+64, i+128, i+192 of the page (row = chunk / 16, logical chunk =
+  // chunk % 16) and stores each at its swizzled place.
+  auto widen_page = [&](lds_u8* dst) {
+    if constexpr (F8) {
+#pragma unroll 1
+      for (int i = 0; i < 4; ++i) {
+        const int ch = lane + 64 * i, r = ch >> 4, lc = ch & 15;
+        const u32x2_t x = *reinterpret_cast<const u32x2_t __attribute__((address_space(3)))*>(
+            my_stg + r * (D * CT::bytes) + lc * 8);
+        u32x4_t y;
+        y[0] = CT::template cvt2<TT, false>(x[0]);
+        y[1] = CT::template cvt2<TT, true>(x[0]);
+        y[2] = CT::template cvt2<TT, false>(x[1]);
+        y[3] = CT::template cvt2<TT, true>(x[1]);
+        *reinterpret_cast<u32x4_t __attribute__((address_space(3)))*>(
+            dst + (16 * wp + r) * ROWB + ((lc ^ swz(r)) * 16)) = y;
+      }
+    }
   };
   // V rows of keys past the sequence end become zero (edge tiles only)
   auto zero_tail = [&](int it, uint8_t* vdst) {
@@ -457,6 +503,9 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
     pv_step(v1, pk[3]);
     l_run += ls;
     __builtin_amdgcn_s_waitcnt(0);
+    if constexpr (F8) {   // the page this wave copied above, if any
+      if (kwave ? (j + 2 < n_tiles) : (j + 1 < n_tiles)) widen_page(kwave ? kd : vd);
+    }
     __syncthreads();
   };
 
@@ -471,10 +520,24 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
     const int pid0 = check_pid(0, load_pid(0));
     if (kwave) {
       copy_page(a.k_cache, pid0, kb0);
-      if (n_tiles > 1) copy_page(a.k_cache, check_pid(1, load_pid(1)), kb1);
+      if constexpr (F8) {
+        __builtin_amdgcn_s_waitcnt(0);
+        widen_page(kb0);
+      }
+      if (n_tiles > 1) {
+        copy_page(a.k_cache, check_pid(1, load_pid(1)), kb1);
+        if constexpr (F8) {
+          __builtin_amdgcn_s_waitcnt(0);
+          widen_page(kb1);
+        }
+      }
       pid_f = load_pid(2);
     } else {
       copy_page(a.v_cache, pid0, vb0);
+      if constexpr (F8) {
+        __builtin_amdgcn_s_waitcnt(0);
+        widen_page(vb0);
+      }
       pid_f = load_pid(1);
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -507,7 +570,7 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   const float l_tot = l_run + xor_f(l_run, 32);
   if (!row_ok) return;
   const bool poison = bad_flag != 0;
-  const float inv = 1.f / l_tot;
+  const float inv = a.v_scale / l_tot;   // v_scale: 1 for 16-bit pools
   char* op = (char*)a.out + ((qrow * a.num_q_heads + head) * D) * 2;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -529,33 +592,45 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   }
 }
 
-template <typename TT>
+template <typename TT, typename CT>
 hipError_t launch_t(int group, const PrefillArgs& a, hipStream_t stream) {
   const int64_t blocks = (int64_t)a.batch * a.num_kv_heads *
                          (a.xcd_split ? 8 * (int64_t)a.m_tiles_x : (int64_t)a.m_tiles);
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)blocks), block(NWP * 64);
   switch (group) {
-    case 1: hipLaunchKernelGGL((prefill_kernel<TT, 1>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((prefill_kernel<TT, 2>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((prefill_kernel<TT, 4>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((prefill_kernel<TT, 8>), grid, block, 0, stream, a); break;
-    case 16: hipLaunchKernelGGL((prefill_kernel<TT, 16>), grid, block, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((prefill_kernel<TT, CT, 1>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<TT, CT, 2>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<TT, CT, 4>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((prefill_kernel<TT, CT, 8>), grid, block, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL((prefill_kernel<TT, CT, 16>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <typename TT>
+hipError_t launch_q(int kv_dtype, int group, const PrefillArgs& a, hipStream_t stream) {
+  switch (kv_dtype) {
+    case 1:
+    case 2: return launch_t<TT, TT>(group, a, stream);
+    case 3: return launch_t<TT, TFP8E4M3>(group, a, stream);
+    case 4: return launch_t<TT, TFP8E5M2>(group, a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 int prefill_rows_per_tile(int group) { return ROWS / group; }
 
-hipError_t launch_prefill(int dtype, int head_dim, int group, const PrefillArgs& a,
-                          hipStream_t stream) {
+hipError_t launch_prefill(int kv_dtype, int q_dtype, int head_dim, int group,
+                          const PrefillArgs& a, hipStream_t stream) {
   if (head_dim != D) return hipErrorInvalidValue;
-  switch (dtype) {
-    case 1: return launch_t<TF16>(group, a, stream);
-    case 2: return launch_t<TBF16>(group, a, stream);
+  if (kv_dtype != 3 && kv_dtype != 4 && kv_dtype != q_dtype) return hipErrorInvalidValue;
+  switch (q_dtype) {
+    case 1: return launch_q<TF16>(kv_dtype, group, a, stream);
+    case 2: return launch_q<TBF16>(kv_dtype, group, a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -76,6 +76,11 @@ CONFIGS: Dict[str, dict] = {
     "llama70b_128k_fp8": dict(kind="decode", seed=6, batch=8, hq=16, hkv=2, d=128,
                               dtype="f16", kv_dtype="fp8_e4m3", k_scale=0.0234375,
                               v_scale=0.01953125, ctx=131072, append=True),
+    # the prefill shape over fp8 e5m2 pools (page 4, section 3.1 serves with
+    # --kv-cache-dtype fp8_e5m2 and chunked prefill), bf16 queries
+    "prefill_fp8": dict(kind="prefill", seed=8, batch=4, hq=32, hkv=8, d=128, dtype="bf16",
+                        hist=32768, chunk=512, kv_dtype="fp8_e5m2", k_scale=0.0234375,
+                        v_scale=0.01953125),
 }
 
 
@@ -354,7 +359,8 @@ def make(name: str, seed: Optional[int] = None) -> Workload:
         b = cfg["batch"]
         return make_prefill(name, seed=seed, batch=b, hq=cfg["hq"], hkv=cfg["hkv"],
                             d=cfg["d"], dtype=cfg["dtype"], hist=[cfg["hist"]] * b,
-                            chunk=[cfg["chunk"]] * b, gen=gen)
+                            chunk=[cfg["chunk"]] * b, gen=gen, kv_dtype=cfg.get("kv_dtype"),
+                            k_scale=cfg.get("k_scale", 1.0), v_scale=cfg.get("v_scale", 1.0))
     b = cfg["batch"]
     if name == "tiny":
         hist = list(cfg["lens"])

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
     assert len(names) >= 10
     for n in names:
         assert hasattr(L, n), n
-    assert L.pkv_version() == 2
+    assert L.pkv_version() == 3
 
 
 def err(L):
@@ -259,8 +259,44 @@ def test_kv_append_quant_args(L):
 
 
 def test_fp8_elsewhere_rejected(L):
-    assert _prefill(L, desc(dtype=3)) == -2
+    assert _prefill(L, desc(dtype=3)) == -1      # fp8 pools need the _ex form's query type
     assert L.pkv_merge_states(FAKE, FAKE, 4, 2, 128, 3, FAKE, None, None) == -2
+
+
+def _prefill_ex(L, d, opts, *, batch=2, hq=4, total=10, max_q=8, stride=8, max_kv=100):
+    return L.pkv_paged_attn_prefill_chunk_ex(C.byref(d), FAKE, FAKE, FAKE, FAKE, batch, hq, total,
+                                             max_q, FAKE, stride, FAKE, max_kv, 0.125,
+                                             None if opts is None else C.byref(opts), FAKE, None,
+                                             None)
+
+
+def _mixed_ex(L, d, opts, *, batch=4, nd=2, total=10, max_q=8, stride=8, max_kv=100):
+    return L.pkv_paged_attn_mixed_ex(C.byref(d), FAKE, FAKE, FAKE, FAKE, batch, nd, 4, total,
+                                     max_q, FAKE, stride, FAKE, max_kv, 0.125, 0,
+                                     None if opts is None else C.byref(opts), FAKE, None, None, 0,
+                                     None)
+
+
+def test_prefill_and_mixed_ex_args(L):
+    f8, f16 = desc(dtype=3), desc(dtype=1)
+    ok = _opts(1, 0.5, 0.25)
+    # host checks pass; nothing to launch with no sequences or no rows
+    assert _prefill_ex(L, f8, ok, batch=0) == 0
+    assert _prefill_ex(L, desc(dtype=4), _opts(2, 0.5, 0.25), total=0) == 0
+    assert _mixed_ex(L, f8, ok, batch=0, nd=0) == 0
+    assert _prefill_ex(L, f16, None, batch=0) == 0            # NULL options: the plain call
+    assert _prefill_ex(L, f8, None, batch=0) == -1            # fp8 needs a query type
+    assert _prefill_ex(L, f8, _opts(3), batch=0) == -2        # fp8 queries are not built
+    assert _prefill_ex(L, f8, _opts(1, 0.0, 1.0), batch=0) == -1      # scales > 0
+    assert _prefill_ex(L, f8, _opts(1, 1.0, float("inf")), batch=0) == -1
+    assert _prefill_ex(L, f16, _opts(2), batch=0) == -1       # 16-bit pools: q_dtype = dtype
+    assert _prefill_ex(L, f16, _opts(1, 2.0, 1.0), batch=0) == -1     # scales: fp8 only
+    assert _prefill_ex(L, f8, _opts(1, 1.0, 1.0, 64, 0), batch=0) == -1   # no window here
+    assert _prefill_ex(L, f8, _opts(1, 1.0, 1.0, 0, 4), batch=0) == -1    # nor a sink
+    assert _mixed_ex(L, f8, _opts(1, 1.0, 1.0, 64, 0), batch=0, nd=0) == -1
+    assert _prefill_ex(L, desc(dtype=3, d=64), ok, batch=0) == -2     # head_dim 128 only
+    assert _prefill_ex(L, desc(dtype=0), _opts(0), batch=0) == -2     # f32: not on MFMA
+    assert _mixed_ex(L, f8, ok, nd=5) == -1                   # more decode rows than sequences
 
 
 def _mixed(L, d, *, batch=4, nd=2, total=10, max_q=8, stride=8, max_kv=100):
