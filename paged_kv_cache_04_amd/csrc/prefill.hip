@@ -42,7 +42,8 @@
 // fp8 pools (OCP E4M3 / E5M2 with one fp32 scale per pool, queries f16 or
 // bf16; page 4, section 3.1 prefills in chunks over an e5m2 cache): a page
 // block is 2 KiB.  The wave that copies a page brings it into a staging
-// buffer of its own, waits for its own copy and widens the page exactly to
+// buffer of its own and, halfway through the iteration (after its weights,
+// before its PV step), waits for its own copy and widens the page exactly to
 // the query type into the same swizzled tile the 16-bit pools use (every fp8
 // value is exact in f16 and in bf16); from there the tile loop is the same.
 // Each element is widened once per workgroup, not once per wave that reads
@@ -485,6 +486,16 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
       for (int g = 0; g < 4; ++g) weights(s_cur, g, mc2, pk[g], ls);
     }
     fence();
+    // fp8: widen the page this wave copied above, if any, once its copy has
+    // landed.  Its destination (K(j), read in iteration j-1, or V(j-1), read
+    // in that iteration's PV) is free since the last barrier, and it is read
+    // only after the next one; widening here overlaps the other waves' PV.
+    if constexpr (F8) {
+      if (kwave ? (j + 2 < n_tiles) : (j + 1 < n_tiles)) {
+        __builtin_amdgcn_s_waitcnt(0);
+        widen_page(kwave ? kd : vd);
+      }
+    }
     if (MASKED && j * BK + BK > kvl) {
       zero_tail(j, vc_raw);
       __syncthreads();
@@ -503,9 +514,6 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
     pv_step(v1, pk[3]);
     l_run += ls;
     __builtin_amdgcn_s_waitcnt(0);
-    if constexpr (F8) {   // the page this wave copied above, if any
-      if (kwave ? (j + 2 < n_tiles) : (j + 1 < n_tiles)) widen_page(kwave ? kd : vd);
-    }
     __syncthreads();
   };
 
