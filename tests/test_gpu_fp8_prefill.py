@@ -176,3 +176,17 @@ def test_fp8_prefill_zero_keys_and_constant_values():
                 want = mean[hist[b] + i].repeat_interleave(G, dim=0).numpy()
                 assert_close(out[row], want, "bf16", f"fp8 prefill zero K b{b} row {i}")
                 row += 1
+
+
+def test_fp8_prefill_bad_page_poisons_its_rows_only():
+    """A block-table entry outside the pool makes every row of its sequence
+    NaN (and its log-sum-exp NaN); the other sequence is untouched."""
+    w = W.make_prefill("f8bad", seed=29, batch=2, hq=16, hkv=2, d=128, dtype="bf16",
+                       hist=[200, 200], chunk=[40, 40], pool_slack=0.2, kv_dtype="fp8_e5m2",
+                       **SCALES)
+    d = to_dev(w, DEV)
+    gpu_append(w, d)
+    d["block_table"][1, 2] = w.num_pages + 3
+    out, lse = gpu_prefill(w, d)
+    assert torch.isfinite(out[:40].float()).all() and torch.isfinite(lse[:40]).all()
+    assert torch.isnan(out[40:].float()).all() and torch.isnan(lse[40:]).all()

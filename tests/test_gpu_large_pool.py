@@ -8,8 +8,9 @@ The compact pool's page p becomes page base + p of a pool of base + n pages
 0x7F) and are never read; tables and slots move with the pages.  Checked for
 the append (bytes, and nothing written below base), gather, decode on both
 kernels (unsplit and split, with and without a window), the fp8 cache with its
-quantizing append, chunked prefill and the mixed batch: bit for bit against
-the compact pool and within tolerance of the oracle."""
+quantizing append, chunked prefill (16-bit and fp8 pools) and the mixed
+batch: bit for bit against the compact pool and within tolerance of the
+oracle."""
 import pytest
 import torch
 
@@ -139,11 +140,12 @@ def test_decode_and_gather_past_4gib(qd, kvd, hq, hkv, lens):
         assert_lse_close(res[1][1].reshape(-1), ref_lse, w.dtype, what)
 
 
-@pytest.mark.parametrize("kind", ["prefill", "mixed"])
+@pytest.mark.parametrize("kind", ["prefill", "prefill fp8", "mixed"])
 def test_prefill_and_mixed_past_4gib(kind):
-    if kind == "prefill":
+    if kind.startswith("prefill"):
+        kw = dict(kv_dtype="fp8_e5m2", k_scale=3 / 128, v_scale=5 / 256) if "fp8" in kind else {}
         w = W.make_prefill("bigp", seed=132, batch=3, hq=32, hkv=8, d=128, dtype="bf16",
-                           hist=[0, 700, 2000], chunk=[300, 64, 129], pool_slack=0.05)
+                           hist=[0, 700, 2000], chunk=[300, 64, 129], pool_slack=0.05, **kw)
         nd = 0
     else:
         w = W.make_mixed("bigm", seed=133, hq=32, hkv=2, d=128, dtype="f16",
@@ -158,13 +160,14 @@ def test_prefill_and_mixed_past_4gib(kind):
     check_pools(w, d, e, base)
     max_q = max(w.meta["chunk_lens"])
     res = []
+    scales = dict(k_scale=w.k_scale, v_scale=w.v_scale)
     for x in (d, e):
-        if kind == "prefill":
+        if kind.startswith("prefill"):
             res.append(pkv.paged_attn_prefill_chunk(x["q"], x["k_cache"], x["v_cache"],
                                                     x["q_indptr"], x["block_table"],
                                                     x["context_lens"], max_q,
                                                     w.max_context_len, w.scale,
-                                                    return_lse=True))
+                                                    return_lse=True, **scales))
         else:
             res.append(pkv.paged_attn_mixed(x["q"], x["k_cache"], x["v_cache"], x["q_indptr"],
                                             x["block_table"], x["context_lens"], nd, max_q,
@@ -173,7 +176,8 @@ def test_prefill_and_mixed_past_4gib(kind):
     torch.cuda.synchronize()
     assert torch.equal(bits(res[0][0]), bits(res[1][0])), f"{kind}: out differs from compact"
     assert torch.equal(bits(res[0][1]), bits(res[1][1])), f"{kind}: lse differs from compact"
-    ref, ref_lse = pkvref.prefill(w.dtype, w.k_cache, w.v_cache, w.q, w.q_indptr, w.block_table,
-                                  w.context_lens, w.scale, n_threads=host_threads())
+    ref, ref_lse = pkvref.prefill_ex(w.dtype, w.kv_dtype, w.k_cache, w.v_cache, w.q, w.q_indptr,
+                                     w.block_table, w.context_lens, w.scale,
+                                     n_threads=host_threads(), **scales)
     assert_close(res[1][0].reshape(ref.shape), ref, w.dtype, kind)
     assert_lse_close(res[1][1].reshape(-1), ref_lse, w.dtype, kind)
