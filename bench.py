@@ -24,6 +24,8 @@ and a parity check of sampled rows against the oracle:
   fp8_decode     the 128K decode over fp8 (e4m3) pools (HBM GB/s)
   window_decode  the 128K decode with a 4096-key window and a 128-key sink
   mixed_batch    an 8192-token batch of decode rows and prefill chunks
+  shared_prefix  256 sequences sharing 2048 tokens of pages: the one-pass decode
+                 and the shared-prefix (cascade) decode, on logical and unique bytes
 """
 from __future__ import annotations
 
@@ -90,9 +92,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="lower bound on the CPU oracle sample's wall time")
-    ap.add_argument("--extras", default="prefill,fp8prefill,fp8,window,mixed",
+    ap.add_argument("--extras", default="prefill,fp8prefill,fp8,window,mixed,prefix",
                     help="comma-separated extra rows to measure: prefill, fp8prefill, fp8, "
-                         "window, mixed ('' or 'none' for none)")
+                         "window, mixed, prefix ('' or 'none' for none)")
     ap.add_argument("--prefill", action="store_true", help="same as --extras prefill")
     ap.add_argument("--graph", action="store_true",
                     help="time the steps as HIP graph replays instead of eager launches")
@@ -306,6 +308,8 @@ def main():
         line["fp8_decode"] = bench_fp8(args, dev, sample)
     if "mixed" in extras:
         line["mixed_batch"] = bench_mixed(args, dev, sample)
+    if "prefix" in extras:
+        line["shared_prefix"] = bench_shared_prefix(args, dev, sample)
 
     print(json.dumps(line), flush=True)
 
@@ -632,6 +636,75 @@ def bench_window(args, dev, sample, reuse=None):
                                   n_threads=host_cores())
         got = out.float().cpu().double().numpy().reshape(-1, w.head_dim)[rows]
         res["parity"] = _parity(got, ref, w.dtype)
+    return res
+
+
+def bench_shared_prefix(args, dev, sample):
+    progress("shared_prefix")
+    import torch
+
+    import paged_kv_cache_04_amd as pkv
+    from paged_kv_cache_04_amd import accounting as A
+    from paged_kv_cache_04_amd import workloads as W
+
+    w = W.make("prefix")
+    kc, vc = w.k_cache.to(dev), w.v_cache.to(dev)
+    q, bt, cl = w.q.to(dev), w.block_table.to(dev), w.context_lens.to(dev)
+    prefix = w.meta["shared_prefix"]
+    pp = prefix // w.page_size
+    prefix_table = bt[0, :pp].contiguous()
+    own = bt[:, pp:]
+    suffix_lens = (cl - prefix).contiguous()
+    max_suffix = w.max_context_len - prefix
+    desc = pkv.cache_desc(kc)
+    n_parts, ws_bytes = pkv.shared_prefix_plan(desc, w.batch, w.num_q_heads, prefix, max_suffix)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    out1 = torch.empty_like(q)
+    n1, ws1_bytes = pkv.decode_plan(desc, w.batch, w.num_q_heads, w.max_context_len, 0)
+    ws1 = torch.empty(max(ws1_bytes, 16), dtype=torch.uint8, device=dev)
+
+    def one_pass():
+        pkv.paged_attn_decode(q, kc, vc, bt, cl, w.max_context_len, w.scale, out=out1,
+                              workspace=ws1)
+
+    def cascade():
+        pkv.paged_attn_decode_shared_prefix(q, kc, vc, prefix_table, prefix, own, suffix_lens,
+                                            max_suffix, w.scale, out=out, workspace=ws)
+
+    lens = w.context_lens.tolist()
+    logical = A.decode_kv_bytes(lens, w.num_kv_heads, w.head_dim, w.dtype)
+    unique = A.decode_kv_bytes([prefix] + [L - prefix for L in lens], w.num_kv_heads,
+                               w.head_dim, w.dtype)
+    one_us, _ = _event_times(one_pass, 30, warmup=5)
+    cas_us, cas_med = _event_times(cascade, 30, warmup=5)
+    cold_us = _cold_event_us(cascade, 10)
+    res = {"workload": "256 sequences sharing 2048 tokens (128 physical pages in every table) "
+                       "+ U{32..512} own tokens, 32 q / 8 kv heads, head_dim 128, bf16 (page 2, "
+                       "section 3.2: identical prefixes share physical pages)",
+           "logical_kv_bytes": int(logical), "unique_kv_bytes": int(unique),
+           "one_pass_decode": {"call_us": round(one_us, 2), "n_split": n1,
+                               "tokens_per_s": round(w.batch / (one_us * 1e-6), 1),
+                               "logical_gbps": round(logical / (one_us * 1e-6) / 1e9, 1),
+                               "unique_gbps": round(unique / (one_us * 1e-6) / 1e9, 1)},
+           "cascade": {"call_us": round(cas_us, 2), "call_median_us": round(cas_med, 2),
+                       "n_parts": n_parts,
+                       "tokens_per_s": round(w.batch / (cas_us * 1e-6), 1),
+                       "logical_gbps": round(logical / (cas_us * 1e-6) / 1e9, 1),
+                       "cold_call_us": round(cold_us, 2)},
+           # the cascade reads each unique byte once: its roofline is HBM on unique bytes
+           "roofline": _hbm_roofline("shared-prefix decode (3 launches: shared pages on MFMA, "
+                                     "own pages split-KV, merge)", unique, cas_us)}
+    if sample:
+        from oracle import pkvref
+        torch.cuda.synchronize()
+        rows = [b * w.num_q_heads + h for b in range(0, w.batch, 16) for h in (0, 31)]
+        ref, _ = pkvref.decode(w.dtype, w.k_cache, w.v_cache, w.q, w.block_table,
+                               w.context_lens, w.scale, rows=rows, n_threads=host_cores())
+        got = out.float().cpu().double().numpy().reshape(-1, w.head_dim)[rows]
+        res["parity"] = _parity(got, ref, w.dtype)
+    del kc, vc
+    torch.cuda.empty_cache()
     return res
 
 

@@ -395,6 +395,55 @@ int pkv_paged_attn_mixed_ex(const pkv_cache_desc* desc, const void* k_cache,
                             void* stream);
 
 /*
+ * decode_shared_prefix_plan -- the partial count and workspace of
+ * paged_attn_decode_shared_prefix for these sizes (host only, no HIP call).
+ * *n_parts = key splits of the shared pages + splits of the own pages (the
+ * latter as pkv_decode_plan_ex would pick them for max_suffix_len);
+ * *workspace_bytes > 0 whenever batch > 0.
+ */
+int pkv_decode_shared_prefix_plan(const pkv_cache_desc* desc, int32_t batch, int32_t num_q_heads,
+                                  int32_t prefix_len, int32_t max_suffix_len,
+                                  int32_t split_tokens, const pkv_decode_opts* opts,
+                                  int32_t* n_parts, size_t* workspace_bytes);
+
+/*
+ * paged_attn_decode_shared_prefix -- decode for a batch whose sequences all
+ * begin with the same physical pages (page 2, section 3.2: identical prompt
+ * prefixes share physical pages; page 4, section 3.3: shared prefixes are
+ * reused from the cache automatically).  The
+ * result is that of paged_attn_decode_ex over, for sequence b, the table
+ * prefix_table ++ block_table[b] and prefix_len + suffix_lens[b] keys; it is
+ * computed as a cascade: the shared pages are read once for the whole batch
+ * (every sequence's query rows against them on the matrix cores, split over
+ * the keys), each sequence's own pages by the split-KV decode, and all
+ * partial results are combined by the log-sum-exp merge (rounding differs
+ * from the one-pass decode; the result is within the same tolerance).
+ *   q, out        : device [batch][H_q][D] of the query type; 16-byte aligned.
+ *   prefix_table  : device int32 [prefix_len / P], the shared pages in order;
+ *                   may be NULL when prefix_len == 0.
+ *   prefix_len    : >= 0, a multiple of P (shared pages are whole pages;
+ *                   PKV_ERR_INVALID otherwise).
+ *   block_table, block_table_stride : device int32 [batch][stride], the pages
+ *                   of each sequence after the shared ones.
+ *   suffix_lens   : device int32 [batch], keys of each sequence after the
+ *                   shared ones (0 allowed); max_suffix_len a host bound, as
+ *                   max_context_len of paged_attn_decode.
+ *   opts          : as for paged_attn_decode_ex (query type, fp8 scales);
+ *                   window and sink must be 0.  NULL: the cache type.
+ *   workspace     : >= the workspace_bytes of decode_shared_prefix_plan,
+ *                   16-byte aligned; holds fp32 partials [batch*H_q][n_parts]
+ *                   [D] and their log-sum-exps.
+ * Pools: f16, bf16 or fp8 (e4m3 / e5m2); head_dim 128; G as for decode.
+ * Three launches on `stream`; no synchronisation.
+ */
+int pkv_paged_attn_decode_shared_prefix(
+    const pkv_cache_desc* desc, const void* k_cache, const void* v_cache, const void* q,
+    int32_t batch, int32_t num_q_heads, const int32_t* prefix_table, int32_t prefix_len,
+    const int32_t* block_table, int32_t block_table_stride, const int32_t* suffix_lens,
+    int32_t max_suffix_len, float scale, int32_t split_tokens, const pkv_decode_opts* opts,
+    void* out, float* lse_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * validate_tables -- host-side check of host copies of the tables (no HIP
  * call): every entry a sequence uses (the first ceil(lens[b]/P) of its row)
  * is in [0, num_pages); 0 <= lens[b] <= stride * P; every slot is < 0 or in

@@ -18,7 +18,9 @@ from .binding import (  # noqa: F401
     merge_states,
     paged_attn_decode,
     paged_attn_decode_partials,
+    paged_attn_decode_shared_prefix,
     paged_attn_mixed,
     paged_attn_prefill_chunk,
+    shared_prefix_plan,
     validate_tables,
 )

@@ -83,13 +83,19 @@ def lib():
                                                       vp, i32, vp, i32, f32, op, vp, vp, vp]
         L.pkv_paged_attn_mixed_ex.argtypes = [dp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp,
                                               i32, vp, i32, f32, i32, op, vp, vp, vp, sz, vp]
+        L.pkv_decode_shared_prefix_plan.argtypes = [dp, i32, i32, i32, i32, i32, op,
+                                                    C.POINTER(i32), C.POINTER(sz)]
+        L.pkv_paged_attn_decode_shared_prefix.argtypes = [dp, vp, vp, vp, i32, i32, vp, i32, vp,
+                                                          i32, vp, i32, f32, i32, op, vp, vp, vp,
+                                                          sz, vp]
         for name in ("pkv_kv_append", "pkv_gather_kv", "pkv_decode_plan", "pkv_paged_attn_decode",
                      "pkv_paged_attn_decode_partials", "pkv_merge_states",
                      "pkv_paged_attn_prefill_chunk", "pkv_validate_tables",
                      "pkv_decode_plan_ex", "pkv_paged_attn_decode_ex",
                      "pkv_paged_attn_decode_partials_ex", "pkv_kv_append_quant",
                      "pkv_paged_attn_mixed", "pkv_decode_split_for_lens",
-                     "pkv_paged_attn_prefill_chunk_ex", "pkv_paged_attn_mixed_ex"):
+                     "pkv_paged_attn_prefill_chunk_ex", "pkv_paged_attn_mixed_ex",
+                     "pkv_decode_shared_prefix_plan", "pkv_paged_attn_decode_shared_prefix"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -403,6 +409,62 @@ def paged_attn_mixed(q, k_cache, v_cache, q_indptr, block_table, kv_lens, num_de
         _check(lib().pkv_paged_attn_mixed(*args, *tail))
     else:
         _check(lib().pkv_paged_attn_mixed_ex(*args, C.byref(opts), *tail))
+    return (out, lse_out) if return_lse else out
+
+
+def shared_prefix_plan(desc: CacheDesc, batch: int, num_q_heads: int, prefix_len: int,
+                       max_suffix_len: int, split_tokens: int = 0,
+                       opts: Optional[DecodeOpts] = None) -> Tuple[int, int]:
+    """pkv_decode_shared_prefix_plan: (n_parts, workspace_bytes)."""
+    n = C.c_int32(0)
+    ws = C.c_size_t(0)
+    _check(lib().pkv_decode_shared_prefix_plan(C.byref(desc), int(batch), int(num_q_heads),
+                                               int(prefix_len), int(max_suffix_len),
+                                               int(split_tokens),
+                                               None if opts is None else C.byref(opts),
+                                               C.byref(n), C.byref(ws)))
+    return n.value, ws.value
+
+
+def paged_attn_decode_shared_prefix(q, k_cache, v_cache, prefix_table, prefix_len: int,
+                                    block_table, suffix_lens, max_suffix_len: int, scale: float,
+                                    split_tokens: int = 0, out=None, lse_out=None,
+                                    workspace=None, return_lse: bool = False,
+                                    k_scale: float = 1.0, v_scale: float = 1.0):
+    """pkv_paged_attn_decode_shared_prefix: decode of a batch whose sequences
+    all begin with the pages of prefix_table (prefix_len keys, whole pages);
+    block_table [B][*] (row stride taken from the tensor, so a column slice of
+    a full table works) and suffix_lens [B] describe each sequence's own
+    pages.  Returns out [B][H_q][D] (and lse [B][H_q])."""
+    desc = _check_pools(k_cache, v_cache)
+    _query_type(q, k_cache)
+    if q.dim() != 3 or q.shape[2] != desc.head_dim:
+        raise ValueError("q must be [B][H_q][D]")
+    batch, hq = int(q.shape[0]), int(q.shape[1])
+    _dev(prefix_table, "prefix_table", torch.int32)
+    _dev(suffix_lens, "suffix_lens", torch.int32)
+    if (not isinstance(block_table, torch.Tensor) or block_table.device.type != "cuda"
+            or block_table.dtype != torch.int32 or block_table.dim() != 2
+            or block_table.shape[0] != batch or block_table.stride(1) != 1):
+        raise ValueError("block_table must be a CUDA int32 [B][*] tensor with contiguous rows")
+    if suffix_lens.shape != (batch,):
+        raise ValueError("suffix_lens must be [B]")
+    opts = decode_opts(q.dtype, k_cache.dtype, k_scale, v_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse_out is None:
+        lse_out = torch.empty((batch, hq), dtype=torch.float32, device=q.device)
+    _, ws_bytes = shared_prefix_plan(desc, batch, hq, prefix_len, max_suffix_len, split_tokens,
+                                     opts)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    ws_len = workspace.numel() * workspace.element_size()
+    _check(lib().pkv_paged_attn_decode_shared_prefix(
+        C.byref(desc), _p(k_cache), _p(v_cache), _p(q), batch, hq, _p(prefix_table),
+        int(prefix_len), _p(block_table), int(block_table.stride(0)), _p(suffix_lens),
+        int(max_suffix_len), float(scale), int(split_tokens),
+        None if opts is None else C.byref(opts), _p(out), _p(lse_out), _p(workspace), ws_len,
+        _stream()))
     return (out, lse_out) if return_lse else out
 
 

@@ -184,8 +184,8 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_mfma_kernel(DecodeArgs a) {
         store_elem<QT>(a.out, row * D + d, o);
         if (d == 0 && a.lse_out) a.lse_out[row] = lse;
       } else {
-        a.o_part[(row * a.n_split + ks) * D + d] = o;
-        if (d == 0) a.lse_part[row * a.n_split + ks] = lse;
+        a.o_part[(row * a.part_stride + a.part_offset + ks) * D + d] = o;
+        if (d == 0) a.lse_part[row * a.part_stride + a.part_offset + ks] = lse;
       }
     }
     return;
@@ -487,8 +487,8 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_mfma_kernel(DecodeArgs a) {
       store_elem<QT>(a.out, row * D + d, out);
       if (d == 0 && a.lse_out) a.lse_out[row] = lse;
     } else {
-      a.o_part[(row * a.n_split + ks) * D + d] = out;
-      if (d == 0) a.lse_part[row * a.n_split + ks] = lse;
+      a.o_part[(row * a.part_stride + a.part_offset + ks) * D + d] = out;
+      if (d == 0) a.lse_part[row * a.part_stride + a.part_offset + ks] = lse;
     }
   }
 }

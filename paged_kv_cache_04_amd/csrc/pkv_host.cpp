@@ -366,6 +366,8 @@ pkv::DecodeArgs decode_args(const pkv_cache_desc* desc, const void* k_cache,
   a.v_scale = dc.opts.v_scale;
   a.window = dc.opts.window;
   a.sink = dc.opts.sink;
+  a.part_stride = plan.n_split;
+  a.part_offset = 0;
   return a;
 }
 
@@ -881,6 +883,170 @@ int pkv_paged_attn_mixed_ex(const pkv_cache_desc* desc, const void* k_cache,
                     total_q_rows, max_q_len, block_table, block_table_stride, kv_lens,
                     max_kv_len, scale, split_tokens, opts, out, lse_out, workspace,
                     workspace_bytes, stream);
+}
+
+namespace {
+
+// Shared-prefix (cascade) decode: the plan of its three launches.
+struct CascadePlan {
+  int group;
+  pkv_decode_opts opts;
+  Plan suffix;            // split-KV decode over each sequence's own pages
+  int32_t n_prefix;       // key splits of the shared pages (0: no shared pages)
+  int32_t split_tiles;    // 64-key tiles per split
+  int32_t m_tiles;        // query-row tiles of the batch
+  int32_t n_parts;        // n_prefix + suffix.n_split partials per row
+  size_t o_bytes;         // partial outputs, rounded up to 256
+  size_t ws_bytes;
+};
+
+constexpr int64_t kPrefixWorkgroups = 256;   // one per CU: one round of residency
+constexpr int64_t kPrefixMinTiles = 4;       // 256 keys per split at least
+
+int cascade_plan(const pkv_cache_desc* desc, int32_t batch, int32_t num_q_heads,
+                 int32_t prefix_len, int32_t max_suffix_len, int32_t split_tokens,
+                 const pkv_decode_opts* opts, CascadePlan* cp) {
+  if (int rc = check_desc(desc)) return rc;
+  if (int rc = resolve_opts(desc, opts, &cp->opts)) return rc;
+  if (int rc = check_heads(desc, num_q_heads, &cp->group)) return rc;
+  if (int rc = check_decode_group(desc, cp->opts.q_dtype, cp->group)) return rc;
+  if (desc->dtype != PKV_F16 && desc->dtype != PKV_BF16 && !is_fp8(desc->dtype))
+    return fail(PKV_ERR_UNSUPPORTED,
+                "the shared pages run on the matrix cores: f16, bf16 or fp8 pools only");
+  if (desc->head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "shared-prefix decode is built for head_dim 128 (got %d)",
+                desc->head_dim);
+  if (cp->opts.window != 0 || cp->opts.sink != 0)
+    return fail(PKV_ERR_INVALID, "window and sink do not apply to the shared-prefix decode");
+  if (batch < 0) return fail(PKV_ERR_INVALID, "batch %d < 0", batch);
+  if (prefix_len < 0 || prefix_len % desc->page_size != 0)
+    return fail(PKV_ERR_INVALID, "prefix_len %d: whole shared pages (a multiple of %d) expected",
+                prefix_len, desc->page_size);
+  if (max_suffix_len < 0) return fail(PKV_ERR_INVALID, "max_suffix_len %d < 0", max_suffix_len);
+  if (int rc = make_plan(desc, batch, num_q_heads, max_suffix_len, split_tokens,
+                         cp->opts.q_dtype, &cp->suffix))
+    return rc;
+  const int rows_per_tile = pkv::prefill_rows_per_tile(cp->group);
+  cp->m_tiles = (batch + rows_per_tile - 1) / rows_per_tile;
+  cp->n_prefix = 0;
+  cp->split_tiles = 0;
+  if (prefix_len > 0 && batch > 0) {
+    const int64_t tiles = (prefix_len + 63) / 64;
+    const int64_t units = (int64_t)desc->num_kv_heads * cp->m_tiles;
+    int64_t want = (kPrefixWorkgroups + units - 1) / units;
+    const int64_t cap = tiles / kPrefixMinTiles > 0 ? tiles / kPrefixMinTiles : 1;
+    if (want > cap) want = cap;
+    if (want < 1) want = 1;
+    const int64_t st = (tiles + want - 1) / want;
+    cp->split_tiles = (int32_t)st;
+    cp->n_prefix = (int32_t)((tiles + st - 1) / st);
+  }
+  cp->n_parts = cp->n_prefix + cp->suffix.n_split;
+  const size_t rows = (size_t)batch * num_q_heads;
+  const size_t ob = rows * (size_t)cp->n_parts * desc->head_dim * sizeof(float);
+  cp->o_bytes = (ob + 255) & ~(size_t)255;
+  cp->ws_bytes = cp->o_bytes + rows * (size_t)cp->n_parts * sizeof(float);
+  const int64_t blocks = (int64_t)desc->num_kv_heads * cp->m_tiles * cp->n_prefix;
+  if (blocks > 0x7fffffff) return fail(PKV_ERR_INVALID, "grid too large");
+  return PKV_OK;
+}
+
+}  // namespace
+
+int pkv_decode_shared_prefix_plan(const pkv_cache_desc* desc, int32_t batch, int32_t num_q_heads,
+                                  int32_t prefix_len, int32_t max_suffix_len,
+                                  int32_t split_tokens, const pkv_decode_opts* opts,
+                                  int32_t* n_parts, size_t* workspace_bytes) {
+  CascadePlan cp;
+  if (int rc = cascade_plan(desc, batch, num_q_heads, prefix_len, max_suffix_len, split_tokens,
+                            opts, &cp))
+    return rc;
+  if (!n_parts || !workspace_bytes) return fail(PKV_ERR_INVALID, "NULL output pointer");
+  *n_parts = cp.n_parts;
+  *workspace_bytes = cp.ws_bytes;
+  return ok();
+}
+
+int pkv_paged_attn_decode_shared_prefix(
+    const pkv_cache_desc* desc, const void* k_cache, const void* v_cache, const void* q,
+    int32_t batch, int32_t num_q_heads, const int32_t* prefix_table, int32_t prefix_len,
+    const int32_t* block_table, int32_t block_table_stride, const int32_t* suffix_lens,
+    int32_t max_suffix_len, float scale, int32_t split_tokens, const pkv_decode_opts* opts,
+    void* out, float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
+  CascadePlan cp;
+  if (int rc = cascade_plan(desc, batch, num_q_heads, prefix_len, max_suffix_len, split_tokens,
+                            opts, &cp))
+    return rc;
+  // the own-pages part is a split-KV decode: its argument checks
+  DecodeCommon dc;
+  if (int rc = check_decode(desc, k_cache, v_cache, q, batch, num_q_heads, block_table,
+                            block_table_stride, suffix_lens, max_suffix_len, scale,
+                            split_tokens, opts, &dc))
+    return rc;
+  if (batch == 0) return ok();
+  if (!out) return fail(PKV_ERR_INVALID, "out is NULL");
+  if (prefix_len > 0 && !prefix_table) return fail(PKV_ERR_INVALID, "prefix_table is NULL");
+  if (!aligned16(out)) return fail(PKV_ERR_INVALID, "out must be 16-byte aligned");
+  if (!workspace || workspace_bytes < cp.ws_bytes)
+    return fail(PKV_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, cp.ws_bytes);
+  if (!aligned16(workspace)) return fail(PKV_ERR_INVALID, "workspace must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  const int32_t prefix_pages = prefix_len / desc->page_size;
+  if (check_mode()) {
+    if (int rc = debug_check_decode(desc, block_table, block_table_stride, suffix_lens, batch,
+                                    max_suffix_len, 0, 0, s))
+      return rc;
+    std::vector<int32_t> pt;
+    if (int rc = fetch_i32(prefix_table, prefix_pages, &pt, s)) return rc;
+    if (int rc = check_pages(desc, pt, prefix_pages, 0, 0, prefix_pages, "prefix")) return rc;
+  }
+  float* o_part = (float*)workspace;
+  float* lse_part = (float*)((char*)workspace + cp.o_bytes);
+  const pkv_decode_opts& o = cp.opts;
+  if (cp.n_prefix > 0) {
+    // the shared pages: every sequence's query rows against them, split over keys
+    pkv::PrefillArgs a{};
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.q = q;
+    a.block_table = prefix_table;
+    a.num_pages = desc->num_pages;
+    a.stride = prefix_pages;
+    a.num_kv_heads = desc->num_kv_heads;
+    a.num_q_heads = num_q_heads;
+    a.batch = 1;
+    a.max_q_len = batch;
+    a.total_q = batch;
+    a.m_tiles = cp.m_tiles;
+    a.xcd_split = 0;
+    a.m_tiles_x = (cp.m_tiles + 7) / 8;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634 * (double)o.k_scale);
+    a.v_scale = o.v_scale;
+    a.kv_len0 = prefix_len;
+    a.n_ksplit = cp.n_prefix;
+    a.split_tiles = cp.split_tiles;
+    a.o_part = o_part;
+    a.lse_part = lse_part;
+    a.part_stride = cp.n_parts;
+    if (int rc = hip_status(pkv::launch_prefill(desc->dtype, o.q_dtype, desc->head_dim,
+                                                cp.group, a, s),
+                            "shared-prefix launch"))
+      return rc;
+  }
+  // each sequence's own pages: split-KV partials after the shared ones
+  pkv::DecodeArgs a = decode_args(desc, k_cache, v_cache, q, num_q_heads, block_table,
+                                  block_table_stride, suffix_lens, scale, dc);
+  a.direct = 0;
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  a.part_stride = cp.n_parts;
+  a.part_offset = cp.n_prefix;
+  if (int rc = hip_status(launch_any_decode(desc, o.q_dtype, dc.group, batch, a, s),
+                          "decode launch"))
+    return rc;
+  return hip_status(pkv::launch_merge(o.q_dtype, desc->head_dim, o_part, lse_part,
+                                      batch * num_q_heads, cp.n_parts, out, lse_out, s),
+                    "merge launch");
 }
 
 int pkv_validate_tables(const pkv_cache_desc* desc, const int32_t* block_table_host,

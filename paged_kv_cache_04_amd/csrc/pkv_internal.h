@@ -30,8 +30,10 @@ struct DecodeArgs {
   int32_t direct;               // 1: final output to out/lse_out; 0: partials
   void* out;                    // [B][H_q][D] (direct)
   float* lse_out;               // [B][H_q] or null (direct)
-  float* o_part;                // [B*H_q][n_split][D] (partials)
-  float* lse_part;              // [B*H_q][n_split]  (partials)
+  float* o_part;                // [B*H_q][part_stride][D] (partials), split ks at part
+  float* lse_part;              // [B*H_q][part_stride]    part_offset + ks
+  int32_t part_stride;          // parts per row (n_split unless other parts share the rows)
+  int32_t part_offset;
 };
 
 struct PrefillArgs {
@@ -55,6 +57,18 @@ struct PrefillArgs {
   float v_scale;                // fp8 pools: V element = v_scale * code; 1 otherwise
   void* out;
   float* lse_out;
+  // Shared-prefix form, chosen by o_part != null (all zero / null for a
+  // chunked prefill): one sequence (batch 1; q_indptr and kv_lens unused) of
+  // total_q query rows over kv_len0 keys, every row seeing every key, the
+  // keys cut into n_ksplit splits of split_tiles 64-key tiles; fp32 partials
+  // [row][part_stride][D] (row = query row * H_q + head) in o_part and
+  // lse_part [row][part_stride], at part ks of each row, instead of out.
+  int32_t kv_len0;
+  int32_t n_ksplit;
+  int32_t split_tiles;
+  float* o_part;
+  float* lse_part;
+  int32_t part_stride;
 };
 
 // Each launcher validates nothing: the host layer has done it.

@@ -49,6 +49,14 @@
 // Each element is widened once per workgroup, not once per wave that reads
 // it.  The K scale is folded into the softmax scale, the V scale into the
 // final normalisation.
+//
+// Shared-prefix form (the first pass of a cascade decode): the decode queries
+// of many sequences that share their first pages (page 2, section 3.2:
+// identical prompt prefixes share physical pages) form one "sequence" of
+// query rows; every row sees every key of the shared pages (no causal mask),
+// the keys are cut into splits so that enough workgroups run, and each split
+// writes fp32 partial results (out / l and the log-sum-exp) for the same
+// log-sum-exp merge that combines split-KV decode partials.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -142,8 +150,9 @@ __device__ __forceinline__ uint2 read_tr(const lds_u8* p) {
 }
 
 // TT: type of q, out and the tiles' elements; CT: type of the pools (TT, or
-// an fp8 type).
-template <typename TT, typename CT, int G>
+// an fp8 type); PFX: the shared-prefix form (one sequence, no causal mask,
+// key splits, fp32 partials) instead of a chunked prefill.
+template <typename TT, typename CT, int G, bool PFX>
 __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   using M = Mfma<TT>;
   constexpr bool F8 = CT::is_fp8;
@@ -174,12 +183,17 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   // start together instead of queueing, alternately with short ones, behind
   // chains of short workgroups on the same CUs.
   const int nbg = a.batch * a.num_kv_heads;
-  int bg, mt;
+  int bg, mt, ks = 0;
   if (a.xcd_split) {
     const int x = blockIdx.x % 8, j = blockIdx.x / 8;
     bg = j / a.m_tiles_x;
     mt = x * a.m_tiles_x + j % a.m_tiles_x;
     if (mt >= a.m_tiles) return;     // padding of the last XCD's range
+  } else if constexpr (PFX) {        // key split next, so a split's row tiles share L2
+    bg = blockIdx.x % nbg;
+    const int id = blockIdx.x / nbg;
+    ks = id % a.n_ksplit;
+    mt = id / a.n_ksplit;
   } else {
     bg = blockIdx.x % nbg;
     mt = blockIdx.x / nbg;
@@ -188,21 +202,25 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   const int g = bg % a.num_kv_heads;
 
   // sequence geometry, with broken preconditions clamped and flagged
-  const int q0 = a.q_indptr[b];
-  int C = a.q_indptr[b + 1] - q0;
-  int kvl = a.kv_lens[b];
+  const int q0 = PFX ? 0 : a.q_indptr[b];
+  int C = PFX ? (int)a.total_q : a.q_indptr[b + 1] - q0;
+  int kvl = PFX ? a.kv_len0 : a.kv_lens[b];
+  const int kv_min = PFX ? 0 : C;   // causal rows are the last C keys
   bool bad = false;
-  if (C < 0 || C > a.max_q_len || kvl < C || kvl > a.stride * P || q0 < 0) {
+  if (C < 0 || C > a.max_q_len || kvl < kv_min || kvl > a.stride * P || q0 < 0) {
     bad = true;
     C = max(0, min(C, a.max_q_len));
-    kvl = max(C, min(kvl, a.stride * P));
+    kvl = max(kv_min, min(kvl, a.stride * P));
   }
   const int pos0 = mt * NPOS;
   if (pos0 >= C) return;  // this tile of positions is past the chunk
   const int npos = min(NPOS, C - pos0);
   const int hist = kvl - C;
-  const int n_keys = hist + pos0 + npos;            // keys seen by the last row here
-  const int n_tiles = (n_keys + BK - 1) / BK;
+  // keys seen by the last row here; the tiles of this key split
+  const int n_keys = PFX ? kvl : hist + pos0 + npos;
+  const int tile0 = PFX ? ks * a.split_tiles : 0;
+  const int tiles_all = (n_keys + BK - 1) / BK;
+  const int n_tiles = PFX ? max(0, min(tiles_all, tile0 + a.split_tiles) - tile0) : tiles_all;
   const int seq_pages = (kvl + P - 1) / P;
   const int32_t* bt_row = a.block_table + (int64_t)b * a.stride;
 
@@ -212,7 +230,23 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   const int head = g * G + row % G;
   const int64_t qrow = (int64_t)q0 + pos;
   const bool row_ok = (row / G) < npos && qrow >= 0 && qrow < a.total_q;
-  const int apos = hist + pos;                       // last key this row sees
+  const int apos = PFX ? kvl - 1 : hist + pos;   // last key this row sees
+
+  if (PFX && n_tiles == 0) {   // an empty key split: o = 0, lse = -inf
+    if (row_ok) {
+      const int64_t prow = (qrow * a.num_q_heads + head) * a.part_stride + ks;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float z = bad ? __builtin_nanf("") : 0.f;
+          *reinterpret_cast<float4*>(a.o_part + prow * D + 32 * db + 8 * j + 4 * half) =
+              make_float4(z, z, z, z);
+        }
+      if (half == 0) a.lse_part[prow] = bad ? __builtin_nanf("") : -INFINITY;
+    }
+    return;
+  }
 
   // Q^T operand: 8 k-steps of 16 head dims; lane holds 8 consecutive dims
   u32x4_t qreg[8];
@@ -255,13 +289,13 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   bool my_bad = false;
   // block-table entry of this wave's page of tile t (0 past the sequence)
   auto load_pid = [&](int t) -> int {
-    const int pi = t * (BK / P) + wp;
+    const int pi = (tile0 + t) * (BK / P) + wp;
     return (t < n_tiles && pi < seq_pages) ? bt_row[pi] : 0;
   };
   // wave-uniform page id, flagged and replaced by page 0 when out of range
   auto check_pid = [&](int t, int loaded) -> int {
     const int pid = __builtin_amdgcn_readfirstlane(loaded);
-    const int pi = t * (BK / P) + wp;
+    const int pi = (tile0 + t) * (BK / P) + wp;
     const bool out = pid < 0 || pid >= a.num_pages;
     if (pi < seq_pages && out) my_bad = true;
     return out ? 0 : pid;
@@ -301,7 +335,7 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   };
   // V rows of keys past the sequence end become zero (edge tiles only)
   auto zero_tail = [&](int it, uint8_t* vdst) {
-    const int first = kvl - it * BK;   // first row to clear
+    const int first = kvl - (tile0 + it) * BK;   // first row to clear
     for (int idx = tid; idx < BK * (ROWB / 16); idx += NWP * 64) {
       const int r = idx / (ROWB / 16);
       if (r >= first)
@@ -367,7 +401,7 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   };
   // keys past this row's position (or the sequence end) are selected out
   auto mask_tile = [&](int it, f32x16_t (&s)[2]) {
-    const int thr = min(apos, kvl - 1) - it * BK - 4 * half;
+    const int thr = min(apos, kvl - 1) - (tile0 + it) * BK - 4 * half;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -496,7 +530,7 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
         widen_page(kwave ? kd : vd);
       }
     }
-    if (MASKED && j * BK + BK > kvl) {
+    if (MASKED && (tile0 + j) * BK + BK > kvl) {
       zero_tail(j, vc_raw);
       __syncthreads();
     }
@@ -553,7 +587,9 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
     s_tile(kb0, s0);
     __syncthreads();   // every wave has read K(0): its buffer takes K(2)
   }
-  const int n_full = min(n_tiles, (hist + pos0 + 1) / BK);
+  // tiles wholly below every row's limit and inside the sequence
+  const int n_full = PFX ? max(0, min(n_tiles, kvl / BK - tile0))
+                         : min(n_tiles, (hist + pos0 + 1) / BK);
   int j = 0;
   for (; j + 1 < n_full; j += 2) {
     iteration(j, kb0, kb1, v_lds0, vb1, s0, s1, BoolTag<false>{});
@@ -579,6 +615,25 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   if (!row_ok) return;
   const bool poison = bad_flag != 0;
   const float inv = a.v_scale / l_tot;   // v_scale: 1 for 16-bit pools
+  if constexpr (PFX) {   // fp32 partials of key split ks
+    const int64_t prow = (qrow * a.num_q_heads + head) * a.part_stride + ks;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float4 v = make_float4(o[db][4 * j] * inv, o[db][4 * j + 1] * inv,
+                               o[db][4 * j + 2] * inv, o[db][4 * j + 3] * inv);
+        if (poison) v = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                                    __builtin_nanf(""));
+        *reinterpret_cast<float4*>(a.o_part + prow * D + 32 * db + 8 * j + 4 * half) = v;
+      }
+    if (half == 0) {
+      float lse = (m_run * c + log2_fast(l_tot) - M::POFF) * kLn2;
+      if (m_run == -INFINITY) lse = -INFINITY;
+      a.lse_part[prow] = poison ? __builtin_nanf("") : lse;
+    }
+    return;
+  }
   char* op = (char*)a.out + ((qrow * a.num_q_heads + head) * D) * 2;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -600,21 +655,30 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   }
 }
 
-template <typename TT, typename CT>
-hipError_t launch_t(int group, const PrefillArgs& a, hipStream_t stream) {
-  const int64_t blocks = (int64_t)a.batch * a.num_kv_heads *
-                         (a.xcd_split ? 8 * (int64_t)a.m_tiles_x : (int64_t)a.m_tiles);
-  if (blocks == 0) return hipSuccess;
-  const dim3 grid((unsigned)blocks), block(NWP * 64);
+template <typename TT, typename CT, bool PFX>
+hipError_t launch_g(int group, const dim3 grid, const PrefillArgs& a, hipStream_t stream) {
+  const dim3 block(NWP * 64);
   switch (group) {
-    case 1: hipLaunchKernelGGL((prefill_kernel<TT, CT, 1>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((prefill_kernel<TT, CT, 2>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((prefill_kernel<TT, CT, 4>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((prefill_kernel<TT, CT, 8>), grid, block, 0, stream, a); break;
-    case 16: hipLaunchKernelGGL((prefill_kernel<TT, CT, 16>), grid, block, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((prefill_kernel<TT, CT, 1, PFX>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<TT, CT, 2, PFX>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<TT, CT, 4, PFX>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((prefill_kernel<TT, CT, 8, PFX>), grid, block, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL((prefill_kernel<TT, CT, 16, PFX>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <typename TT, typename CT>
+hipError_t launch_t(int group, const PrefillArgs& a, hipStream_t stream) {
+  const bool pfx = a.o_part != nullptr;
+  const int64_t blocks = (int64_t)a.batch * a.num_kv_heads *
+                         (a.xcd_split ? 8 * (int64_t)a.m_tiles_x : (int64_t)a.m_tiles) *
+                         (pfx ? a.n_ksplit : 1);
+  if (blocks == 0) return hipSuccess;
+  const dim3 grid((unsigned)blocks);
+  return pfx ? launch_g<TT, CT, true>(group, grid, a, stream)
+             : launch_g<TT, CT, false>(group, grid, a, stream);
 }
 
 template <typename TT>

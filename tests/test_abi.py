@@ -313,3 +313,49 @@ def test_mixed_args(L):
     assert _mixed(L, d, nd=1, max_q=0) == -1              # chunks need max_q_len >= 1
     assert _mixed(L, desc(dtype=0)) == -2                 # the chunk path is MFMA: f16/bf16
     assert _mixed(L, d, batch=0, nd=0) == 0
+
+
+def _shared(L, d, opts=None, *, batch=2, hq=4, prefix=256, stride=8, max_suffix=100,
+            ws=FAKE, ws_bytes=1 << 30, prefix_table=FAKE, out=FAKE):
+    return L.pkv_paged_attn_decode_shared_prefix(
+        C.byref(d), FAKE, FAKE, FAKE, batch, hq, prefix_table, prefix, FAKE, stride, FAKE,
+        max_suffix, 0.125, 0, None if opts is None else C.byref(opts), out, None, ws, ws_bytes,
+        None)
+
+
+def test_shared_prefix_plan_and_args(L):
+    d = desc(num_pages=10000, hkv=8)
+    n, ws = C.c_int32(), C.c_size_t()
+
+    def plan(batch, hq, prefix, max_suffix, split=0, dd=d, opts=None):
+        rc = L.pkv_decode_shared_prefix_plan(C.byref(dd), batch, hq, prefix, max_suffix, split,
+                                             None if opts is None else C.byref(opts),
+                                             C.byref(n), C.byref(ws))
+        return rc, n.value, ws.value
+
+    # the 256-sequence batch sharing 2048 tokens: 8 splits of the shared keys
+    # (8 KV heads x 4 row tiles x 8 = 256 workgroups) + the own pages' split
+    rc, parts, wsb = plan(256, 32, 2048, 513)
+    assert rc == 0 and parts == 9
+    rows = 256 * 32
+    assert wsb == (rows * parts * 128 * 4 + 255) // 256 * 256 + rows * parts * 4
+    rc, parts, _ = plan(6, 16, 0, 701)            # no shared pages: the decode's own splits
+    m = C.c_int32()
+    assert L.pkv_decode_plan(C.byref(d), 6, 16, 701, 0, C.byref(m), C.byref(ws)) == 0
+    assert rc == 0 and parts == m.value
+    assert plan(2, 16, 100, 10)[0] == -1          # shared part not whole pages
+    assert plan(2, 16, -16, 10)[0] == -1
+    assert plan(2, 16, 256, -1)[0] == -1
+    assert plan(2, 16, 256, 10, dd=desc(dtype=0))[0] == -2       # f32 pools
+    assert plan(2, 16, 256, 10, dd=desc(d=64))[0] == -2          # head_dim 128 only
+    assert plan(2, 16, 256, 10, opts=_opts(2, 1.0, 1.0, 64, 0))[0] == -1   # no window
+    # the call: host checks before any launch
+    assert _shared(L, desc(), prefix=100) == -1
+    assert _shared(L, desc(), prefix_table=None) == -1
+    assert _shared(L, desc(), out=None) == -1
+    assert _shared(L, desc(), ws=None) == -3
+    assert _shared(L, desc(), ws_bytes=16) == -3
+    assert _shared(L, desc(), max_suffix=8 * 16 + 1) == -1     # beyond stride * P
+    assert _shared(L, desc(), batch=0) == 0
+    assert _shared(L, desc(dtype=3), batch=0) == -1             # fp8: needs the query type
+    assert _shared(L, desc(dtype=3), _opts(1, 0.5, 0.5), batch=0) == 0

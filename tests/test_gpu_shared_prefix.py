@@ -1,0 +1,149 @@
+"""GPU parity of the shared-prefix (cascade) decode.
+
+A batch whose sequences all begin with the same physical pages (page 2,
+section 3.2: identical prompt prefixes share physical pages) decodes through
+pkv_paged_attn_decode_shared_prefix: the shared pages once for the whole batch
+on the matrix cores, each sequence's own pages by the split-KV decode, all
+partials merged by log-sum-exp.  The result must be that of the plain decode
+over the concatenated table: compared with the oracle's decode over the full
+tables (every row and log-sum-exp), with the GPU's one-pass decode, and on
+the degenerate forms (no shared pages; no own pages)."""
+import pytest
+import torch
+
+import paged_kv_cache_04_amd as pkv
+from oracle import pkvref
+from paged_kv_cache_04_amd import workloads as W
+
+from helpers import assert_close, assert_lse_close, host_threads, to_dev
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+P = 16
+
+
+def build(qd, hq, hkv, prefix, suffix, kv=None, append=True, seed=0):
+    kw = dict(kv_dtype=kv, k_scale=3 / 128, v_scale=5 / 256) if kv else {}
+    return W.make_decode("sp", seed=seed or (hq + 3 * hkv + prefix), batch=len(suffix), hq=hq,
+                         hkv=hkv, d=128, dtype=qd, hist_lens=[prefix + s for s in suffix],
+                         append=append, pool_slack=0.2, shared_prefix=prefix, **kw)
+
+
+def gpu_append(w, d):
+    if d["k_new"] is None:
+        return
+    if w.is_fp8:
+        pkv.kv_append_quant(d["k_cache"], d["v_cache"], d["k_new"], d["v_new"], d["slots"],
+                            w.k_scale, w.v_scale)
+    else:
+        pkv.kv_append(d["k_cache"], d["v_cache"], d["k_new"], d["v_new"], d["slots"])
+
+
+def oracle(w, rows=None):
+    if w.k_new is not None:
+        if w.is_fp8:
+            f8 = W.DTYPES[w.kv_dtype]
+            kq = torch.from_numpy(pkvref.quant_fp8(w.kv_dtype, w.dtype, w.k_new, w.k_scale))
+            vq = torch.from_numpy(pkvref.quant_fp8(w.kv_dtype, w.dtype, w.v_new, w.v_scale))
+            pkvref.kv_append(w.kv_dtype, w.k_cache, w.v_cache, kq.view(f8), vq.view(f8), w.slots)
+        else:
+            pkvref.kv_append(w.dtype, w.k_cache, w.v_cache, w.k_new, w.v_new, w.slots)
+    return pkvref.decode_ex(w.dtype, w.kv_dtype, w.k_cache, w.v_cache, w.q, w.block_table,
+                            w.context_lens, w.scale, k_scale=w.k_scale, v_scale=w.v_scale,
+                            rows=rows, n_threads=host_threads())
+
+
+def cascade(w, d, prefix, split=0):
+    pp = prefix // P
+    bt = d["block_table"]
+    prefix_table = bt[0, :pp].contiguous() if pp else torch.zeros(1, dtype=torch.int32,
+                                                                 device=DEV)
+    own = bt[:, pp:] if bt.shape[1] > pp else bt      # the pages after the shared ones
+    suffix_lens = (d["context_lens"] - prefix).contiguous()
+    max_suffix = int(suffix_lens.max().item())
+    out, lse = pkv.paged_attn_decode_shared_prefix(d["q"], d["k_cache"], d["v_cache"],
+                                                   prefix_table, prefix, own, suffix_lens,
+                                                   max_suffix, w.scale, split_tokens=split,
+                                                   return_lse=True, k_scale=w.k_scale,
+                                                   v_scale=w.v_scale)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+CASES = [
+    ("bf16", None, 32, 8, 256, [0, 1, 15, 16, 100, 700]),    # G 4: vector decode for own pages
+    ("f16", None, 16, 2, 1024, [5, 300, 2000, 40]),          # G 8
+    ("bf16", None, 32, 2, 512, [3, 64, 1000]),               # G 16
+    ("f16", "fp8_e4m3", 16, 2, 768, [10, 500]),              # fp8 pools, G 8
+    ("bf16", "fp8_e5m2", 32, 8, 256, [0, 33, 129]),          # fp8 pools, G 4
+    ("f16", None, 8, 8, 4096, [7, 70]),                      # G 1, long shared part
+    ("bf16", None, 16, 2, 272, [9, 90]),                     # shared part ends mid-tile
+]
+
+
+@pytest.mark.parametrize("split", [0, 64])
+@pytest.mark.parametrize("qd,kv,hq,hkv,prefix,suffix", CASES)
+def test_shared_prefix_matches_oracle(qd, kv, hq, hkv, prefix, suffix, split):
+    w = build(qd, hq, hkv, prefix, suffix, kv=kv)
+    d = to_dev(w, DEV)
+    gpu_append(w, d)
+    out, lse = cascade(w, d, prefix, split)
+    full, full_lse = pkv.paged_attn_decode(d["q"], d["k_cache"], d["v_cache"], d["block_table"],
+                                           d["context_lens"], w.max_context_len, w.scale,
+                                           return_lse=True, k_scale=w.k_scale,
+                                           v_scale=w.v_scale)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle(w)
+    what = f"shared prefix {qd}/{kv or qd} G{hq // hkv} prefix {prefix} split {split}"
+    assert_close(out.reshape(ref.shape), ref, qd, what)
+    assert_lse_close(lse.reshape(-1), ref_lse, qd, what)
+    assert_close(out.float(), full.float().cpu().numpy(), qd, what + " vs one-pass decode")
+
+
+def test_no_shared_pages_is_the_plain_decode():
+    w = build("bf16", 16, 2, 0, [5, 300, 1000])
+    d = to_dev(w, DEV)
+    gpu_append(w, d)
+    out, lse = cascade(w, d, 0)
+    ref, ref_lse = oracle(w)
+    assert_close(out.reshape(ref.shape), ref, "bf16", "prefix 0")
+    assert_lse_close(lse.reshape(-1), ref_lse, "bf16", "prefix 0")
+
+
+def test_only_shared_pages():
+    """Every sequence is exactly the shared prefix (no own keys)."""
+    w = build("f16", 16, 2, 512, [0, 0, 0], append=False)
+    d = to_dev(w, DEV)
+    out, lse = cascade(w, d, 512)
+    ref, ref_lse = oracle(w)
+    assert_close(out.reshape(ref.shape), ref, "f16", "prefix only")
+    assert_lse_close(lse.reshape(-1), ref_lse, "f16", "prefix only")
+
+
+def test_bad_shared_page_poisons_every_row():
+    w = build("bf16", 16, 2, 256, [10, 20])
+    d = to_dev(w, DEV)
+    gpu_append(w, d)
+    bt = d["block_table"].clone()
+    prefix_table = bt[0, :16].contiguous()
+    prefix_table[3] = w.num_pages + 7
+    out, lse = pkv.paged_attn_decode_shared_prefix(d["q"], d["k_cache"], d["v_cache"],
+                                                   prefix_table, 256, bt[:, 16:],
+                                                   (d["context_lens"] - 256).contiguous(), 21,
+                                                   w.scale, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.isnan(out.float()).all() and torch.isnan(lse).all()
+
+
+def test_prefix_workload_sampled():
+    """The 256-sequence batch sharing 2048 tokens: sampled rows against the
+    oracle's decode over the full tables."""
+    w = W.make("prefix")
+    print("[shared prefix parity] 256 x (2048 shared + 32..512 own)", flush=True)
+    d = to_dev(w, DEV)
+    out, lse = cascade(w, d, w.meta["shared_prefix"])
+    hq = w.num_q_heads
+    rows = [b * hq + h for b in range(0, w.batch, 5) for h in (0, 7, 31)]
+    ref, ref_lse = oracle(w, rows=rows)
+    assert_close(out.reshape(-1, w.head_dim)[rows], ref, w.dtype, "prefix workload")
+    assert_lse_close(lse.reshape(-1)[rows], ref_lse, w.dtype, "prefix workload")
