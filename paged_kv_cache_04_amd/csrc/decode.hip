@@ -16,8 +16,11 @@
 // pages_per_split logical pages; wave w of the workgroup takes pages
 // w, w+4, w+8, ... of the split.  Each wave keeps its own (m, l, acc) state;
 // the four are combined through LDS at the end.  Every wave keeps the loads
-// of its next two pages in flight while it computes the current one (three
-// register buffers).  K/V are read once, with streaming (non-temporal) loads.
+// of the next pages in flight while it computes the current one (register
+// buffers: two for 16-bit pools at G <= 4, which then fit three workgroups
+// per CU -- more resident waves hide the start-up of short sequences --, three
+// for 16-bit pools at G = 8 and two for f32, at two workgroups per CU; five
+// for fp8).  K/V are read once, with streaming (non-temporal) loads.
 //
 // Per page (16 tokens x D elements, one contiguous 2-8 KiB block per head):
 //   K, "row layout": 8 lanes per token, 8 tokens per pass, 2 passes; lane c of
@@ -91,8 +94,11 @@ struct DecodeCfg {
   static constexpr bool PACKED = (QES == 2); // packed-pair PV for 16-bit queries
   // f16 probabilities are stored as p * 2^15
   static constexpr float POFF = QT::is_f16 ? 15.f : 0.f;
-  // pages in flight per wave: the one being computed plus NB - 1 ahead
-  static constexpr int NB = FP8 ? 5 : ((ES == 4) ? 2 : 3);
+  // pages in flight per wave: the one being computed plus NB - 1 ahead; OCC:
+  // workgroups per CU the registers are sized for
+  static constexpr bool OCC3 = !FP8 && ES == 2 && G <= 4;
+  static constexpr int NB = FP8 ? 5 : ((ES == 4 || OCC3) ? 2 : 3);
+  static constexpr int OCC = OCC3 ? 3 : 2;
   static_assert(KV >= 1 && KV * KL * VEC == D, "head_dim / vector mismatch");
   static_assert(QW >= 1, "q vector layout");
   static_assert(TG >= 1 && VT * TG == P, "V layout mismatch");
@@ -179,7 +185,7 @@ struct PageRegs {
 // WIN: a sliding window is in force (the visited-page map and the hidden-key
 // test are compiled only then).
 template <typename QT, typename CT, int D, int G, bool WIN>
-__global__ __launch_bounds__(NW * 64, 2) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(NW * 64, (DecodeCfg<QT, CT, D, G>::OCC)) void decode_kernel(DecodeArgs a) {
   using C = DecodeCfg<QT, CT, D, G>;
   using TT = QT;
   constexpr int ES = C::ES, VEC = C::VEC;
