@@ -318,7 +318,8 @@ int pkv_merge_states(const float* o_parts, const float* lse_parts, int32_t rows,
  *   lse_out      : device float [total_q_rows][H_q] or NULL.
  * QK^T and PV run on the matrix cores (MFMA, fp32 accumulation); the
  * probabilities enter the PV product rounded to the query type.  Needs f16
- * or bf16 pools and head_dim 128 (fp8 pools: the _ex form).
+ * or bf16 pools with head_dim 128 or 64 (fp8 pools, head_dim 128: the _ex
+ * form).
  */
 int pkv_paged_attn_prefill_chunk(const pkv_cache_desc* desc, const void* k_cache,
                                  const void* v_cache, const void* q, const int32_t* q_indptr,
@@ -367,8 +368,8 @@ int pkv_paged_attn_prefill_chunk_ex(const pkv_cache_desc* desc, const void* k_ca
  *   max_q_len  : host bound >= C_b of every chunk sequence (>= 1 if any).
  *   workspace  : >= the workspace_bytes of pkv_decode_plan(desc, num_decode,
  *                num_q_heads, max_kv_len, split_tokens); may be NULL when 0.
- * Other arguments as for paged_attn_prefill_chunk (f16 or bf16, head_dim 128;
- * fp8 pools: the _ex form).
+ * Other arguments as for paged_attn_prefill_chunk (f16 or bf16 pools, head_dim
+ * 128 or 64; fp8 pools, head_dim 128: the _ex form).
  */
 int pkv_paged_attn_mixed(const pkv_cache_desc* desc, const void* k_cache, const void* v_cache,
                          const void* q, const int32_t* q_indptr, int32_t batch,
@@ -433,7 +434,8 @@ int pkv_decode_shared_prefix_plan(const pkv_cache_desc* desc, int32_t batch, int
  *   workspace     : >= the workspace_bytes of decode_shared_prefix_plan,
  *                   16-byte aligned; holds fp32 partials [batch*H_q][n_parts]
  *                   [D] and their log-sum-exps.
- * Pools: f16, bf16 or fp8 (e4m3 / e5m2); head_dim 128; G as for decode.
+ * Pools: f16 or bf16 with head_dim 128 or 64, fp8 (e4m3 / e5m2) with head_dim
+ * 128; G as for decode.
  * Three launches on `stream`; no synchronisation.
  */
 int pkv_paged_attn_decode_shared_prefix(

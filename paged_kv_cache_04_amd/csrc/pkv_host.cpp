@@ -703,8 +703,9 @@ int prefill_checks(const pkv_cache_desc* desc, int32_t num_q_heads, int32_t batc
   if (desc->dtype != PKV_F16 && desc->dtype != PKV_BF16 && !is_fp8(desc->dtype))
     return fail(PKV_ERR_UNSUPPORTED,
                 "prefill runs on the matrix cores: f16, bf16 or fp8 pools only");
-  if (desc->head_dim != 128)
-    return fail(PKV_ERR_UNSUPPORTED, "prefill is built for head_dim 128 (got %d)",
+  if (desc->head_dim != 128 && !(desc->head_dim == 64 && !is_fp8(desc->dtype)))
+    return fail(PKV_ERR_UNSUPPORTED,
+                "prefill is built for head_dim 128, and 64 with 16-bit pools (got %d)",
                 desc->head_dim);
   if (o->window != 0 || o->sink != 0)
     return fail(PKV_ERR_INVALID, "window and sink apply to decode only (got %d, %d)", o->window,
@@ -913,9 +914,10 @@ int cascade_plan(const pkv_cache_desc* desc, int32_t batch, int32_t num_q_heads,
   if (desc->dtype != PKV_F16 && desc->dtype != PKV_BF16 && !is_fp8(desc->dtype))
     return fail(PKV_ERR_UNSUPPORTED,
                 "the shared pages run on the matrix cores: f16, bf16 or fp8 pools only");
-  if (desc->head_dim != 128)
-    return fail(PKV_ERR_UNSUPPORTED, "shared-prefix decode is built for head_dim 128 (got %d)",
-                desc->head_dim);
+  if (desc->head_dim != 128 && !(desc->head_dim == 64 && !is_fp8(desc->dtype)))
+    return fail(PKV_ERR_UNSUPPORTED,
+                "shared-prefix decode is built for head_dim 128, and 64 with 16-bit pools "
+                "(got %d)", desc->head_dim);
   if (cp->opts.window != 0 || cp->opts.sink != 0)
     return fail(PKV_ERR_INVALID, "window and sink do not apply to the shared-prefix decode");
   if (batch < 0) return fail(PKV_ERR_INVALID, "batch %d < 0", batch);

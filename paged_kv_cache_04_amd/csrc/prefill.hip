@@ -9,6 +9,9 @@
 // section 2.2).  Keys are reached through the block table (page 3, section
 // 3.2).
 //
+// head_dim 128, or 64 with 16-bit pools (the tiles then hold 128-byte rows;
+// the QK products take half the k-steps and PV half the output blocks).
+//
 // Work decomposition.  A workgroup (8 wavefronts, one per CU) owns 256 query
 // rows of one (sequence, KV head): 256 / G chunk positions times the G query
 // heads that share the KV head (page 4, section 2.2, GQA), so the G heads
@@ -65,12 +68,9 @@ namespace pkv {
 namespace {
 
 constexpr int P = kPageSize;
-constexpr int D = 128;           // head_dim of the MFMA kernel
 constexpr int BK = 64;           // keys per tile (4 pages)
 constexpr int NWP = 8;           // waves per workgroup
 constexpr int ROWS = 256;        // query rows per workgroup
-constexpr int ROWB = D * 2;      // bytes per key row (256)
-constexpr int TILEB = BK * ROWB; // bytes per K or V tile (16 KiB)
 constexpr int kLazyLog2 = 8;     // weights stay below 2^(8 + POFF)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -122,12 +122,26 @@ struct Mfma<TF16> {
 };
 
 // Chunk permutation of key row r (physical chunk = logical chunk ^ swz(r)),
-// for 64 LDS banks (256 bytes per cycle).  It is a bijection on r % 16, so
-// the K operand reads of 16 consecutive rows at one logical chunk hit all 16
-// chunk positions; and it puts r % 4 into chunk bits 2-3 and r / 4 % 4 into
-// bits 0-1, so the transposing V reads of 32 lanes (4 keys x two adjacent
-// 32-byte chunk pairs) cover 8 distinct chunk pairs.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// for 64 LDS banks (256 bytes per cycle).
+// NCH = 16 (head_dim 128, 256-byte rows): a bijection on r % 16, so the K
+// operand reads of 16 consecutive rows at one logical chunk hit all 16 chunk
+// positions; and it puts r % 4 into chunk bits 2-3 and r / 4 % 4 into bits
+// 0-1, so the transposing V reads of 32 lanes (4 keys x two adjacent 32-byte
+// chunk pairs) cover 8 distinct chunk pairs.
+// NCH = 8 (head_dim 64, 128-byte rows: rows r and r + 1 share the 64 banks,
+// one half each): x = (r / 2) % 8 is mapped by a bijection g, so the 8 rows
+// of one parity among 16 consecutive rows hit 8 distinct chunks; g sends x
+// and x + 1 (the two keys of one parity among 4 consecutive keys) to
+// different chunk pairs, which keeps the transposing V reads apart.
+template <int NCH>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (NCH == 16) {
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  } else {
+    const int x = (r >> 1) & 7;
+    return ((x & 1) << 2) | (x >> 1);
+  }
+}
 
 // Direct global-to-LDS copy through a buffer descriptor: lane i's 16 bytes
 // at byte offset voff of the buffer go to lds_base + 16 * i.
@@ -150,12 +164,21 @@ __device__ __forceinline__ uint2 read_tr(const lds_u8* p) {
 }
 
 // TT: type of q, out and the tiles' elements; CT: type of the pools (TT, or
-// an fp8 type); PFX: the shared-prefix form (one sequence, no causal mask,
-// key splits, fp32 partials) instead of a chunked prefill.
-template <typename TT, typename CT, int G, bool PFX>
+// an fp8 type); D: head_dim (128, or 64 for 16-bit pools); PFX: the
+// shared-prefix form (one sequence, no causal mask, key splits, fp32
+// partials) instead of a chunked prefill.
+template <typename TT, typename CT, int D, int G, bool PFX>
 __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   using M = Mfma<TT>;
   constexpr bool F8 = CT::is_fp8;
+  constexpr int ROWB = D * 2;       // bytes per tile row (a key's D elements of TT)
+  constexpr int TILEB = BK * ROWB;  // bytes per K or V tile
+  constexpr int NCH = ROWB / 16;    // 16-byte chunks per tile row
+  constexpr int KS = D / 16;        // QK k-steps (16 head dims each)
+  constexpr int QG = KS / 2;        // QK groups of two k-steps
+  constexpr int DB = D / 32;        // PV output blocks of 32 head dims
+  static_assert(D == 64 || D == 128, "head_dim");
+  static_assert(!F8 || D == 128, "fp8 pools are built for head_dim 128");
   constexpr int PAGEB = P * D * CT::bytes;  // bytes of one (page, head) block
   constexpr int NPOS = ROWS / G;  // chunk positions per workgroup
   __shared__ __align__(1024) uint8_t k_lds0[TILEB];
@@ -236,7 +259,7 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
     if (row_ok) {
       const int64_t prow = (qrow * a.num_q_heads + head) * a.part_stride + ks;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float z = bad ? __builtin_nanf("") : 0.f;
@@ -249,12 +272,12 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   }
 
   // Q^T operand: 8 k-steps of 16 head dims; lane holds 8 consecutive dims
-  u32x4_t qreg[8];
+  u32x4_t qreg[KS];
   {
     const bool neg = a.scale_log2 < 0.f;  // fold the sign of the scale into q
     const char* qp = (const char*)a.q + ((qrow * a.num_q_heads + head) * D) * 2;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       u32x4 x;
       if (row_ok) x = load16(qp + (16 * ks + 8 * half) * 2);
       else x.w[0] = x.w[1] = x.w[2] = x.w[3] = 0u;
@@ -280,11 +303,13 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int wp = wu & 3;          // page of the tile this wave copies
   const bool kwave = wu < 4;      // waves 0-3 copy K pages, waves 4-7 V pages
-  uint32_t dma_off[4];
+  constexpr int NDMA = F8 ? 1 : PAGEB / 1024;   // 1-KiB copies per page (16-bit pools)
+  constexpr int RPC = 1024 / ROWB;               // tile rows per 1-KiB copy
+  uint32_t dma_off[NDMA];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 4 * j + (lane >> 4);               // key row within the page
-    dma_off[j] = (uint32_t)(r * ROWB + (((lane & 15) ^ swz(r)) * 16));
+  for (int j = 0; j < NDMA; ++j) {
+    const int r = RPC * j + lane / NCH;          // key row within the page
+    dma_off[j] = (uint32_t)(r * ROWB + (((lane % NCH) ^ swz<NCH>(r)) * 16));
   }
   bool my_bad = false;
   // block-table entry of this wave's page of tile t (0 past the sequence)
@@ -309,7 +334,7 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
       for (int j = 0; j < PAGEB / 1024; ++j) dma16(r, (uint32_t)(j * 1024 + 16 * lane), my_stg + j * 1024);
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dma16(r, dma_off[j], dst + (16 * wp + 4 * j) * ROWB);
+      for (int j = 0; j < NDMA; ++j) dma16(r, dma_off[j], dst + (16 * wp + RPC * j) * ROWB);
     }
   };
   // fp8: widen the staged page (after this wave's own copy has landed) into
@@ -319,8 +344,8 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   auto widen_page = [&](lds_u8* dst) {
     if constexpr (F8) {
 #pragma unroll 1
-      for (int i = 0; i < 4; ++i) {
-        const int ch = lane + 64 * i, r = ch >> 4, lc = ch & 15;
+      for (int i = 0; i < P * NCH / 64; ++i) {
+        const int ch = lane + 64 * i, r = ch / NCH, lc = ch % NCH;
         const u32x2_t x = *reinterpret_cast<const u32x2_t __attribute__((address_space(3)))*>(
             my_stg + r * (D * CT::bytes) + lc * 8);
         u32x4_t y;
@@ -329,7 +354,7 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
         y[2] = CT::template cvt2<TT, false>(x[1]);
         y[3] = CT::template cvt2<TT, true>(x[1]);
         *reinterpret_cast<u32x4_t __attribute__((address_space(3)))*>(
-            dst + (16 * wp + r) * ROWB + ((lc ^ swz(r)) * 16)) = y;
+            dst + (16 * wp + r) * ROWB + ((lc ^ swz<NCH>(r)) * 16)) = y;
       }
     }
   };
@@ -345,9 +370,9 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   };
 
   // ---- accumulators
-  f32x16_t o[4];
+  f32x16_t o[DB];
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
   // reference max of this row (raw scores): the running max at its last
@@ -358,19 +383,19 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   // Per-lane LDS byte offsets, the same for every tile: the K operand of
   // k-step ks (row n, logical chunk 2ks + half) and the V^T operand reads of
   // head-dim block db for key slots 0..3 (a) and 4..7 (b) at k-step 0.
-  int k_off[8];
+  int k_off[KS];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) k_off[ks] = n * ROWB + (((2 * ks + half) ^ swz(n)) * 16);
+  for (int ks = 0; ks < KS; ++ks) k_off[ks] = n * ROWB + (((2 * ks + half) ^ swz<NCH>(n)) * 16);
   const int q16 = lane >> 4, li = lane & 15;
   const int kk = li >> 2, jj = li & 3;
   const int key_a0 = 4 * (q16 >> 1) + kk;      // key of slots 0..3 at k-step 0
-  int va_off[4], vb_off[4];
+  int va_off[DB], vb_off[DB];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
+  for (int db = 0; db < DB; ++db) {
     const int dcol = 32 * db + 16 * (q16 & 1) + 4 * jj;   // first of 4 head dims
     const int lc = dcol >> 3, sub8 = (dcol & 7) * 2;      // chunk, byte in chunk
-    va_off[db] = key_a0 * ROWB + ((lc ^ swz(key_a0)) * 16) + sub8;
-    vb_off[db] = (key_a0 + 8) * ROWB + ((lc ^ swz(key_a0 + 8)) * 16) + sub8;
+    va_off[db] = key_a0 * ROWB + ((lc ^ swz<NCH>(key_a0)) * 16) + sub8;
+    vb_off[db] = (key_a0 + 8) * ROWB + ((lc ^ swz<NCH>(key_a0 + 8)) * 16) + sub8;
   }
 
   // S^T = K Q^T of one tile, two 32-key blocks: score i of block kb is key
@@ -393,7 +418,7 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   };
   auto s_tile = [&](const lds_u8* kt, f32x16_t (&s)[2]) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int g = 0; g < QG; ++g) {
       KOps ka;
       k_read(kt, g, ka);
       s_group(g, ka, s);
@@ -428,10 +453,10 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   // 4..7), dims +4j .. +4j+3, so result lane i holds dim +i for keys k = 0..3.
   // The swizzle of key 16ks + x equals that of key x, so k-step ks only adds
   // 16 rows to the k-step 0 offsets.
-  typedef u32x4_t VOps[4];
+  typedef u32x4_t VOps[DB];
   auto v_read = [&](const lds_u8* vt, int ks, VOps& va) {
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int db = 0; db < DB; ++db) {
       const uint2 lo = read_tr(vt + ks * 16 * ROWB + va_off[db]);
       const uint2 hi = read_tr(vt + ks * 16 * ROWB + vb_off[db]);
       va[db][0] = lo.x;
@@ -442,7 +467,7 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   };
   auto pv_step = [&](const VOps& va, const u32x4_t& pk) {
 #pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] = M::run(va[db], pk, o[db]);
+    for (int db = 0; db < DB; ++db) o[db] = M::run(va[db], pk, o[db]);
   };
   auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
 
@@ -486,11 +511,13 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
     u32x4_t pk[4];
     float ls = 0.f;
     KOps ka;
+    // head_dim 64 has two QK groups: they go with every second weights step
+    constexpr int QSTEP = 4 / QG;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      k_read(kc, g, ka);
+      if (g % QSTEP == 0) k_read(kc, g / QSTEP, ka);
       weights(s_cur, g, mc, pk[g], ls);
-      s_group(g, ka, s_nxt);
+      if (g % QSTEP == 0) s_group(g / QSTEP, ka, s_nxt);
       fence();
     }
     // A weight above 2^(8+POFF) shows in its lane's sum; so does a reference
@@ -510,7 +537,7 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
       const float alpha = (m_run == -INFINITY) ? 0.f : exp2_fast((m_run - m_new) * c);
       l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
       m_run = m_new;
@@ -618,7 +645,7 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   if constexpr (PFX) {   // fp32 partials of key split ks
     const int64_t prow = (qrow * a.num_q_heads + head) * a.part_stride + ks;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float4 v = make_float4(o[db][4 * j] * inv, o[db][4 * j + 1] * inv,
@@ -636,7 +663,7 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   }
   char* op = (char*)a.out + ((qrow * a.num_q_heads + head) * D) * 2;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int d = 32 * db + 8 * j + 4 * half;
@@ -655,21 +682,21 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   }
 }
 
-template <typename TT, typename CT, bool PFX>
+template <typename TT, typename CT, int D, bool PFX>
 hipError_t launch_g(int group, const dim3 grid, const PrefillArgs& a, hipStream_t stream) {
   const dim3 block(NWP * 64);
   switch (group) {
-    case 1: hipLaunchKernelGGL((prefill_kernel<TT, CT, 1, PFX>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((prefill_kernel<TT, CT, 2, PFX>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((prefill_kernel<TT, CT, 4, PFX>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((prefill_kernel<TT, CT, 8, PFX>), grid, block, 0, stream, a); break;
-    case 16: hipLaunchKernelGGL((prefill_kernel<TT, CT, 16, PFX>), grid, block, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((prefill_kernel<TT, CT, D, 1, PFX>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<TT, CT, D, 2, PFX>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<TT, CT, D, 4, PFX>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((prefill_kernel<TT, CT, D, 8, PFX>), grid, block, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL((prefill_kernel<TT, CT, D, 16, PFX>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <typename TT, typename CT>
+template <typename TT, typename CT, int D>
 hipError_t launch_t(int group, const PrefillArgs& a, hipStream_t stream) {
   const bool pfx = a.o_part != nullptr;
   const int64_t blocks = (int64_t)a.batch * a.num_kv_heads *
@@ -677,17 +704,25 @@ hipError_t launch_t(int group, const PrefillArgs& a, hipStream_t stream) {
                          (pfx ? a.n_ksplit : 1);
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)blocks);
-  return pfx ? launch_g<TT, CT, true>(group, grid, a, stream)
-             : launch_g<TT, CT, false>(group, grid, a, stream);
+  return pfx ? launch_g<TT, CT, D, true>(group, grid, a, stream)
+             : launch_g<TT, CT, D, false>(group, grid, a, stream);
 }
 
 template <typename TT>
-hipError_t launch_q(int kv_dtype, int group, const PrefillArgs& a, hipStream_t stream) {
+hipError_t launch_q(int kv_dtype, int head_dim, int group, const PrefillArgs& a,
+                    hipStream_t stream) {
   switch (kv_dtype) {
     case 1:
-    case 2: return launch_t<TT, TT>(group, a, stream);
-    case 3: return launch_t<TT, TFP8E4M3>(group, a, stream);
-    case 4: return launch_t<TT, TFP8E5M2>(group, a, stream);
+    case 2:
+      if (head_dim == 64) return launch_t<TT, TT, 64>(group, a, stream);
+      if (head_dim == 128) return launch_t<TT, TT, 128>(group, a, stream);
+      return hipErrorInvalidValue;
+    case 3:
+      return head_dim == 128 ? launch_t<TT, TFP8E4M3, 128>(group, a, stream)
+                             : hipErrorInvalidValue;
+    case 4:
+      return head_dim == 128 ? launch_t<TT, TFP8E5M2, 128>(group, a, stream)
+                             : hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
@@ -698,11 +733,10 @@ int prefill_rows_per_tile(int group) { return ROWS / group; }
 
 hipError_t launch_prefill(int kv_dtype, int q_dtype, int head_dim, int group,
                           const PrefillArgs& a, hipStream_t stream) {
-  if (head_dim != D) return hipErrorInvalidValue;
   if (kv_dtype != 3 && kv_dtype != 4 && kv_dtype != q_dtype) return hipErrorInvalidValue;
   switch (q_dtype) {
-    case 1: return launch_q<TF16>(kv_dtype, group, a, stream);
-    case 2: return launch_q<TBF16>(kv_dtype, group, a, stream);
+    case 1: return launch_q<TF16>(kv_dtype, head_dim, group, a, stream);
+    case 2: return launch_q<TBF16>(kv_dtype, head_dim, group, a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -193,7 +193,7 @@ def _prefill(L, d, *, batch=2, hq=4, total=10, max_q=8, stride=8, max_kv=100, q=
 
 def test_prefill_args(L):
     assert _prefill(L, desc(dtype=0)) == -2              # f32 is not built on MFMA
-    assert _prefill(L, desc(d=64)) == -2                 # head_dim 64 not built
+    assert _prefill(L, desc(d=64), batch=0) == 0         # head_dim 64: 16-bit pools
     assert _prefill(L, desc(), hq=3) == -1
     assert _prefill(L, desc(), max_kv=8 * 16 + 1) == -1
     assert _prefill(L, desc(), max_q=200) == -1          # longer than max_kv
@@ -347,7 +347,8 @@ def test_shared_prefix_plan_and_args(L):
     assert plan(2, 16, -16, 10)[0] == -1
     assert plan(2, 16, 256, -1)[0] == -1
     assert plan(2, 16, 256, 10, dd=desc(dtype=0))[0] == -2       # f32 pools
-    assert plan(2, 16, 256, 10, dd=desc(d=64))[0] == -2          # head_dim 128 only
+    assert plan(2, 16, 256, 10, dd=desc(d=64))[0] == 0           # head_dim 64, 16-bit
+    assert plan(2, 16, 256, 10, dd=desc(d=64, dtype=3), opts=_opts(1))[0] == -2   # fp8: 128
     assert plan(2, 16, 256, 10, opts=_opts(2, 1.0, 1.0, 64, 0))[0] == -1   # no window
     # the call: host checks before any launch
     assert _shared(L, desc(), prefix=100) == -1

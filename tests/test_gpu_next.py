@@ -261,6 +261,20 @@ def test_mixed_batch_all_rows(dtype, hq, hkv, split):
     assert_lse_close(lse.reshape(-1), ref_lse, dtype, f"mixed {dtype} G{hq // hkv}")
 
 
+@pytest.mark.parametrize("dtype,hq,hkv", [("bf16", 16, 4), ("f16", 8, 8)])
+def test_mixed_batch_head_dim_64(dtype, hq, hkv):
+    """head_dim 64: decode rows on the vector kernel, chunks on the MFMA
+    kernel's 64-dim form; every row against the oracle."""
+    w = W.make_mixed("mx64", seed=hq + hkv + 64, hq=hq, hkv=hkv, d=64, dtype=dtype,
+                     decode_hist=[0, 16, 300, 1000], chunk_hist=[0, 37, 500],
+                     chunk=[7, 129, 64], pool_slack=0.2)
+    d = to_dev(w, DEV)
+    out, lse = mixed_run(w, d, 256)
+    ref, ref_lse = oracle_mixed(w)
+    assert_close(out.reshape(ref.shape), ref, dtype, f"mixed D64 {dtype} G{hq // hkv}")
+    assert_lse_close(lse.reshape(-1), ref_lse, dtype, f"mixed D64 {dtype} G{hq // hkv}")
+
+
 @pytest.mark.parametrize("layout", ["decode only", "chunks only"])
 def test_mixed_batch_degenerate(layout):
     if layout == "decode only":

@@ -62,28 +62,32 @@ def test_prefill_config_sampled_rows():
     check_prefill(w, rows)
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (8, 2), (16, 2), (32, 2)])
-def test_prefill_shapes_all_rows(dtype, hq, hkv):
-    """Every row of ragged chunks over ragged histories, G = 1, 2, 4, 8, 16."""
+def test_prefill_shapes_all_rows(dtype, hq, hkv, d):
+    """Every row of ragged chunks over ragged histories, G = 1, 2, 4, 8, 16,
+    head_dim 128 and 64."""
     hist = [0, 1, 15, 100, 1000, 37]
     chunk = [1, 33, 128, 200, 5, 129]
-    w = W.make_prefill("shape", seed=hq + hkv, batch=len(hist), hq=hq, hkv=hkv, d=128,
+    w = W.make_prefill("shape", seed=hq + hkv + d, batch=len(hist), hq=hq, hkv=hkv, d=d,
                        dtype=dtype, hist=hist, chunk=chunk, pool_slack=0.2)
-    check_prefill(w, what=f"{dtype} G{hq // hkv}")
+    check_prefill(w, what=f"{dtype} G{hq // hkv} D{d}")
 
 
-@pytest.mark.parametrize("dtype,hq,hkv", [("bf16", 8, 8), ("f16", 8, 4), ("bf16", 32, 2)])
-def test_prefill_workgroup_and_tile_boundaries(dtype, hq, hkv):
+@pytest.mark.parametrize("dtype,hq,hkv,d", [("bf16", 8, 8, 128), ("f16", 8, 4, 128),
+                                            ("bf16", 32, 2, 128), ("f16", 16, 2, 64),
+                                            ("bf16", 8, 8, 64)])
+def test_prefill_workgroup_and_tile_boundaries(dtype, hq, hkv, d):
     """A workgroup holds 256 / G chunk positions and keys go in 64-key tiles:
     chunks one below, at and one above multiples of 256 / G, over histories
     one below, at and one above multiples of 64, every row."""
     npos = 256 // (hq // hkv)
     chunk = [npos - 1, npos, npos + 1, 2 * npos + 1]
     hist = [63, 64, 65, 127]
-    w = W.make_prefill("edge", seed=hq * 7 + hkv, batch=4, hq=hq, hkv=hkv, d=128, dtype=dtype,
+    w = W.make_prefill("edge", seed=hq * 7 + hkv + d, batch=4, hq=hq, hkv=hkv, d=d, dtype=dtype,
                        hist=hist, chunk=chunk, pool_slack=0.2)
-    check_prefill(w, what=f"{dtype} G{hq // hkv} edges")
+    check_prefill(w, what=f"{dtype} G{hq // hkv} D{d} edges")
 
 
 def test_prefill_one_row_chunk_matches_decode():

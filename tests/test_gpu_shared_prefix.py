@@ -22,10 +22,10 @@ DEV = torch.device("cuda:0")
 P = 16
 
 
-def build(qd, hq, hkv, prefix, suffix, kv=None, append=True, seed=0):
+def build(qd, hq, hkv, prefix, suffix, kv=None, append=True, seed=0, d=128):
     kw = dict(kv_dtype=kv, k_scale=3 / 128, v_scale=5 / 256) if kv else {}
     return W.make_decode("sp", seed=seed or (hq + 3 * hkv + prefix), batch=len(suffix), hq=hq,
-                         hkv=hkv, d=128, dtype=qd, hist_lens=[prefix + s for s in suffix],
+                         hkv=hkv, d=d, dtype=qd, hist_lens=[prefix + s for s in suffix],
                          append=append, pool_slack=0.2, shared_prefix=prefix, **kw)
 
 
@@ -98,6 +98,17 @@ def test_shared_prefix_matches_oracle(qd, kv, hq, hkv, prefix, suffix, split):
     assert_close(out.reshape(ref.shape), ref, qd, what)
     assert_lse_close(lse.reshape(-1), ref_lse, qd, what)
     assert_close(out.float(), full.float().cpu().numpy(), qd, what + " vs one-pass decode")
+
+
+@pytest.mark.parametrize("qd,hq,hkv", [("bf16", 16, 4), ("f16", 16, 2)])
+def test_shared_prefix_head_dim_64(qd, hq, hkv):
+    w = build(qd, hq, hkv, 512, [3, 200, 1000], d=64)
+    d = to_dev(w, DEV)
+    gpu_append(w, d)
+    out, lse = cascade(w, d, 512)
+    ref, ref_lse = oracle(w)
+    assert_close(out.reshape(ref.shape), ref, qd, f"shared prefix D64 G{hq // hkv}")
+    assert_lse_close(lse.reshape(-1), ref_lse, qd, f"shared prefix D64 G{hq // hkv}")
 
 
 def test_no_shared_pages_is_the_plain_decode():
