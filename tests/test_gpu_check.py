@@ -156,3 +156,36 @@ def test_gather_bad_page(check_on):
     row[6] = -3
     with pytest.raises(PkvError, match=r"gather block_table\[0\]\[6\]"):
         pkv.gather_kv(d["k_cache"], d["v_cache"], row, 100)
+
+
+def test_shared_prefix_tables(monkeypatch):
+    """The shared-prefix call checks the shared pages and each sequence's own
+    pages and lengths; valid tables give the bits they give without the check."""
+    w = W.make_decode("cks", seed=67, batch=3, hq=16, hkv=2, d=128, dtype="bf16",
+                      hist_lens=[256 + 5, 256 + 100, 256 + 700], append=False, pool_slack=0.2,
+                      shared_prefix=256)
+    d = to_dev(w, DEV)
+    bt = d["block_table"]
+    prefix_table = bt[0, :16].contiguous()
+    own = bt[:, 16:]
+    lens = (d["context_lens"] - 256).contiguous()
+
+    def call(pt, ln):
+        out = pkv.paged_attn_decode_shared_prefix(d["q"], d["k_cache"], d["v_cache"], pt, 256,
+                                                  own, ln, 700, w.scale)
+        torch.cuda.synchronize()
+        return out
+
+    monkeypatch.setenv("PKV_CHECK", "1")
+    checked = call(prefix_table, lens)
+    bad = prefix_table.clone()
+    bad[5] = w.num_pages
+    with pytest.raises(PkvError, match="PKV_CHECK: prefix"):
+        call(bad, lens)
+    long_lens = lens.clone()
+    long_lens[1] = 701
+    with pytest.raises(PkvError, match="PKV_CHECK: decode context_lens"):
+        call(prefix_table, long_lens)
+    monkeypatch.setenv("PKV_CHECK", "0")
+    plain = call(prefix_table, lens)
+    assert torch.equal(bits(checked), bits(plain))
