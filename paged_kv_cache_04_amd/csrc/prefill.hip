@@ -198,20 +198,21 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   // Workgroups are handed to the 8 XCDs round-robin (workgroup i to XCD
   // i % 8), and each XCD has its own L2.  Default order: (b, kv head) fastest,
   // so when there are at least 8 such pairs each XCD keeps whole pairs and all
-  // their query tiles share the K/V stream in its L2.  With xcd_split, XCD x
-  // takes the x-th eighth of the query tiles of every pair instead: every XCD
-  // gets the same share of long and short sequences, and the tiles of one
-  // pair on one XCD still read the same keys together.  Each XCD walks the
-  // pairs one after another (pair-major), so that a long pair's workgroups
-  // start together instead of queueing, alternately with short ones, behind
-  // chains of short workgroups on the same CUs.
+  // their query tiles share the K/V stream in its L2.  With xcd_split (long
+  // chunks) the query tiles of each pair are dealt round the XCDs, tile mt to
+  // XCD (mt + pair) % 8: a pair's tiles on one XCD still read the same keys
+  // (all start at key 0), every XCD gets light and heavy causal tiles alike,
+  // and the first tile of the pairs -- all a one-row chunk has -- lands on a
+  // different XCD for each pair.  Each XCD walks the pairs one after another
+  // (pair-major), so that a long pair's workgroups start together instead of
+  // queueing behind chains of short workgroups on the same CUs.
   const int nbg = a.batch * a.num_kv_heads;
   int bg, mt, ks = 0;
   if (a.xcd_split) {
     const int x = blockIdx.x % 8, j = blockIdx.x / 8;
     bg = j / a.m_tiles_x;
-    mt = x * a.m_tiles_x + j % a.m_tiles_x;
-    if (mt >= a.m_tiles) return;     // padding of the last XCD's range
+    mt = 8 * (j % a.m_tiles_x) + ((x + 8 - (bg & 7)) & 7);
+    if (mt >= a.m_tiles) return;     // padding past the last tile
   } else if constexpr (PFX) {        // key split next, so a split's row tiles share L2
     bg = blockIdx.x % nbg;
     const int id = blockIdx.x / nbg;
