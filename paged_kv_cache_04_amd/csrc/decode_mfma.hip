@@ -18,9 +18,14 @@
 //   S^T:  per page, 4 MFMAs (K-dim 128 = 4 x 32) of K (16 keys x 32 dims,
 //         straight from HBM into registers) and Q^T (32 dims x 16 heads, held
 //         in registers).  The dimension order inside each MFMA is permuted so
-//         that a lane's K operand is one contiguous 16-byte load; Q^T uses the
-//         same order.  Output: lane (n = l % 16, q = l / 16) holds the scores
-//         of head n for keys 4q .. 4q+3 of the page.
+//         that a lane's K operand is 16 contiguous bytes of its key row; Q^T
+//         uses the same order.  The loads themselves read whole 128-byte
+//         lines (8 rows per instruction, two lanes' groups per line), and a
+//         select plus a swap of the two 8-lane halves of each 16-lane row
+//         rebuild the operand: a load shaped as the operand would read a
+//         64-byte half of 16 lines, twice the L2 requests per byte.
+//         Output: lane (n = l % 16, q = l / 16) holds the scores of head n
+//         for keys 4q .. 4q+3 of the page.
 //   P^T:  the scores of both pages, exponentiated, are exactly the B operand
 //         of the PV MFMA (keys 4q..4q+3 of page A, then of page B), packed to
 //         f16/bf16 in place.
@@ -104,6 +109,12 @@ struct MCfg {
   static constexpr int KL = FP8 ? 2 : 4;       // 16-byte K loads per lane and page
   static constexpr int VD = PAGEB / 1024;      // 1-KiB direct loads per V page (4 / 2)
   static constexpr int NB = FP8 ? 3 : 2;       // steps (page pairs) in flight per wave
+  // non-temporal (streaming) hints, as measured on the 128K decode: 16-bit
+  // pools are fastest with both K loads and V copies streaming (~3% over
+  // neither); fp8 pools with only the V copies streaming (both streaming, or
+  // neither, is 10-15% slower there)
+  static constexpr bool K_NT = !FP8;
+  static constexpr bool V_NT = true;
   static constexpr int OPS = 2 * (KL + VD);    // memory instructions per step
   static_assert(NB * OPS <= 63, "vmcnt range");
 };
@@ -226,7 +237,7 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_mfma_kernel(DecodeArgs a) {
 
   // Loads of step s into register slot / LDS slot SLOT: K rows of both pages
   // into registers, V pages into this wave's LDS buffer of the slot.
-  auto issue = [&](int s, auto slot_tag) {
+  auto issue = [&](int s, auto slot_tag) __attribute__((always_inline)) {
     constexpr int SLOT = decltype(slot_tag)::value;
     if ((s & 31) == 0) {  // page ids of steps s .. s+31, staged in LDS
       const int v = p0 + 8 * (s + (lane >> 1)) + 2 * w + (lane & 1);
@@ -244,11 +255,16 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_mfma_kernel(DecodeArgs a) {
       if (v >= p1 || pid < 0 || pid >= a.num_pages) pid = 0;   // a readable page
       const int64_t blk = ((int64_t)pid * a.num_kv_heads + g) * head_block;
       const char* kbase = (const char*)a.k_cache + blk;
-      // K operand: lane (key n, group q) reads 16 contiguous bytes per load
+      // K rows: loads 2L and 2L + 1 read the 128-byte line L of rows 0 .. 7
+      // and 8 .. 15, whole: lane (n, q) of load 2L + x reads row 8x + n % 8,
+      // bytes 128L + 64((n / 8) ^ x) + 16q .. +15 (k_operand rebuilds the
+      // MFMA layout from the pair)
 #pragma unroll
       for (int j = 0; j < C::KL; ++j) {
-        const int off = n * C::ROW + (C::FP8 ? 64 * j + 16 * q : 64 * j + 16 * q);
-        kr[SLOT][h][j] = __builtin_bit_cast(u32x4_t, load16_stream(kbase + off));
+        const int x = j & 1;
+        const int off = ((n & 7) + 8 * x) * C::ROW + 128 * (j >> 1) + 64 * ((n >> 3) ^ x) + 16 * q;
+        kr[SLOT][h][j] =
+            __builtin_bit_cast(u32x4_t, C::K_NT ? load16_stream(kbase + off) : load16(kbase + off));
       }
       // V page: 1-KiB direct copies; lane i fills LDS bytes 16i .. 16i+15 of
       // the copy, i.e. physical row r / chunk c, holding logical chunk c ^ swz
@@ -266,11 +282,36 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_mfma_kernel(DecodeArgs a) {
           const int row = pos >> 8, pg = (pos >> 5) & 7, half = (pos >> 4) & 1;
           src = row * 256 + (((pg ^ row) & 7) << 5) + (half << 4);
         }
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            vr, (void __attribute__((address_space(3)))*)(dst + c * 1024), 16, (uint32_t)src, 0,
-            0, 0);
+        lds_u8* to = dst + c * 1024;
+        // the cache policy is an immediate: one literal per form
+        if constexpr (C::V_NT)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (void __attribute__((address_space(3)))*)to,
+                                                   16, (uint32_t)src, 0, 0, 2);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (void __attribute__((address_space(3)))*)to,
+                                                   16, (uint32_t)src, 0, 0, 0);
       }
     }
+  };
+
+  // K operand of row n, bytes 64j + 16q .. +15 of the row, from the load
+  // pair (X, Y) of line j / 2: the first half of a line sits in X for rows
+  // 0 .. 7 and in Y for rows 8 .. 15, each in its own lane; the second half
+  // sits in the lane n ^ 8 of X (rows 0 .. 7) or Y (rows 8 .. 15)
+  auto k_operand = [&](u32x4_t xr, u32x4_t yr, int j) __attribute__((always_inline)) {
+    u32x4_t r;
+    const bool lo = n < 8;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (j & 1) {
+        const uint32_t xs = (uint32_t)__builtin_amdgcn_mov_dpp((int)xr[e], kDppRowRor8, 0xF, 0xF, true);
+        const uint32_t ys = (uint32_t)__builtin_amdgcn_mov_dpp((int)yr[e], kDppRowRor8, 0xF, 0xF, true);
+        r[e] = lo ? xs : ys;
+      } else {
+        r[e] = lo ? xr[e] : yr[e];
+      }
+    }
+    return r;
   };
 
   auto vis = [&](int t) {
@@ -280,7 +321,7 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_mfma_kernel(DecodeArgs a) {
 
   // Step s from slot SLOT; `later` = steps issued after it (their memory
   // instructions may still be in flight).
-  auto compute = [&](int s, int later, auto slot_tag) {
+  auto compute = [&](int s, int later, auto slot_tag) __attribute__((always_inline)) {
     constexpr int SLOT = decltype(slot_tag)::value;
     // wait for this step's loads (K registers and V copies)
     if (later >= 2) __builtin_amdgcn_s_waitcnt(((2 * C::OPS) & 15) | (((2 * C::OPS) >> 4) << 14) | 0x0F70);
@@ -318,18 +359,22 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       sacc[h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      u32x4_t kop[C::KL];
+#pragma unroll
+      for (int j = 0; j < C::KL; ++j)
+        kop[j] = k_operand(kr[SLOT][h][j & ~1], kr[SLOT][h][j | 1], j);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         u32x4_t av;
         if constexpr (C::FP8) {
-          const u32x4_t raw = kr[SLOT][h][j >> 1];
+          const u32x4_t raw = kop[j >> 1];
           const uint32_t w0 = raw[2 * (j & 1)], w1 = raw[2 * (j & 1) + 1];
           av[0] = CT::template cvt2<QT, false>(w0);
           av[1] = CT::template cvt2<QT, true>(w0);
           av[2] = CT::template cvt2<QT, false>(w1);
           av[3] = CT::template cvt2<QT, true>(w1);
         } else {
-          av = kr[SLOT][h][j];
+          av = kop[j];
         }
         sacc[h] = M::run(av, qb[j], sacc[h]);
       }
