@@ -2,7 +2,11 @@
 
 One step is one pass of the decode hot path over one batch: kv_append of one
 new token per sequence, the split-KV partial decode over every stored key
-(the appended one included), and the log-sum-exp merge.  The default workload
+(the appended one included), and the log-sum-exp merge.  The new tokens are
+stored by the decode launch itself (pkv_paged_attn_decode_append_partials:
+the workgroup that reads a sequence's last page writes the row first), so a
+step is two launches; --separate-append times kv_append as a launch of its
+own instead (three launches, the same results bit for bit).  The default workload
 is Llama-3-70B's per-GPU head share at 128K context: batch 8, 16 query / 2 KV
 heads, head_dim 128, fp16 K/V in 16-token pages, 131072 keys per sequence.
 
@@ -96,6 +100,8 @@ def parse():
                     help="comma-separated extra rows to measure: prefill, fp8prefill, fp8, "
                          "window, mixed, prefix ('' or 'none' for none)")
     ap.add_argument("--prefill", action="store_true", help="same as --extras prefill")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="store the new tokens with their own kv_append launch")
     ap.add_argument("--graph", action="store_true",
                     help="time the steps as HIP graph replays instead of eager launches")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -154,9 +160,16 @@ def main():
     # one call to each entry point per step, arguments marshalled once
     o_parts, l_parts, _ = pkv.paged_attn_decode_partials(
         *dargs, split_tokens=args.split_tokens, workspace=workspace)
+    fused = has_append and not args.separate_append
     call_append = (pkv.binding.prepare_kv_append(kc, vc, k_new, v_new, slots)
-                   if has_append else None)
-    call_partials = pkv.binding.prepare_decode_partials(*dargs, args.split_tokens, workspace)
+                   if has_append and not fused else None)
+    if fused:
+        call_partials = pkv.binding.prepare_decode_append_partials(
+            q, kc, vc, k_new, v_new, bt, cl, w.max_context_len, w.scale, args.split_tokens,
+            workspace)
+    else:
+        call_partials = pkv.binding.prepare_decode_partials(*dargs, args.split_tokens,
+                                                            workspace)
     call_merge = pkv.binding.prepare_merge_states(o_parts, l_parts, out, lse)
 
     def step(ev=None):
@@ -192,9 +205,14 @@ def main():
     if args.graph:
         # the same three calls per step, replayed as one HIP graph: no launch gaps
         def issue_step():
-            if has_append:
-                pkv.binding.prepare_kv_append(kc, vc, k_new, v_new, slots)()
-            pkv.binding.prepare_decode_partials(*dargs, args.split_tokens, workspace)()
+            if fused:
+                pkv.binding.prepare_decode_append_partials(
+                    q, kc, vc, k_new, v_new, bt, cl, w.max_context_len, w.scale,
+                    args.split_tokens, workspace)()
+            else:
+                if has_append:
+                    pkv.binding.prepare_kv_append(kc, vc, k_new, v_new, slots)()
+                pkv.binding.prepare_decode_partials(*dargs, args.split_tokens, workspace)()
             pkv.binding.prepare_merge_states(o_parts, l_parts, out, lse)()
         t0 = time.perf_counter()
         ms_per_step = _graph_us(issue_step, args.steps, args.warmup) / 1e3
@@ -210,7 +228,10 @@ def main():
     _, warm_event_us = _event_times(call_partials, 10)
 
     kv_bytes = A.decode_kv_bytes(w.context_lens.tolist(), w.num_kv_heads, w.head_dim, w.dtype)
-    achieved = kv_bytes / (kern_avg_us * 1e-6) / 1e9
+    # the fused launch also reads the new rows and stores them in the pools
+    kern_bytes = kv_bytes + (A.append_bytes(w.batch, w.num_kv_heads, w.head_dim, w.dtype)
+                             if fused else 0)
+    achieved = kern_bytes / (kern_avg_us * 1e-6) / 1e9
     tokens_per_s = w.batch / (ms_per_step * 1e-3)
 
     traffic = None
@@ -277,14 +298,17 @@ def main():
                    "head_dim": w.head_dim, "page_size": w.page_size, "n_split": n_split,
                    "split_tokens": args.split_tokens},
         "kv_gbps": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-        "roofline": {"bound": "hbm", "kernel": f"{_decode_kernel_name(w)} (split-KV partials)",
+        "roofline": {"bound": "hbm",
+                     "kernel": f"{_decode_kernel_name(w)} (split-KV partials"
+                               f"{', storing the new tokens' if fused else ''})",
                      "achieved": round(achieved, 1), "peak": A.HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / A.HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": kv_bytes,
+                     "algorithmic_bytes_per_launch": kern_bytes,
                      "kernel_avg_us": round(kern_avg_us, 2),
                      "in_step_event_us": round(step_kern_us, 2)},
+        "step_launches": (2 if fused or not has_append else 3),
         "cold_cache": {"event_us": round(cold_us, 2), "warm_event_us": round(warm_event_us, 2),
-                       "achieved_gbps": round(kv_bytes / (cold_us * 1e-6) / 1e9, 1)},
+                       "achieved_gbps": round(kern_bytes / (cold_us * 1e-6) / 1e9, 1)},
         "cpu_baseline": cpu,
         "parity": parity,
         "host_wall_s": round(wall, 4),
@@ -330,7 +354,8 @@ def _kernel_sha() -> str:
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_04_amd", "csrc")
-    for name in ("decode.hip", "decode_mfma.hip", "pkv_device.h", "pkv_internal.h"):
+    for name in ("decode.hip", "decode_mfma.hip", "pkv_device.h", "pkv_internal.h",
+                 "pkv_append.h"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -516,22 +541,36 @@ def bench_fp8(args, dev, sample):
     o_parts, l_parts, _ = pkv.paged_attn_decode_partials(
         q, kc, vc, bt, cl, w.max_context_len, w.scale, workspace=ws, k_scale=w.k_scale,
         v_scale=w.v_scale)
-    c_app = pkv.binding.prepare_kv_append_quant(kc, vc, k_new, v_new, slots, w.k_scale,
-                                                w.v_scale)
-    c_part = pkv.binding.prepare_decode_partials(q, kc, vc, bt, cl, w.max_context_len, w.scale,
-                                                 0, ws, w.k_scale, w.v_scale)
+    # the step: the decode launch that also quantizes and stores the new
+    # tokens (or, with --separate-append, kv_append_quant before it), the merge
+    sep = args.separate_append
+
+    def parts():
+        if sep:
+            return pkv.binding.prepare_decode_partials(q, kc, vc, bt, cl, w.max_context_len,
+                                                       w.scale, 0, ws, w.k_scale, w.v_scale)
+        return pkv.binding.prepare_decode_append_partials(q, kc, vc, k_new, v_new, bt, cl,
+                                                          w.max_context_len, w.scale, 0, ws,
+                                                          w.k_scale, w.v_scale)
+
+    def app():
+        return pkv.binding.prepare_kv_append_quant(kc, vc, k_new, v_new, slots, w.k_scale,
+                                                   w.v_scale)
+
+    c_app = app() if sep else None
+    c_part = parts()
     c_merge = pkv.binding.prepare_merge_states(o_parts, l_parts, out)
 
     def step():
-        c_app()
+        if c_app is not None:
+            c_app()
         c_part()
         c_merge()
 
     def issue_step():
-        pkv.binding.prepare_kv_append_quant(kc, vc, k_new, v_new, slots, w.k_scale,
-                                            w.v_scale)()
-        pkv.binding.prepare_decode_partials(q, kc, vc, bt, cl, w.max_context_len, w.scale, 0, ws,
-                                            w.k_scale, w.v_scale)()
+        if sep:
+            app()()
+        parts()()
         pkv.binding.prepare_merge_states(o_parts, l_parts, out)()
 
     eager_us, _ = _event_times(step, 30, warmup=10)
@@ -540,6 +579,8 @@ def bench_fp8(args, dev, sample):
     part_us = _back_to_back_us(c_part, 30)
     cold_us = _cold_event_us(c_part, 20)
     kv_bytes = sum(w.context_lens.tolist()) * 2 * w.num_kv_heads * w.head_dim * 1
+    if not sep:   # f16 rows read, fp8 rows stored
+        kv_bytes += w.batch * w.num_kv_heads * w.head_dim * 2 * (2 + 1)
     res = {"workload": "Llama-3-70B per-GPU share at 128K over fp8 (OCP e4m3) pools with fp32 "
                        "scales: batch 8, 16 q / 2 kv heads, head_dim 128, f16 queries, page 16, "
                        "131072 keys per sequence (131071 stored + 1 quantized on append)",

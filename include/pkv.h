@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define PKV_VERSION 3
+#define PKV_VERSION 4
 
 /*
  * Element types.  The fp8 types are the OCP 8-bit floats (E4M3 without
@@ -264,6 +264,46 @@ int pkv_paged_attn_decode_partials_ex(const pkv_cache_desc* desc, const void* k_
                                       int32_t max_context_len, float scale,
                                       int32_t split_tokens, const pkv_decode_opts* opts,
                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * paged_attn_decode_append, paged_attn_decode_append_partials -- a decode
+ * step whose new tokens are stored by the decode launch itself.  The result
+ * equals kv_append (kv_append_quant for fp8 caches) of each sequence's newest
+ * token followed by paged_attn_decode_ex (paged_attn_decode_partials_ex),
+ * bit for bit, with one kernel launch fewer.  A step of page 2, section 5.2
+ * stores the new token's K/V in its page (allocated ahead) and then attends
+ * it with the rest; that token sits at position L - 1 of its sequence,
+ * L = context_lens[b], so only the decode workgroup whose split ends at that
+ * page reads it.  That workgroup stores the row before it loads anything.
+ * For each b with 1 <= L and every KV head g, with
+ * s = block_table[b][(L - 1) / P] * P + (L - 1) % P:
+ *     k_cache[s / P][g][s % P][:] = k_new[b][g][:]   (same for V)
+ * (fp8 caches: each element divided by opts->k_scale (v_scale) in IEEE fp32
+ * and rounded to the fp8 code, as kv_append_quant does).
+ *   k_cache, v_cache : device, updated in place (the row at L - 1 only).
+ *   k_new, v_new     : device [batch][H_kv][D] of opts->q_dtype (the cache
+ *                      dtype, except for fp8 caches: f16 or bf16), 16-byte
+ *                      aligned.
+ * Other arguments, layouts and errors are as for paged_attn_decode_ex and
+ * paged_attn_decode_partials_ex.  L = 0 stores nothing.  A length or page the
+ * decode flags as invalid (NaN output rows) stores nothing for that sequence.
+ * Two sequences whose newest tokens map to the same slot race, as two equal
+ * slots do in kv_append.
+ */
+int pkv_paged_attn_decode_append(const pkv_cache_desc* desc, void* k_cache, void* v_cache,
+                                 const void* k_new, const void* v_new, const void* q,
+                                 int32_t batch, int32_t num_q_heads, const int32_t* block_table,
+                                 int32_t block_table_stride, const int32_t* context_lens,
+                                 int32_t max_context_len, float scale, int32_t split_tokens,
+                                 const pkv_decode_opts* opts, void* out, float* lse_out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+int pkv_paged_attn_decode_append_partials(
+    const pkv_cache_desc* desc, void* k_cache, void* v_cache, const void* k_new,
+    const void* v_new, const void* q, int32_t batch, int32_t num_q_heads,
+    const int32_t* block_table, int32_t block_table_stride, const int32_t* context_lens,
+    int32_t max_context_len, float scale, int32_t split_tokens, const pkv_decode_opts* opts,
+    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * kv_append_quant -- kv_append into an fp8 cache from wider new tokens.

@@ -17,6 +17,8 @@ from .binding import (  # noqa: F401
     kv_append_quant,
     merge_states,
     paged_attn_decode,
+    paged_attn_decode_append,
+    paged_attn_decode_append_partials,
     paged_attn_decode_partials,
     paged_attn_decode_shared_prefix,
     paged_attn_mixed,

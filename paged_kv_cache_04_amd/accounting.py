@@ -39,6 +39,12 @@ def decode_kv_bytes(context_lens: Iterable[int], num_kv_heads: int, head_dim: in
     return sum(int(l) for l in context_lens) * per
 
 
+def append_bytes(n_tokens: int, num_kv_heads: int, head_dim: int, dtype: str) -> int:
+    """HBM bytes of storing n_tokens new K and V rows of the same type: each
+    row is read from the new-token buffer and written to its page slot."""
+    return 2 * n_tokens * num_kv_heads * head_dim * DTYPE_BYTES[dtype] * 2
+
+
 def decode_unique_kv_bytes(page_lists, context_lens, num_kv_heads: int, head_dim: int,
                            page_size: int, dtype: str) -> int:
     """Bytes of distinct physical pages touched (shared-prefix pages once)."""

@@ -88,6 +88,11 @@ def lib():
         L.pkv_paged_attn_decode_shared_prefix.argtypes = [dp, vp, vp, vp, i32, i32, vp, i32, vp,
                                                           i32, vp, i32, f32, i32, op, vp, vp, vp,
                                                           sz, vp]
+        L.pkv_paged_attn_decode_append.argtypes = [dp, vp, vp, vp, vp, vp, i32, i32, vp, i32,
+                                                   vp, i32, f32, i32, op, vp, vp, vp, sz, vp]
+        L.pkv_paged_attn_decode_append_partials.argtypes = [dp, vp, vp, vp, vp, vp, i32, i32,
+                                                            vp, i32, vp, i32, f32, i32, op, vp,
+                                                            sz, vp]
         for name in ("pkv_kv_append", "pkv_gather_kv", "pkv_decode_plan", "pkv_paged_attn_decode",
                      "pkv_paged_attn_decode_partials", "pkv_merge_states",
                      "pkv_paged_attn_prefill_chunk", "pkv_validate_tables",
@@ -95,7 +100,8 @@ def lib():
                      "pkv_paged_attn_decode_partials_ex", "pkv_kv_append_quant",
                      "pkv_paged_attn_mixed", "pkv_decode_split_for_lens",
                      "pkv_paged_attn_prefill_chunk_ex", "pkv_paged_attn_mixed_ex",
-                     "pkv_decode_shared_prefix_plan", "pkv_paged_attn_decode_shared_prefix"):
+                     "pkv_decode_shared_prefix_plan", "pkv_paged_attn_decode_shared_prefix",
+                     "pkv_paged_attn_decode_append", "pkv_paged_attn_decode_append_partials"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -317,6 +323,73 @@ def paged_attn_decode_partials(q, k_cache, v_cache, block_table, context_lens,
     return o_parts, lse_parts, workspace
 
 
+def _append_common(q, k_cache, v_cache, k_new, v_new, block_table, context_lens,
+                   max_context_len, scale, split_tokens, k_scale, v_scale, window, sink):
+    """Checks and the leading C arguments shared by the decode-with-append calls."""
+    desc, batch, hq = _decode_common(q, k_cache, v_cache, block_table, context_lens,
+                                     max_context_len)
+    _dev(k_new, "k_new", q.dtype)
+    _dev(v_new, "v_new", q.dtype)
+    if (k_new.shape != (batch, desc.num_kv_heads, desc.head_dim)
+            or v_new.shape != k_new.shape):
+        raise ValueError("k_new/v_new must be [B][H_kv][D]")
+    opts = decode_opts(q.dtype, k_cache.dtype, k_scale, v_scale, window, sink)
+    common = (C.byref(desc), _p(k_cache), _p(v_cache), _p(k_new), _p(v_new), _p(q), batch, hq,
+              _p(block_table), int(block_table.shape[1]), _p(context_lens),
+              int(max_context_len), float(scale), int(split_tokens),
+              C.byref(opts) if opts is not None else None)
+    return desc, batch, hq, opts, common
+
+
+def paged_attn_decode_append(q, k_cache, v_cache, k_new, v_new, block_table, context_lens,
+                             max_context_len: int, scale: float, split_tokens: int = 0,
+                             out=None, lse_out=None, workspace=None, return_lse: bool = False,
+                             k_scale: float = 1.0, v_scale: float = 1.0, window: int = 0,
+                             sink: int = 0):
+    """pkv_paged_attn_decode_append: stores k_new[b] / v_new[b] ([B][H_kv][D],
+    q's dtype) at position context_lens[b] - 1 of each sequence (quantized by
+    the scales for fp8 caches) and decodes, in the decode's own launches.
+    Returns out (and lse) as paged_attn_decode does."""
+    desc, batch, hq, opts, common = _append_common(
+        q, k_cache, v_cache, k_new, v_new, block_table, context_lens, max_context_len, scale,
+        split_tokens, k_scale, v_scale, window, sink)
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse_out is None:
+        lse_out = torch.empty((batch, hq), dtype=torch.float32, device=q.device)
+    _, ws_bytes = decode_plan(desc, batch, hq, max_context_len, split_tokens, opts)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pkv_paged_attn_decode_append(*common, _p(out), _p(lse_out), _p(workspace),
+                                              ws_len, _stream()))
+    return (out, lse_out) if return_lse else out
+
+
+def paged_attn_decode_append_partials(q, k_cache, v_cache, k_new, v_new, block_table,
+                                      context_lens, max_context_len: int, scale: float,
+                                      split_tokens: int = 0, workspace=None,
+                                      k_scale: float = 1.0, v_scale: float = 1.0,
+                                      window: int = 0, sink: int = 0):
+    """pkv_paged_attn_decode_append_partials: the append and the first pass.
+    Returns (o_parts, lse_parts, workspace) as paged_attn_decode_partials."""
+    desc, batch, hq, opts, common = _append_common(
+        q, k_cache, v_cache, k_new, v_new, block_table, context_lens, max_context_len, scale,
+        split_tokens, k_scale, v_scale, window, sink)
+    n_split, _ = decode_plan(desc, batch, hq, max_context_len, split_tokens, opts)
+    ob, total = partials_bytes(batch, hq, n_split, desc.head_dim)
+    if workspace is None:
+        workspace = torch.empty(total, dtype=torch.uint8, device=q.device)
+    ws_len = workspace.numel() * workspace.element_size()
+    _check(lib().pkv_paged_attn_decode_append_partials(*common, _p(workspace), ws_len,
+                                                       _stream()))
+    rows = batch * hq
+    o_parts = workspace[:rows * n_split * desc.head_dim * 4].view(torch.float32).view(
+        rows, n_split, desc.head_dim)
+    lse_parts = workspace[ob:ob + rows * n_split * 4].view(torch.float32).view(rows, n_split)
+    return o_parts, lse_parts, workspace
+
+
 def merge_states(o_parts, lse_parts, out_dtype=torch.float32, out=None, lse_out=None,
                  return_lse: bool = False):
     """pkv_merge_states.  o_parts [rows][n][D] float32, lse_parts [rows][n]."""
@@ -527,6 +600,22 @@ def prepare_decode_partials(q, k_cache, v_cache, block_table, context_lens,
         args = common + (C.byref(opts), _p(workspace), ws_len, _stream())
     return PreparedCall(fn, args,
                         (desc, opts, q, k_cache, v_cache, block_table, context_lens, workspace))
+
+
+def prepare_decode_append_partials(q, k_cache, v_cache, k_new, v_new, block_table,
+                                   context_lens, max_context_len: int, scale: float,
+                                   split_tokens: int, workspace, k_scale: float = 1.0,
+                                   v_scale: float = 1.0, window: int = 0,
+                                   sink: int = 0) -> PreparedCall:
+    _dev(workspace, "workspace")
+    desc, _, _, opts, common = _append_common(
+        q, k_cache, v_cache, k_new, v_new, block_table, context_lens, max_context_len, scale,
+        split_tokens, k_scale, v_scale, window, sink)
+    ws_len = workspace.numel() * workspace.element_size()
+    return PreparedCall(lib().pkv_paged_attn_decode_append_partials,
+                        common + (_p(workspace), ws_len, _stream()),
+                        (desc, opts, q, k_cache, v_cache, k_new, v_new, block_table,
+                         context_lens, workspace))
 
 
 def prepare_kv_append_quant(k_cache, v_cache, k_new, v_new, slots, k_scale: float,

@@ -62,6 +62,7 @@
 // the tail of the last page.
 #include "pkv_device.h"
 #include "pkv_internal.h"
+#include "pkv_append.h"
 
 namespace pkv {
 
@@ -255,6 +256,13 @@ __global__ __launch_bounds__(NW * 64, (DecodeCfg<QT, CT, D, G>::OCC)) void decod
     return;
   }
   if (tid == 0) bad_flag = 0;
+  // the split that ends at the last visited page holds position L - 1: store
+  // the newest token there first (all of this workgroup's loads come after)
+  if (a.k_new != nullptr && !len_bad && L > 0 && p1 == n_vp) {
+    append_newest<QT, CT, D>(a, b, g, L, tid, NW * 64);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
 
   // row layout: lane = tk * 8 + c
   const int c = lane & (C::KL - 1);

@@ -49,6 +49,7 @@
 // a window cuts.
 #include "pkv_device.h"
 #include "pkv_internal.h"
+#include "pkv_append.h"
 
 namespace pkv {
 
@@ -202,6 +203,13 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_mfma_kernel(DecodeArgs a) {
     return;
   }
   if (tid == 0) bad_flag = 0;
+  // the split that ends at the last visited page holds position L - 1: store
+  // the newest token there first (all of this workgroup's loads come after)
+  if (a.k_new != nullptr && !len_bad && L > 0 && p1 == n_vp) {
+    append_newest<QT, CT, D>(a, b, g, L, tid, NW * 64);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
 
   // Q^T operand: lane (head n, group q), MFMA j holds the 8 dims the K
   // operand of the same MFMA uses (16-bit: 32j + 8q ..; fp8: 64(j/2) + 16q +

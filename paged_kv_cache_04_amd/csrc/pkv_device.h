@@ -128,6 +128,7 @@ struct TFP8E4M3 {
   static constexpr int bytes = 1;
   static constexpr bool is_f16 = false;
   static constexpr bool is_fp8 = true;
+  static constexpr bool is_e4m3 = true;
   template <typename QT, bool HI>
   static __device__ __forceinline__ uint32_t cvt2(uint32_t w) {
     if constexpr (QT::is_f16)
@@ -141,6 +142,7 @@ struct TFP8E5M2 {
   static constexpr int bytes = 1;
   static constexpr bool is_f16 = false;
   static constexpr bool is_fp8 = true;
+  static constexpr bool is_e4m3 = false;
   template <typename QT, bool HI>
   static __device__ __forceinline__ uint32_t cvt2(uint32_t w) {
     if constexpr (QT::is_f16)
@@ -149,6 +151,48 @@ struct TFP8E5M2 {
       return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.f, HI));
   }
 };
+
+// Four fp32 values to four fp8 codes (byte e from y[e]): values beyond the
+// largest finite one are clipped to it first (the conversion itself rounds
+// to nearest even and does not saturate), NaN becomes 0x7F.
+template <bool E4M3>
+__device__ __forceinline__ uint32_t fp8_pack4(const float (&y)[4]) {
+  constexpr float kMax = E4M3 ? 448.f : 57344.f;
+  float c[4];
+  uint32_t nan_mask = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    nan_mask |= (y[e] != y[e]) ? (0xffu << (8 * e)) : 0u;
+    c[e] = fminf(fmaxf(y[e], -kMax), kMax);
+  }
+  uint32_t w;
+  if constexpr (E4M3) {
+    w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+    w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], (int)w, true);
+  } else {
+    w = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c[0], c[1], 0, false);
+    w = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c[2], c[3], (int)w, true);
+  }
+  return (w & ~nan_mask) | (0x7f7f7f7fu & nan_mask);
+}
+
+// Source element i of a 16-byte vector group, widened exactly to fp32.
+template <typename ST>
+__device__ __forceinline__ float src_elem(const u32x4 (&v)[4], int i);
+template <>
+__device__ __forceinline__ float src_elem<TF32>(const u32x4 (&v)[4], int i) {
+  return u2f(v[i / 4].w[i % 4]);
+}
+template <>
+__device__ __forceinline__ float src_elem<TF16>(const u32x4 (&v)[4], int i) {
+  const uint32_t w = v[i / 8].w[(i % 8) / 2];
+  return (i & 1) ? TF16::hi(w) : TF16::lo(w);
+}
+template <>
+__device__ __forceinline__ float src_elem<TBF16>(const u32x4 (&v)[4], int i) {
+  const uint32_t w = v[i / 8].w[(i % 8) / 2];
+  return (i & 1) ? TBF16::hi(w) : TBF16::lo(w);
+}
 
 // Store one float as element type TT at p[idx].
 template <typename TT>

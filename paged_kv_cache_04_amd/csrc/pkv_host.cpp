@@ -368,7 +368,19 @@ pkv::DecodeArgs decode_args(const pkv_cache_desc* desc, const void* k_cache,
   a.sink = dc.opts.sink;
   a.part_stride = plan.n_split;
   a.part_offset = 0;
+  a.k_quant = dc.opts.k_scale;
+  a.v_quant = dc.opts.v_scale;
   return a;
+}
+
+// The newest-token rows of the decode-with-append calls: both or neither
+// (plain decode), 16-byte aligned when the batch is not empty.
+int check_new_rows(int32_t batch, const void* k_new, const void* v_new, bool append) {
+  if (!append || batch == 0) return PKV_OK;
+  if (!k_new || !v_new) return fail(PKV_ERR_INVALID, "k_new / v_new is NULL");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(PKV_ERR_INVALID, "k_new and v_new must be 16-byte aligned");
+  return PKV_OK;
 }
 
 // The decode kernel for these types and shapes: matrix cores for grouped
@@ -384,12 +396,14 @@ int decode_impl(const pkv_cache_desc* desc, const void* k_cache, const void* v_c
                 const void* q, int32_t batch, int32_t num_q_heads, const int32_t* block_table,
                 int32_t block_table_stride, const int32_t* context_lens, int32_t max_context_len,
                 float scale, int32_t split_tokens, const pkv_decode_opts* opts, void* out,
-                float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
+                float* lse_out, void* workspace, size_t workspace_bytes, void* stream,
+                const void* k_new = nullptr, const void* v_new = nullptr, bool append = false) {
   DecodeCommon dc;
   if (int rc = check_decode(desc, k_cache, v_cache, q, batch, num_q_heads, block_table,
                             block_table_stride, context_lens, max_context_len, scale,
                             split_tokens, opts, &dc))
     return rc;
+  if (int rc = check_new_rows(batch, k_new, v_new, append)) return rc;
   if (batch == 0) return ok();
   if (!out) return fail(PKV_ERR_INVALID, "out is NULL");
   if (check_mode())
@@ -399,6 +413,8 @@ int decode_impl(const pkv_cache_desc* desc, const void* k_cache, const void* v_c
       return rc;
   pkv::DecodeArgs a = decode_args(desc, k_cache, v_cache, q, num_q_heads, block_table,
                                   block_table_stride, context_lens, scale, dc);
+  a.k_new = append ? k_new : nullptr;
+  a.v_new = append ? v_new : nullptr;
   hipStream_t s = (hipStream_t)stream;
   const int qdt = dc.opts.q_dtype;
   if (dc.plan.n_split == 1) {
@@ -430,12 +446,14 @@ int partials_impl(const pkv_cache_desc* desc, const void* k_cache, const void* v
                   int32_t block_table_stride, const int32_t* context_lens,
                   int32_t max_context_len, float scale, int32_t split_tokens,
                   const pkv_decode_opts* opts, void* workspace, size_t workspace_bytes,
-                  void* stream) {
+                  void* stream, const void* k_new = nullptr, const void* v_new = nullptr,
+                  bool append = false) {
   DecodeCommon dc;
   if (int rc = check_decode(desc, k_cache, v_cache, q, batch, num_q_heads, block_table,
                             block_table_stride, context_lens, max_context_len, scale,
                             split_tokens, opts, &dc))
     return rc;
+  if (int rc = check_new_rows(batch, k_new, v_new, append)) return rc;
   if (batch == 0) return ok();
   if (!workspace || workspace_bytes < dc.plan.ws_bytes)
     return fail(PKV_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes,
@@ -448,6 +466,8 @@ int partials_impl(const pkv_cache_desc* desc, const void* k_cache, const void* v
       return rc;
   pkv::DecodeArgs a = decode_args(desc, k_cache, v_cache, q, num_q_heads, block_table,
                                   block_table_stride, context_lens, scale, dc);
+  a.k_new = append ? k_new : nullptr;
+  a.v_new = append ? v_new : nullptr;
   a.direct = 0;
   a.o_part = (float*)workspace;
   a.lse_part = (float*)((char*)workspace + dc.plan.o_bytes);
@@ -644,6 +664,29 @@ int pkv_paged_attn_decode_partials_ex(const pkv_cache_desc* desc, const void* k_
   return partials_impl(desc, k_cache, v_cache, q, batch, num_q_heads, block_table,
                        block_table_stride, context_lens, max_context_len, scale, split_tokens,
                        opts, workspace, workspace_bytes, stream);
+}
+
+int pkv_paged_attn_decode_append(const pkv_cache_desc* desc, void* k_cache, void* v_cache,
+                                 const void* k_new, const void* v_new, const void* q,
+                                 int32_t batch, int32_t num_q_heads, const int32_t* block_table,
+                                 int32_t block_table_stride, const int32_t* context_lens,
+                                 int32_t max_context_len, float scale, int32_t split_tokens,
+                                 const pkv_decode_opts* opts, void* out, float* lse_out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(desc, k_cache, v_cache, q, batch, num_q_heads, block_table,
+                     block_table_stride, context_lens, max_context_len, scale, split_tokens, opts,
+                     out, lse_out, workspace, workspace_bytes, stream, k_new, v_new, true);
+}
+
+int pkv_paged_attn_decode_append_partials(
+    const pkv_cache_desc* desc, void* k_cache, void* v_cache, const void* k_new,
+    const void* v_new, const void* q, int32_t batch, int32_t num_q_heads,
+    const int32_t* block_table, int32_t block_table_stride, const int32_t* context_lens,
+    int32_t max_context_len, float scale, int32_t split_tokens, const pkv_decode_opts* opts,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  return partials_impl(desc, k_cache, v_cache, q, batch, num_q_heads, block_table,
+                       block_table_stride, context_lens, max_context_len, scale, split_tokens,
+                       opts, workspace, workspace_bytes, stream, k_new, v_new, true);
 }
 
 int pkv_kv_append_quant(const pkv_cache_desc* desc, void* k_cache, void* v_cache,

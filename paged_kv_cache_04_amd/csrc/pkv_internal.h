@@ -34,6 +34,13 @@ struct DecodeArgs {
   float* lse_part;              // [B*H_q][part_stride]    part_offset + ks
   int32_t part_stride;          // parts per row (n_split unless other parts share the rows)
   int32_t part_offset;
+  // Newest-token append (null: none): row b of k_new / v_new [B][H_kv][D]
+  // (q's type) goes to position context_lens[b] - 1 before it is attended;
+  // fp8 caches quantize it by the pool scales k_quant / v_quant.
+  const void* k_new;
+  const void* v_new;
+  float k_quant;
+  float v_quant;
 };
 
 struct PrefillArgs {

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
     assert len(names) >= 10
     for n in names:
         assert hasattr(L, n), n
-    assert L.pkv_version() == 3
+    assert L.pkv_version() == 4
 
 
 def err(L):
@@ -360,3 +360,38 @@ def test_shared_prefix_plan_and_args(L):
     assert _shared(L, desc(), batch=0) == 0
     assert _shared(L, desc(dtype=3), batch=0) == -1             # fp8: needs the query type
     assert _shared(L, desc(dtype=3), _opts(1, 0.5, 0.5), batch=0) == 0
+
+
+def _decode_append(L, d, opts=None, *, partials=False, batch=2, hq=4, stride=8, max_len=100,
+                   split=0, k_new=FAKE, v_new=FAKE, ws=None, ws_bytes=0, out=FAKE):
+    lead = (C.byref(d), FAKE, FAKE, k_new, v_new, FAKE, batch, hq, FAKE, stride, FAKE, max_len,
+            0.125, split, C.byref(opts) if opts is not None else None)
+    if partials:
+        return L.pkv_paged_attn_decode_append_partials(*lead, ws, ws_bytes, None)
+    return L.pkv_paged_attn_decode_append(*lead, out, None, ws, ws_bytes, None)
+
+
+def test_decode_append_args(L):
+    """The decode-with-append calls check what the decode calls check, plus
+    the new rows: both present and 16-byte aligned (an empty batch needs
+    neither)."""
+    d = desc()
+    for partials in (False, True):
+        kw = dict(partials=partials)
+        assert _decode_append(L, d, k_new=None, **kw) == -1
+        assert "k_new" in err(L)
+        assert _decode_append(L, d, v_new=None, **kw) == -1
+        assert _decode_append(L, d, k_new=C.c_void_p((1 << 20) + 2), **kw) == -1
+        assert "aligned" in err(L)
+        assert _decode_append(L, d, hq=3, **kw) == -1                 # not a multiple of H_kv
+        assert _decode_append(L, d, max_len=8 * 16 + 1, **kw) == -1   # beyond stride * P
+        assert _decode_append(L, d, batch=0, k_new=None, v_new=None, **kw) == 0
+        f8 = desc(dtype=3)
+        assert _decode_append(L, f8, **kw) == -1                      # fp8 needs a q type
+        assert _decode_append(L, f8, _opts(q_dtype=1, k_scale=0.0), **kw) == -1
+        assert _decode_append(L, f8, _opts(q_dtype=1), batch=0, **kw) == 0
+    # the full call needs out, and a workspace once split; the partials need a workspace
+    assert _decode_append(L, d, out=None) == -1
+    assert _decode_append(L, d, max_len=128, split=32) == -3
+    assert _decode_append(L, d, partials=True) == -3
+

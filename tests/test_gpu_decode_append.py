@@ -1,0 +1,174 @@
+"""Decode with the newest token stored by the decode launch itself.
+
+A decode step stores each sequence's new token in its page, allocated
+ahead, then attends it with the rest (page 2, section 5.2).
+pkv_paged_attn_decode_append must leave the pools and give the outputs of
+kv_append (kv_append_quant for fp8 pools) followed by the decode, bit for
+bit, and match the oracle's append and decode within tolerance.
+
+Cases:
+- both decode kernels: matrix cores at G 8, the vector kernel at G 1, 2 and 4;
+- f32 at head_dim 64;
+- fp8 pools with their quantizing append;
+- a window, and unsplit and split launches;
+- new tokens at the first row of a page, at its last row, and as the only key;
+- the partials form;
+- a sequence of length 0, and one whose last page id is out of range: both
+  store nothing, and their rows are as the separate calls give them."""
+import pytest
+import torch
+
+import paged_kv_cache_04_amd as pkv
+from oracle import pkvref
+from paged_kv_cache_04_amd import workloads as W
+
+from helpers import assert_close, assert_lse_close, bits, host_threads, to_dev
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+# L - 1 lands on: row 0 of page 0 (L 1), the last row of page 0 (L 16), row 0
+# of page 1 (L 17), and inside later pages
+LENS = [0, 15, 16, 299, 1999, 4999]        # stored tokens; one more is appended
+
+CASES = [
+    # qd, kvd, hq, hkv, d, split, window, sink
+    ("f16", "", 16, 2, 128, 0, 0, 0),               # matrix cores, G 8, split by the plan
+    ("bf16", "", 16, 2, 128, 8192, 0, 0),           # matrix cores, one split (direct)
+    ("bf16", "", 32, 8, 128, 256, 0, 0),            # vector kernel, G 4, split
+    ("f16", "", 8, 4, 128, 0, 0, 0),                # vector kernel, G 2
+    ("f32", "", 4, 4, 64, 128, 0, 0),               # f32, G 1, head_dim 64
+    ("f16", "fp8_e4m3", 16, 2, 128, 0, 0, 0),       # fp8, matrix cores
+    ("bf16", "fp8_e5m2", 8, 4, 128, 256, 0, 0),     # fp8, vector kernel
+    ("f16", "", 16, 2, 128, 0, 700, 16),            # window + sink, matrix cores
+    ("bf16", "", 32, 8, 128, 0, 300, 32),           # window + sink, vector kernel
+]
+
+
+def make(qd, kvd, hq, hkv, d, seed, lens=LENS):
+    kw = dict(kv_dtype=kvd, k_scale=3 / 128, v_scale=5 / 256) if kvd else {}
+    return W.make_decode("append", seed=seed, batch=len(lens), hq=hq, hkv=hkv, d=d, dtype=qd,
+                         hist_lens=lens, append=True, pool_slack=0.05, **kw)
+
+
+def separate_append(w, x):
+    if w.is_fp8:
+        pkv.kv_append_quant(x["k_cache"], x["v_cache"], x["k_new"], x["v_new"], x["slots"],
+                            w.k_scale, w.v_scale)
+    else:
+        pkv.kv_append(x["k_cache"], x["v_cache"], x["k_new"], x["v_new"], x["slots"])
+
+
+def oracle_append(w):
+    if w.is_fp8:
+        kq = torch.from_numpy(pkvref.quant_fp8(w.kv_dtype, w.dtype, w.k_new, w.k_scale))
+        vq = torch.from_numpy(pkvref.quant_fp8(w.kv_dtype, w.dtype, w.v_new, w.v_scale))
+        pkvref.kv_append(w.kv_dtype, w.k_cache, w.v_cache, kq.view(W.DTYPES[w.kv_dtype]),
+                         vq.view(W.DTYPES[w.kv_dtype]), w.slots)
+    else:
+        pkvref.kv_append(w.dtype, w.k_cache, w.v_cache, w.k_new, w.v_new, w.slots)
+
+
+def same_bits(a, b, what):
+    assert torch.equal(bits(a), bits(b)), what
+
+
+@pytest.mark.parametrize("qd,kvd,hq,hkv,d,split,window,sink", CASES)
+def test_decode_append_matches_separate_calls_and_oracle(qd, kvd, hq, hkv, d, split, window,
+                                                         sink):
+    w = make(qd, kvd, hq, hkv, d, seed=141)
+    sep, fused = to_dev(w, DEV), to_dev(w, DEV)
+    opt = dict(split_tokens=split, return_lse=True, k_scale=w.k_scale, v_scale=w.v_scale,
+               window=window, sink=sink)
+    separate_append(w, sep)
+    ref = pkv.paged_attn_decode(sep["q"], sep["k_cache"], sep["v_cache"], sep["block_table"],
+                                sep["context_lens"], w.max_context_len, w.scale, **opt)
+    got = pkv.paged_attn_decode_append(fused["q"], fused["k_cache"], fused["v_cache"],
+                                       fused["k_new"], fused["v_new"], fused["block_table"],
+                                       fused["context_lens"], w.max_context_len, w.scale, **opt)
+    torch.cuda.synchronize()
+    what = f"{qd}/{kvd or qd} G {hq // hkv} D {d} split {split} window {window}"
+    same_bits(fused["k_cache"], sep["k_cache"], what + ": K pool")
+    same_bits(fused["v_cache"], sep["v_cache"], what + ": V pool")
+    same_bits(got[0], ref[0], what + ": out")
+    same_bits(got[1], ref[1], what + ": lse")
+
+    oracle_append(w)
+    same_bits(fused["k_cache"].cpu(), w.k_cache, what + ": K pool vs oracle append")
+    same_bits(fused["v_cache"].cpu(), w.v_cache, what + ": V pool vs oracle append")
+    o, lse = pkvref.decode_ex(w.dtype, w.kv_dtype, w.k_cache, w.v_cache, w.q, w.block_table,
+                              w.context_lens, w.scale, k_scale=w.k_scale, v_scale=w.v_scale,
+                              window=window, sink=sink, n_threads=host_threads())
+    assert_close(got[0].reshape(o.shape), o, w.dtype, what)
+    assert_lse_close(got[1].reshape(-1), lse, w.dtype, what)
+
+
+@pytest.mark.parametrize("qd,kvd,hq,hkv", [("f16", "", 16, 2), ("bf16", "", 32, 8),
+                                           ("bf16", "fp8_e4m3", 16, 2)])
+def test_decode_append_partials(qd, kvd, hq, hkv):
+    """The partials form stores the rows and writes the partials of the
+    separate calls, bit for bit; merging them gives the full call's output."""
+    w = make(qd, kvd, hq, hkv, 128, seed=142)
+    sep, fused = to_dev(w, DEV), to_dev(w, DEV)
+    sc = dict(k_scale=w.k_scale, v_scale=w.v_scale)
+    separate_append(w, sep)
+    po, pl, _ = pkv.paged_attn_decode_partials(sep["q"], sep["k_cache"], sep["v_cache"],
+                                               sep["block_table"], sep["context_lens"],
+                                               w.max_context_len, w.scale, split_tokens=512,
+                                               **sc)
+    fo, fl, _ = pkv.paged_attn_decode_append_partials(
+        fused["q"], fused["k_cache"], fused["v_cache"], fused["k_new"], fused["v_new"],
+        fused["block_table"], fused["context_lens"], w.max_context_len, w.scale,
+        split_tokens=512, **sc)
+    torch.cuda.synchronize()
+    same_bits(fused["k_cache"], sep["k_cache"], "K pool")
+    same_bits(fused["v_cache"], sep["v_cache"], "V pool")
+    same_bits(fo, po, "o_parts")
+    same_bits(fl, pl, "lse_parts")
+    out = pkv.merge_states(fo, fl, out_dtype=fused["q"].dtype)
+    full = pkv.paged_attn_decode(sep["q"], sep["k_cache"], sep["v_cache"], sep["block_table"],
+                                 sep["context_lens"], w.max_context_len, w.scale,
+                                 split_tokens=512, **sc)
+    torch.cuda.synchronize()
+    same_bits(out.reshape(full.shape), full, "merged partials vs full call")
+
+
+@pytest.mark.parametrize("hq,hkv", [(16, 2), (32, 8)])
+@pytest.mark.parametrize("split", [0, 256])
+def test_decode_append_stores_nothing_for_empty_or_bad_rows(hq, hkv, split):
+    """Sequence 1 has length 0 and sequence 3's last page id is outside the
+    pool: neither stores a row; the others do.  The separate calls skip them
+    through slot -1.  Pools, outputs and lse match bit for bit (row 1: 0 and
+    -inf; row 3: NaN, the decode's flag for a bad page)."""
+    w = make("f16", "", hq, hkv, 128, seed=143, lens=[40, 0, 300, 700, 17])
+    sep, fused = to_dev(w, DEV), to_dev(w, DEV)
+    last3 = (int(w.context_lens[3]) - 1) // 16
+    for x in (sep, fused):
+        x["context_lens"][1] = 0
+        x["block_table"][3, last3] = w.num_pages + 5
+    sep["slots"][1] = -1
+    sep["slots"][3] = -1
+    separate_append(w, sep)
+    opt = dict(split_tokens=split, return_lse=True)
+    ref = pkv.paged_attn_decode(sep["q"], sep["k_cache"], sep["v_cache"], sep["block_table"],
+                                sep["context_lens"], w.max_context_len, w.scale, **opt)
+    got = pkv.paged_attn_decode_append(fused["q"], fused["k_cache"], fused["v_cache"],
+                                       fused["k_new"], fused["v_new"], fused["block_table"],
+                                       fused["context_lens"], w.max_context_len, w.scale, **opt)
+    torch.cuda.synchronize()
+    same_bits(fused["k_cache"], sep["k_cache"], "K pool")
+    same_bits(fused["v_cache"], sep["v_cache"], "V pool")
+    same_bits(got[0], ref[0], "out")
+    same_bits(got[1], ref[1], "lse")
+    assert bool((got[0][1] == 0).all()) and bool(torch.isneginf(got[1][1]).all())
+    assert bool(torch.isnan(got[0][3].float()).all())
+    # the other rows are finite and their new tokens were stored
+    for b in (0, 2, 4):
+        assert bool(torch.isfinite(got[0][b].float()).all())
+    # the pool outside the stored slots is unchanged
+    untouched = torch.ones(w.num_pages, 16, dtype=torch.bool)
+    for b in (0, 2, 4):
+        s = int(w.slots[b])
+        untouched[s // 16, s % 16] = False
+    kc = w.k_cache.permute(0, 2, 1, 3)[untouched]
+    same_bits(fused["k_cache"].cpu().permute(0, 2, 1, 3)[untouched], kc, "K pool elsewhere")
