@@ -320,7 +320,8 @@ def main():
         extras.append("prefill")
     sample = not args.no_cpu_baseline
     if "window" in extras:
-        reuse = (w, (q, kc, vc, bt, cl)) if args.config == "llama70b_128k" else None
+        reuse = ((w, (q, kc, vc, bt, cl, k_new, v_new)) if args.config == "llama70b_128k"
+                 else None)
         line["window_decode"] = bench_window(args, dev, sample, reuse)
     del kc, vc, workspace
     torch.cuda.empty_cache()
@@ -340,11 +341,9 @@ def main():
 
 def _decode_kernel_name(w) -> str:
     """The decode kernel the library runs for this workload: the matrix-core
-    kernel for 8 or 16 query heads per KV head (fp8 pools from 4), else the
-    vector kernel."""
+    kernel for 4, 8 or 16 query heads per KV head, else the vector kernel."""
     g = w.num_q_heads // w.num_kv_heads
-    mfma = (w.head_dim == 128 and w.dtype in ("f16", "bf16")
-            and (g in (8, 16) or (w.is_fp8 and g == 4)))
+    mfma = w.head_dim == 128 and w.dtype in ("f16", "bf16") and g in (4, 8, 16)
     return "decode_mfma_kernel" if mfma else "decode_kernel"
 
 
@@ -573,7 +572,11 @@ def bench_fp8(args, dev, sample):
         parts()()
         pkv.binding.prepare_merge_states(o_parts, l_parts, out)()
 
-    eager_us, _ = _event_times(step, 30, warmup=10)
+    # steps back to back between one event pair (as the main row's total is
+    # taken); an event pair around every step would add its host cost, which
+    # exceeds a short step's GPU time
+    event_us, _ = _event_times(step, 30, warmup=10)
+    eager_us = _back_to_back_us(step, 30)
     step_us = _graph_us(issue_step, 30) if args.graph else eager_us
     _, part_med = _event_times(c_part, 30)
     part_us = _back_to_back_us(c_part, 30)
@@ -586,6 +589,7 @@ def bench_fp8(args, dev, sample):
                        "131072 keys per sequence (131071 stored + 1 quantized on append)",
            "tokens_per_s": round(w.batch / (step_us * 1e-6), 1), "ms_per_step": round(
                step_us / 1e3, 5), "eager_ms_per_step": round(eager_us / 1e3, 5),
+           "per_step_event_ms": round(event_us / 1e3, 5),
            "n_split": n_split, "kernel_median_us": round(part_med, 2),
            "roofline": _hbm_roofline("decode_mfma_kernel<f16 q, fp8 e4m3 cache> (split-KV partials)",
                                      kv_bytes, part_us),
@@ -614,16 +618,18 @@ def bench_window(args, dev, sample, reuse=None):
     import torch
 
     import paged_kv_cache_04_amd as pkv
+    from paged_kv_cache_04_amd import accounting as A
     from paged_kv_cache_04_amd import workloads as W
 
     window, sink = 4096, 128
     if reuse is not None:      # the main 128K workload, its append already applied
-        w, (q, kc, vc, bt, cl) = reuse
+        w, (q, kc, vc, bt, cl, k_new, v_new) = reuse
     else:
         w = W.make("llama70b_128k")
         kc, vc = w.k_cache.to(dev), w.v_cache.to(dev)
         q, bt, cl = w.q.to(dev), w.block_table.to(dev), w.context_lens.to(dev)
-        pkv.kv_append(kc, vc, w.k_new.to(dev), w.v_new.to(dev), w.slots.to(dev))
+        k_new, v_new = w.k_new.to(dev), w.v_new.to(dev)
+        pkv.kv_append(kc, vc, k_new, v_new, w.slots.to(dev))
         if sample:
             from oracle import pkvref
             pkvref.kv_append(w.dtype, w.k_cache, w.v_cache, w.k_new, w.v_new, w.slots)
@@ -635,8 +641,17 @@ def bench_window(args, dev, sample, reuse=None):
     out = torch.empty_like(q)
     o_parts, l_parts, _ = pkv.paged_attn_decode_partials(
         q, kc, vc, bt, cl, w.max_context_len, w.scale, workspace=ws, window=window, sink=sink)
-    c_part = pkv.binding.prepare_decode_partials(q, kc, vc, bt, cl, w.max_context_len, w.scale,
-                                                 0, ws, window=window, sink=sink)
+    # a decode step as in the main row: the partial launch also stores the new
+    # tokens (the same rows again: the pools keep their bits)
+    def parts():
+        if args.separate_append:
+            return pkv.binding.prepare_decode_partials(q, kc, vc, bt, cl, w.max_context_len,
+                                                       w.scale, 0, ws, window=window, sink=sink)
+        return pkv.binding.prepare_decode_append_partials(q, kc, vc, k_new, v_new, bt, cl,
+                                                          w.max_context_len, w.scale, 0, ws,
+                                                          window=window, sink=sink)
+
+    c_part = parts()
     c_merge = pkv.binding.prepare_merge_states(o_parts, l_parts, out)
 
     def step():
@@ -644,11 +659,14 @@ def bench_window(args, dev, sample, reuse=None):
         c_merge()
 
     def issue_step():
-        pkv.binding.prepare_decode_partials(q, kc, vc, bt, cl, w.max_context_len, w.scale, 0, ws,
-                                            window=window, sink=sink)()
+        parts()()
         pkv.binding.prepare_merge_states(o_parts, l_parts, out)()
 
-    eager_us, _ = _event_times(step, 30, warmup=10)
+    # steps back to back between one event pair (as the main row's total is
+    # taken); an event pair around every step would add its host cost, which
+    # exceeds a short step's GPU time
+    event_us, _ = _event_times(step, 30, warmup=10)
+    eager_us = _back_to_back_us(step, 30)
     step_us = _graph_us(issue_step, 30) if args.graph else eager_us
     _, part_med = _event_times(c_part, 30)
     part_us = _back_to_back_us(c_part, 30)
@@ -656,11 +674,15 @@ def bench_window(args, dev, sample, reuse=None):
     es = 4 if w.dtype == "f32" else 2
     vis = [min(L, window) + min(sink, max(0, L - window)) for L in w.context_lens.tolist()]
     kv_bytes = sum(vis) * 2 * w.num_kv_heads * w.head_dim * es
+    if not args.separate_append:
+        kv_bytes += A.append_bytes(w.batch, w.num_kv_heads, w.head_dim, w.dtype)
     res = {"workload": "the 128K decode workload with a sliding window: each query sees its "
                        "4096 most recent keys and the first 128 (page 4, section 2.3's local "
-                       "window + global tokens); pages wholly outside are not read",
+                       "window + global tokens); pages wholly outside are not read; the step "
+                       "stores the new tokens in its partial launch",
            "tokens_per_s": round(w.batch / (step_us * 1e-6), 1),
            "ms_per_step": round(step_us / 1e3, 5), "eager_ms_per_step": round(eager_us / 1e3, 5),
+           "per_step_event_ms": round(event_us / 1e3, 5),
            "n_split": n_split,
            "kernel_median_us": round(part_med, 2),
            "roofline": _hbm_roofline("decode_mfma_kernel (windowed split-KV partials)", kv_bytes,

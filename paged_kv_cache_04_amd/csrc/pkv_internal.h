@@ -92,9 +92,9 @@ hipError_t launch_gather(int dtype, int head_dim, int num_kv_heads, int64_t num_
 hipError_t launch_decode(int kv_dtype, int q_dtype, int head_dim, int group, int batch,
                          const DecodeArgs& a, hipStream_t stream);
 
-// Decode on the matrix cores (16-bit queries, head_dim 128, G = 8 or 16 with
-// any 16-bit or fp8 pool, G = 4 with fp8 pools); same arguments and results
-// as launch_decode, which builds G <= 8 only.
+// Decode on the matrix cores (16-bit queries, head_dim 128, G = 4, 8 or 16
+// with any 16-bit or fp8 pool); same arguments and results as launch_decode,
+// which builds G <= 8 only.
 bool decode_mfma_supported(int kv_dtype, int q_dtype, int head_dim, int group);
 hipError_t launch_decode_mfma(int kv_dtype, int q_dtype, int group, int batch,
                               const DecodeArgs& a, hipStream_t stream);

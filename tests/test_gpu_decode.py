@@ -64,9 +64,10 @@ def test_decode_llama70b_128k_parity():
     ("f32", 64, 2, 2), ("f32", 128, 8, 1), ("f32", 64, 8, 1), ("f32", 128, 4, 2),
     ("f16", 64, 4, 2), ("f16", 128, 2, 1), ("f16", 64, 8, 1), ("f16", 128, 1, 1),
     ("bf16", 64, 16, 2), ("bf16", 128, 6, 3), ("bf16", 64, 1, 1), ("bf16", 128, 16, 16),
-    # G = 8 and 16 at head_dim 128: the matrix-core kernel
+    ("bf16", 64, 8, 2),                      # G = 4 at head_dim 64: the vector kernel
+    # G = 4, 8 and 16 at head_dim 128: the matrix-core kernel
     ("f16", 128, 16, 2), ("bf16", 128, 8, 1), ("bf16", 128, 32, 4), ("f16", 128, 32, 2),
-    ("bf16", 128, 16, 1),
+    ("bf16", 128, 16, 1), ("f16", 128, 8, 2), ("bf16", 128, 4, 1),
 ])
 def test_decode_shapes(dtype, d, hq, hkv):
     """Every (dtype, head_dim, group) kernel variant, ragged lengths spanning

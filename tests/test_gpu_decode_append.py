@@ -7,7 +7,8 @@ kv_append (kv_append_quant for fp8 pools) followed by the decode, bit for
 bit, and match the oracle's append and decode within tolerance.
 
 Cases:
-- both decode kernels: matrix cores at G 8, the vector kernel at G 1, 2 and 4;
+- both decode kernels: matrix cores at G 4 and 8, the vector kernel at G 1, 2
+  and 4 (head_dim 64);
 - f32 at head_dim 64;
 - fp8 pools with their quantizing append;
 - a window, and unsplit and split launches;
@@ -35,13 +36,15 @@ CASES = [
     # qd, kvd, hq, hkv, d, split, window, sink
     ("f16", "", 16, 2, 128, 0, 0, 0),               # matrix cores, G 8, split by the plan
     ("bf16", "", 16, 2, 128, 8192, 0, 0),           # matrix cores, one split (direct)
-    ("bf16", "", 32, 8, 128, 256, 0, 0),            # vector kernel, G 4, split
+    ("bf16", "", 32, 8, 128, 256, 0, 0),            # matrix cores, G 4, split
+    ("bf16", "", 32, 8, 64, 256, 0, 0),             # vector kernel, G 4, head_dim 64
     ("f16", "", 8, 4, 128, 0, 0, 0),                # vector kernel, G 2
     ("f32", "", 4, 4, 64, 128, 0, 0),               # f32, G 1, head_dim 64
     ("f16", "fp8_e4m3", 16, 2, 128, 0, 0, 0),       # fp8, matrix cores
     ("bf16", "fp8_e5m2", 8, 4, 128, 256, 0, 0),     # fp8, vector kernel
     ("f16", "", 16, 2, 128, 0, 700, 16),            # window + sink, matrix cores
-    ("bf16", "", 32, 8, 128, 0, 300, 32),           # window + sink, vector kernel
+    ("bf16", "", 32, 8, 128, 0, 300, 32),           # window + sink, matrix cores, G 4
+    ("f16", "", 8, 4, 128, 0, 300, 32),             # window + sink, vector kernel, G 2
 ]
 
 

@@ -30,9 +30,11 @@ def replay_matches(graph, outputs, eager, other_work, reps=4):
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("hq", [8, 16])
-def test_decode_step_graph(hq):
-    """append + split-KV partials + merge, as the decode step runs."""
+def test_decode_step_graph(hq, fused):
+    """append + split-KV partials + merge, as the decode step runs: three
+    launches, or two when the partial launch stores the new tokens."""
     w = W.make_decode("gr", seed=101 + hq, batch=4, hq=hq, hkv=2, d=128, dtype="f16",
                       hist_lens=[100, 1000, 3000, 5000], append=True, pool_slack=0.1)
     d = to_dev(w, DEV)
@@ -48,15 +50,20 @@ def test_decode_step_graph(hq):
     o_parts, l_parts, _ = pkv.paged_attn_decode_partials(*dargs, split_tokens=256, workspace=ws)
 
     def step_calls():
+        merge = B.prepare_merge_states(o_parts, l_parts, out, lse)
+        if fused:
+            return (B.prepare_decode_append_partials(d["q"], d["k_cache"], d["v_cache"],
+                                                     d["k_new"], d["v_new"], d["block_table"],
+                                                     d["context_lens"], w.max_context_len,
+                                                     w.scale, 256, ws), merge)
         return (B.prepare_kv_append(d["k_cache"], d["v_cache"], d["k_new"], d["v_new"],
                                     d["slots"]),
-                B.prepare_decode_partials(*dargs, 256, ws),
-                B.prepare_merge_states(o_parts, l_parts, out, lse))
+                B.prepare_decode_partials(*dargs, 256, ws), merge)
 
     for c in step_calls():
         c()
     torch.cuda.synchronize()
-    eager = (out.clone(), lse.clone())
+    eager = (out.clone(), lse.clone(), d["k_cache"].clone(), d["v_cache"].clone())
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -67,7 +74,10 @@ def test_decode_step_graph(hq):
     def other_work():
         pkv.paged_attn_decode(*dargs, split_tokens=0, out=other)
 
-    replay_matches(g, (out, lse), eager, other_work)
+    replay_matches(g, (out, lse), eager[:2], other_work)
+    # the replays stored the same rows again: the pools are as after the eager step
+    assert torch.equal(bits(d["k_cache"]), bits(eager[2]))
+    assert torch.equal(bits(d["v_cache"]), bits(eager[3]))
 
 
 def test_prefill_and_mixed_graph():

@@ -96,7 +96,8 @@ def check_pools(w, d, e, base):
 
 DECODE = [
     ("f16", "", 16, 2, [300, 2000, 5000]),          # matrix-core kernel, G = 8
-    ("bf16", "", 32, 8, [40, 700, 1500]),           # vector kernel, G = 4
+    ("bf16", "", 32, 8, [40, 700, 1500]),           # matrix cores, G = 4
+    ("bf16", "", 16, 8, [40, 700, 1500]),           # vector kernel, G = 2
     ("f16", "fp8_e4m3", 16, 2, [300, 2000, 5000]),  # fp8 pools, matrix cores
 ]
 

@@ -71,7 +71,7 @@ def cascade(w, d, prefix, split=0):
 
 
 CASES = [
-    ("bf16", None, 32, 8, 256, [0, 1, 15, 16, 100, 700]),    # G 4: vector decode for own pages
+    ("bf16", None, 32, 8, 256, [0, 1, 15, 16, 100, 700]),    # G 4: matrix-core decode for own pages
     ("f16", None, 16, 2, 1024, [5, 300, 2000, 40]),          # G 8
     ("bf16", None, 32, 2, 512, [3, 64, 1000]),               # G 16
     ("f16", "fp8_e4m3", 16, 2, 768, [10, 500]),              # fp8 pools, G 8
