@@ -9,8 +9,8 @@ The compact pool's page p becomes page base + p of a pool of base + n pages
 the append (bytes, and nothing written below base), gather, decode on both
 kernels (unsplit and split, with and without a window), the fp8 cache with its
 quantizing append, chunked prefill (16-bit and fp8 pools) and the mixed
-batch: bit for bit against the compact pool and within tolerance of the
-oracle."""
+batch, and the decode call that stores the newest tokens itself: bit for bit
+against the compact pool and within tolerance of the oracle."""
 import pytest
 import torch
 
@@ -139,6 +139,36 @@ def test_decode_and_gather_past_4gib(qd, kvd, hq, hkv, lens):
                                         sink=sink, n_threads=host_threads(), **scales)
         assert_close(res[1][0].reshape(ref.shape), ref, w.dtype, what)
         assert_lse_close(res[1][1].reshape(-1), ref_lse, w.dtype, what)
+
+
+@pytest.mark.parametrize("qd,kvd,hq,hkv", [("f16", "", 16, 2), ("bf16", "", 16, 8),
+                                           ("f16", "fp8_e4m3", 16, 2)])
+def test_decode_append_past_4gib(qd, kvd, hq, hkv):
+    """The decode launch that stores the newest tokens itself: the rows land
+    above 4 GiB, nothing below changes, and pools and outputs carry the bits
+    of the compact pool's run."""
+    kw = dict(kv_dtype=kvd, k_scale=3 / 128, v_scale=5 / 256) if kvd else {}
+    w = W.make_decode("bigapp", seed=134, batch=3, hq=hq, hkv=hkv, d=128, dtype=qd,
+                      hist_lens=[0, 1999, 4000], append=True, pool_slack=0.05, **kw)
+    d = to_dev(w, DEV)
+    e, base = lift(w, d)
+    res = []
+    for x in (d, e):
+        res.append(pkv.paged_attn_decode_append(x["q"], x["k_cache"], x["v_cache"], x["k_new"],
+                                                x["v_new"], x["block_table"],
+                                                x["context_lens"], w.max_context_len, w.scale,
+                                                split_tokens=512, return_lse=True,
+                                                k_scale=w.k_scale, v_scale=w.v_scale))
+    oracle_append(w)
+    check_pools(w, d, e, base)
+    assert torch.equal(bits(res[0][0]), bits(res[1][0])), "out differs from compact"
+    assert torch.equal(bits(res[0][1]), bits(res[1][1])), "lse differs from compact"
+    ref, ref_lse = pkvref.decode_ex(w.dtype, w.kv_dtype, w.k_cache, w.v_cache, w.q,
+                                    w.block_table, w.context_lens, w.scale,
+                                    k_scale=w.k_scale, v_scale=w.v_scale,
+                                    n_threads=host_threads())
+    assert_close(res[1][0].reshape(ref.shape), ref, w.dtype, "decode with append")
+    assert_lse_close(res[1][1].reshape(-1), ref_lse, w.dtype, "decode with append")
 
 
 @pytest.mark.parametrize("kind", ["prefill", "prefill fp8", "mixed"])
