@@ -69,6 +69,28 @@ def test_decode_bad_page(check_on):
         decode(w, d, split=0)
 
 
+@pytest.mark.parametrize("partials", [False, True])
+def test_decode_append_bad_last_page(check_on, partials):
+    """The decode that stores the newest tokens checks its tables first: a
+    bad id for the page that would receive a new token is reported, and
+    nothing is stored (the pools keep their bits)."""
+    w = W.make_decode("ck", seed=66, batch=3, hq=16, hkv=2, d=128, dtype="f16",
+                      hist_lens=[100, 300, 200], append=True, pool_slack=0.2)
+    last = (int(w.context_lens[2]) - 1) // 16
+    w.block_table[2, last] = -3
+    d = to_dev(w, DEV)
+    args = (d["q"], d["k_cache"], d["v_cache"], d["k_new"], d["v_new"], d["block_table"],
+            d["context_lens"], w.max_context_len, w.scale)
+    with pytest.raises(PkvError, match=rf"PKV_CHECK: decode block_table\[2\]\[{last}\]"):
+        if partials:
+            pkv.paged_attn_decode_append_partials(*args, split_tokens=64)
+        else:
+            pkv.paged_attn_decode_append(*args, split_tokens=64)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(d["k_cache"]), bits(w.k_cache))
+    assert torch.equal(bits(d["v_cache"]), bits(w.v_cache))
+
+
 def test_decode_length_over_bound(check_on):
     w = W.make_decode("ck", seed=64, batch=2, hq=8, hkv=2, d=128, dtype="bf16",
                       hist_lens=[100, 300], append=False, pool_slack=0.5)
