@@ -480,6 +480,9 @@ def test_kv_bytes_formula_reproduces_printed_sizes():
     assert accounting.kv_cache_gib(80, 8, 128, 131072, 2) == 40.0
     assert accounting.kv_bytes_per_token_layer(2, 128, 2) == 1024
     assert accounting.decode_kv_bytes([131072] * 8, 2, 128, "f16") == 1 << 30
+    # storing 8 new tokens: 8 tokens x 2 heads x 128 elements x 2 bytes, for K and V,
+    # read once from the new-token buffer and written once to the pool
+    assert accounting.append_bytes(8, 2, 128, "f16") == 8 * 2 * 128 * 2 * 2 * 2
 
 
 def test_prefill_pair_count():
