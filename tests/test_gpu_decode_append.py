@@ -15,7 +15,9 @@ Cases:
 - new tokens at the first row of a page, at its last row, and as the only key;
 - the partials form;
 - a sequence of length 0, and one whose last page id is out of range: both
-  store nothing, and their rows are as the separate calls give them."""
+  store nothing, and their rows are as the separate calls give them;
+- a closed form: with a window of 1 every query sees only the stored token,
+  so the output is v_new itself, bit for bit."""
 import pytest
 import torch
 
@@ -175,3 +177,28 @@ def test_decode_append_stores_nothing_for_empty_or_bad_rows(hq, hkv, split):
         untouched[s // 16, s % 16] = False
     kc = w.k_cache.permute(0, 2, 1, 3)[untouched]
     same_bits(fused["k_cache"].cpu().permute(0, 2, 1, 3)[untouched], kc, "K pool elsewhere")
+
+
+@pytest.mark.parametrize("qd,hq,hkv,d", [("f16", 16, 2, 128), ("bf16", 32, 8, 128),
+                                         ("f16", 8, 4, 128), ("f32", 4, 4, 64),
+                                         ("bf16", 16, 8, 64)])
+def test_decode_append_window_one_sees_only_the_new_token(qd, hq, hkv, d):
+    """With a window of 1 and no sink each query attends only the token the
+    launch has just stored (position L - 1), whose weight is 1: every query
+    head of KV head g returns v_new[b][g] exactly, and lse is that token's
+    scaled score.  Pins that the row was stored where the decode reads it."""
+    w = make(qd, "", hq, hkv, d, seed=144)
+    x = to_dev(w, DEV)
+    for split in (0, 64):
+        out, lse = pkv.paged_attn_decode_append(x["q"], x["k_cache"], x["v_cache"], x["k_new"],
+                                                x["v_new"], x["block_table"],
+                                                x["context_lens"], w.max_context_len, w.scale,
+                                                split_tokens=split, return_lse=True, window=1)
+        torch.cuda.synchronize()
+        g = hq // hkv
+        want = x["v_new"].repeat_interleave(g, dim=1)          # [B][H_q][D]
+        same_bits(out, want, f"{qd} G {g} D {d} split {split}: out vs v_new")
+        # lse = scale * q . k_new (one key), within the decode's tolerance
+        s = (x["q"].double() * x["k_new"].double().repeat_interleave(g, dim=1)).sum(-1)
+        assert_lse_close(lse.reshape(-1), (s * w.scale).reshape(-1).cpu().numpy(), w.dtype,
+                         f"{qd} G {g} D {d} split {split}")
