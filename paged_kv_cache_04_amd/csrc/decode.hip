@@ -533,11 +533,20 @@ __global__ __launch_bounds__(NW * 64, (DecodeCfg<QT, CT, D, G>::OCC)) void decod
 template <typename QT, typename CT, int D, bool WIN>
 hipError_t launch_w(int group, const dim3 grid, const DecodeArgs& a, hipStream_t stream) {
   const dim3 block(NW * 64);
+  // 16-bit queries at head_dim 128 run G = 4 and 8 on the matrix cores (see
+  // decode_mfma_supported): those instances are not built here
+  constexpr bool MC = QT::bytes == 2 && D == 128;
   switch (group) {
     case 1: hipLaunchKernelGGL((decode_kernel<QT, CT, D, 1, WIN>), grid, block, 0, stream, a); break;
     case 2: hipLaunchKernelGGL((decode_kernel<QT, CT, D, 2, WIN>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<QT, CT, D, 4, WIN>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((decode_kernel<QT, CT, D, 8, WIN>), grid, block, 0, stream, a); break;
+    case 4:
+      if constexpr (MC) return hipErrorInvalidValue;
+      else hipLaunchKernelGGL((decode_kernel<QT, CT, D, 4, WIN>), grid, block, 0, stream, a);
+      break;
+    case 8:
+      if constexpr (MC) return hipErrorInvalidValue;
+      else hipLaunchKernelGGL((decode_kernel<QT, CT, D, 8, WIN>), grid, block, 0, stream, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
