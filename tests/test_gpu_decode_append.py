@@ -17,7 +17,8 @@ Cases:
 - a sequence of length 0, and one whose last page id is out of range: both
   store nothing, and their rows are as the separate calls give them;
 - a closed form: with a window of 1 every query sees only the stored token,
-  so the output is v_new itself, bit for bit."""
+  so the output is v_new itself, bit for bit (fp8 pools: v_scale times the
+  stored code, the oracle's quantizer giving the code)."""
 import pytest
 import torch
 
@@ -202,3 +203,24 @@ def test_decode_append_window_one_sees_only_the_new_token(qd, hq, hkv, d):
         s = (x["q"].double() * x["k_new"].double().repeat_interleave(g, dim=1)).sum(-1)
         assert_lse_close(lse.reshape(-1), (s * w.scale).reshape(-1).cpu().numpy(), w.dtype,
                          f"{qd} G {g} D {d} split {split}")
+
+
+@pytest.mark.parametrize("qd,kvd,hq,hkv", [("f16", "fp8_e4m3", 16, 2), ("bf16", "fp8_e5m2", 32, 8),
+                                           ("f16", "fp8_e5m2", 8, 4)])
+def test_decode_append_fp8_window_one_returns_the_stored_codes(qd, kvd, hq, hkv):
+    """fp8 pools, window 1: the output is v_scale times the fp8 code the
+    launch stored for v_new (the oracle's quantizer gives the codes).  The
+    scales are short binary fractions, so code * v_scale is exact in fp32
+    and the output is that value rounded once to the query type."""
+    w = make(qd, kvd, hq, hkv, 128, seed=145)
+    x = to_dev(w, DEV)
+    out = pkv.paged_attn_decode_append(x["q"], x["k_cache"], x["v_cache"], x["k_new"],
+                                       x["v_new"], x["block_table"], x["context_lens"],
+                                       w.max_context_len, w.scale, window=1,
+                                       k_scale=w.k_scale, v_scale=w.v_scale)
+    torch.cuda.synchronize()
+    codes = torch.from_numpy(pkvref.quant_fp8(w.kv_dtype, w.dtype, w.v_new, w.v_scale))
+    vals = pkvref.to_double(w.kv_dtype, codes.view(W.DTYPES[w.kv_dtype])) * w.v_scale
+    want = torch.from_numpy(vals).to(W.DTYPES[w.dtype])
+    g = hq // hkv
+    same_bits(out.cpu(), want.repeat_interleave(g, dim=1), f"{kvd} G {g}: out vs v_scale * code")
