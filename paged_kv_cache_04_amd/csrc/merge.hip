@@ -54,21 +54,6 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
   const float* lp = lse_parts + row * n_parts;
   const float* op = o_parts + row * n_parts * (int64_t)D;
 
-  // this lane's parts k = grp, grp + NG, ... (at most MAXK of them), loaded
-  // before the row max is known so that both loads are in flight together
-  const int grp = lane / LPP, li = lane % LPP;
-  constexpr int MAXK = (kWaveRowParts + NG - 1) / NG;
-  float4 ov[MAXK];
-  float lv[MAXK];
-#pragma unroll
-  for (int i = 0; i < MAXK; ++i) {
-    const int k = grp + i * NG;
-    const bool in = k < n_parts;
-    ov[i] = in ? *reinterpret_cast<const float4*>(op + (int64_t)k * D + li * 4)
-               : make_float4(0.f, 0.f, 0.f, 0.f);
-    lv[i] = in ? lp[k] : -INFINITY;
-  }
-
   // row max and NaN check
   float mx = -INFINITY;
   int nan_seen = 0;
@@ -93,11 +78,12 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
   }
   const float wsum = wave_sum(ws);
 
+  const int grp = lane / LPP, li = lane % LPP;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-  for (int i = 0; i < MAXK; ++i) {     // parts in ascending k, as before
-    const float l = lv[i];
-    const float4 o = ov[i];
+#pragma unroll 4
+  for (int k = grp; k < n_parts; k += NG) {
+    const float l = lp[k];
+    const float4 o = *reinterpret_cast<const float4*>(op + (int64_t)k * D + li * 4);
     const bool skip = (l == -INFINITY);
     const float wk = skip ? 0.f : exp2_fast((l - M) * kLog2e);
     acc.x += skip ? 0.f : wk * o.x;
