@@ -235,9 +235,9 @@ int pkv_decode_plan_ex(const pkv_cache_desc* desc, int32_t batch, int32_t num_q_
  * visits (lens_host[b] keys of sequence b, window-aware under opts): when
  * every sequence visits as many pages it returns the automatic split;
  * otherwise a split that spreads them over about 1024 workgroups (four per
- * CU, balanced by the hardware), with at least 32 pages per split, adjusted
- * so that the decode runs an odd number of splits when its max_context_len is
- * the largest length (the XCDs then share the short sequences' work evenly).
+ * CU, balanced by the hardware), with at least 32 pages (512 keys) per
+ * split.  The decode hands out every sequence's first split before any
+ * second split, so the longest pieces of work start first.
  *   lens_host    : host int32 [batch], the lengths the decode will see
  *   opts         : as for decode_plan_ex (may be NULL)
  *   split_tokens : out, a multiple of P, to pass to decode_plan(_ex) and to

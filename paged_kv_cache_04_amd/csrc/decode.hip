@@ -202,11 +202,10 @@ __global__ __launch_bounds__(NW * 64, (DecodeCfg<QT, CT, D, G>::OCC)) void decod
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  int bid = blockIdx.x;
-  const int ks = bid % a.n_split;
-  bid /= a.n_split;
-  const int g = bid % a.num_kv_heads;
-  const int b = bid / a.num_kv_heads;
+  int ks, unit;
+  if (!decode_item(blockIdx.x, a, &ks, &unit)) return;   // padding workgroup
+  const int g = unit % a.num_kv_heads;
+  const int b = unit / a.num_kv_heads;
   const int hq0 = g * G;
 
   // A length outside [0, stride * P], or more visited pages than the grid
@@ -554,7 +553,8 @@ hipError_t launch_w(int group, const dim3 grid, const DecodeArgs& a, hipStream_t
 
 template <typename QT, typename CT, int D>
 hipError_t launch_g(int group, int batch, const DecodeArgs& a, hipStream_t stream) {
-  const int64_t blocks = (int64_t)batch * a.num_kv_heads * a.n_split;
+  (void)batch;
+  const int64_t blocks = decode_grid(a);
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)blocks);
   if (a.window > 0) return launch_w<QT, CT, D, true>(group, grid, a, stream);

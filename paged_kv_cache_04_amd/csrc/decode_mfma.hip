@@ -154,11 +154,10 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_mfma_kernel(DecodeArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15;       // head column (S^T, P^T, O^T) / key row (K operand)
   const int q = lane >> 4;       // 16-lane group
-  int bid = blockIdx.x;
-  const int ks = bid % a.n_split;
-  bid /= a.n_split;
-  const int g = bid % a.num_kv_heads;
-  const int b = bid / a.num_kv_heads;
+  int ks, unit;
+  if (!decode_item(blockIdx.x, a, &ks, &unit)) return;   // padding workgroup
+  const int g = unit % a.num_kv_heads;
+  const int b = unit / a.num_kv_heads;
   const int hq0 = g * G;
 
   int L = a.context_lens[b];
@@ -560,7 +559,8 @@ hipError_t launch_w(int group, const dim3 grid, const DecodeArgs& a, hipStream_t
 
 template <typename QT, typename CT>
 hipError_t launch_c(int group, int batch, const DecodeArgs& a, hipStream_t stream) {
-  const int64_t blocks = (int64_t)batch * a.num_kv_heads * a.n_split;
+  (void)batch;
+  const int64_t blocks = decode_grid(a);
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)blocks);
   if (a.window > 0) return launch_w<QT, CT, true>(group, grid, a, stream);

@@ -348,9 +348,11 @@ int check_decode(const pkv_cache_desc* desc, const void* k_cache, const void* v_
 pkv::DecodeArgs decode_args(const pkv_cache_desc* desc, const void* k_cache,
                             const void* v_cache, const void* q, int32_t num_q_heads,
                             const int32_t* block_table, int32_t stride,
-                            const int32_t* context_lens, float scale, const DecodeCommon& dc) {
+                            const int32_t* context_lens, float scale, const DecodeCommon& dc,
+                            int32_t batch) {
   const Plan& plan = dc.plan;
   pkv::DecodeArgs a{};
+  a.n_units = batch * desc->num_kv_heads;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
   a.q = q;
@@ -412,7 +414,7 @@ int decode_impl(const pkv_cache_desc* desc, const void* k_cache, const void* v_c
                                     (hipStream_t)stream))
       return rc;
   pkv::DecodeArgs a = decode_args(desc, k_cache, v_cache, q, num_q_heads, block_table,
-                                  block_table_stride, context_lens, scale, dc);
+                                  block_table_stride, context_lens, scale, dc, batch);
   a.k_new = append ? k_new : nullptr;
   a.v_new = append ? v_new : nullptr;
   hipStream_t s = (hipStream_t)stream;
@@ -465,7 +467,7 @@ int partials_impl(const pkv_cache_desc* desc, const void* k_cache, const void* v
                                     (hipStream_t)stream))
       return rc;
   pkv::DecodeArgs a = decode_args(desc, k_cache, v_cache, q, num_q_heads, block_table,
-                                  block_table_stride, context_lens, scale, dc);
+                                  block_table_stride, context_lens, scale, dc, batch);
   a.k_new = append ? k_new : nullptr;
   a.v_new = append ? v_new : nullptr;
   a.direct = 0;
@@ -599,21 +601,11 @@ int pkv_decode_split_for_lens(const pkv_cache_desc* desc, int32_t batch, int32_t
       return rc;
     pps = plan.pages_per_split;
   } else {
+    // about kUnevenWorkgroups equal splits over the pages the batch visits;
+    // the split-major grid hands the first splits (the longest work) out
+    // first and spreads every round over the XCDs
     pps = (total * desc->num_kv_heads + kUnevenWorkgroups - 1) / kUnevenWorkgroups;
     if (pps < kUnevenMinPages) pps = kUnevenMinPages;
-    // An odd number of splits: workgroup i runs on XCD i % 8 and a unit's
-    // splits are consecutive workgroups, so with n splits the first split of
-    // unit u lands on XCD (u * n) % 8; an odd n spreads the units' first
-    // splits -- all a short sequence has -- over every XCD, where an even n
-    // would stack them on a few.
-    const int64_t max_pages = ((int64_t)plan_len(max_len, o, P) + P - 1) / P;   // as make_plan
-    for (int64_t p = pps; p > kUnevenMinPages / 2; --p) {
-      const int64_t n = (max_pages + p - 1) / p;
-      if (n == 1 || (n & 1)) {
-        pps = p;
-        break;
-      }
-    }
   }
   if (pps * P > 0x7fffffff) return fail(PKV_ERR_INVALID, "split out of range");
   *split_tokens = (int32_t)(pps * P);
@@ -1080,7 +1072,7 @@ int pkv_paged_attn_decode_shared_prefix(
   }
   // each sequence's own pages: split-KV partials after the shared ones
   pkv::DecodeArgs a = decode_args(desc, k_cache, v_cache, q, num_q_heads, block_table,
-                                  block_table_stride, suffix_lens, scale, dc);
+                                  block_table_stride, suffix_lens, scale, dc, batch);
   a.direct = 0;
   a.o_part = o_part;
   a.lse_part = lse_part;

@@ -41,7 +41,32 @@ struct DecodeArgs {
   const void* v_new;
   float k_quant;
   float v_quant;
+  int32_t n_units;              // batch * H_kv
 };
+
+// Grid of a decode launch.  Work units are (sequence b, KV head g), unit =
+// b * H_kv + g, each cut into n_split splits.  The grid is split-major: all
+// first splits, then all second splits, and so on, each round covering the
+// units padded to a multiple of 8 and rotated by its split index.
+// Workgroups reach the 8 XCDs round-robin (workgroup i to XCD i % 8), so a
+// unit's splits land on different XCDs and every XCD gets a share of each
+// round; the hardware hands out the longest work (the first splits, full
+// length unless the sequence is short) before the sequences' remainders.
+// (A unit-major grid put the only split of every short sequence on the same
+// few XCDs whenever n_split was even.)
+inline int64_t decode_grid(const DecodeArgs& a) {
+  return ((int64_t)a.n_units + 7) / 8 * 8 * a.n_split;
+}
+
+// The (split ks, unit) of decode workgroup `bid`; false for a padding
+// workgroup, which has no work.
+__device__ __forceinline__ bool decode_item(int bid, const DecodeArgs& a, int* ks, int* unit) {
+  const int up = (a.n_units + 7) / 8 * 8;
+  const int k = bid / up, r = bid % up;
+  *ks = k;
+  *unit = (r - k % up + up) % up;
+  return *unit < a.n_units;
+}
 
 struct PrefillArgs {
   const void* k_cache;

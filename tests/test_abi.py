@@ -143,6 +143,7 @@ def test_split_for_lens(L):
                                 C.byref(ws)) == 0
     assert split([131072, 100000], opts=opts) == (0, 16 * math.ceil(265 / n.value))
     assert split([100, 200])[1] == 32 * 16                  # at least 32 pages per split
+    assert split([16 * 64, 160]) == (0, 32 * 16)            # never below 32 pages
     assert L.pkv_decode_plan(C.byref(d), 64, 32, 4096, 0, C.byref(n), C.byref(ws)) == 0
     assert split([4096] * 64, hq=32) == (0, 16 * math.ceil(256 / n.value))   # equal: automatic
     assert split([5, -1])[0] == -1
