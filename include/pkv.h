@@ -306,6 +306,35 @@ int pkv_paged_attn_decode_append_partials(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * paged_attn_decode_append_noalloc -- paged_attn_decode_append without a
+ * workspace argument, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The split-KV partials go to a static device array of
+ * pkv_noalloc_scratch_bytes() bytes (16 MiB), one per GPU, held until the
+ * process ends; the call itself allocates and frees nothing.  Arguments,
+ * layouts, results (bit for bit) and errors are those of
+ * paged_attn_decode_append with the same split_tokens, plus
+ * PKV_ERR_WORKSPACE when the split plan needs more than that array
+ * (batch * H_q * n_split * (D + 1) * 4 bytes, the partials rounded up to 256
+ * bytes; pass a larger split_tokens).  A plan with n_split == 1 needs none.
+ * Every call on a GPU uses that GPU's one array: calls that overlap on one
+ * GPU (on different streams, or from different threads) race and give
+ * unspecified results; calls on one stream are ordered and safe.  The first
+ * call on a device looks up the array's device address (no allocation).
+ */
+int pkv_paged_attn_decode_append_noalloc(const pkv_cache_desc* desc, void* k_cache,
+                                         void* v_cache, const void* k_new, const void* v_new,
+                                         const void* q, int32_t batch, int32_t num_q_heads,
+                                         const int32_t* block_table, int32_t block_table_stride,
+                                         const int32_t* context_lens, int32_t max_context_len,
+                                         float scale, int32_t split_tokens,
+                                         const pkv_decode_opts* opts, void* out, float* lse_out,
+                                         void* stream);
+
+/* Bytes of the static scratch array of paged_attn_decode_append_noalloc. */
+size_t pkv_noalloc_scratch_bytes(void);
+
+/*
  * kv_append_quant -- kv_append into an fp8 cache from wider new tokens.
  * For each i with s = slot_mapping[i] >= 0 (and < num_pages * P), every KV
  * head g and element d:

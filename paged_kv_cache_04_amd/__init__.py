@@ -16,8 +16,10 @@ from .binding import (  # noqa: F401
     kv_append,
     kv_append_quant,
     merge_states,
+    noalloc_scratch_bytes,
     paged_attn_decode,
     paged_attn_decode_append,
+    paged_attn_decode_append_noalloc,
     paged_attn_decode_append_partials,
     paged_attn_decode_partials,
     paged_attn_decode_shared_prefix,

@@ -93,6 +93,11 @@ def lib():
         L.pkv_paged_attn_decode_append_partials.argtypes = [dp, vp, vp, vp, vp, vp, i32, i32,
                                                             vp, i32, vp, i32, f32, i32, op, vp,
                                                             sz, vp]
+        L.pkv_paged_attn_decode_append_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, i32, i32,
+                                                           vp, i32, vp, i32, f32, i32, op, vp,
+                                                           vp, vp]
+        L.pkv_noalloc_scratch_bytes.restype = sz
+        L.pkv_noalloc_scratch_bytes.argtypes = []
         for name in ("pkv_kv_append", "pkv_gather_kv", "pkv_decode_plan", "pkv_paged_attn_decode",
                      "pkv_paged_attn_decode_partials", "pkv_merge_states",
                      "pkv_paged_attn_prefill_chunk", "pkv_validate_tables",
@@ -101,7 +106,8 @@ def lib():
                      "pkv_paged_attn_mixed", "pkv_decode_split_for_lens",
                      "pkv_paged_attn_prefill_chunk_ex", "pkv_paged_attn_mixed_ex",
                      "pkv_decode_shared_prefix_plan", "pkv_paged_attn_decode_shared_prefix",
-                     "pkv_paged_attn_decode_append", "pkv_paged_attn_decode_append_partials"):
+                     "pkv_paged_attn_decode_append", "pkv_paged_attn_decode_append_partials",
+                     "pkv_paged_attn_decode_append_noalloc"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -364,6 +370,31 @@ def paged_attn_decode_append(q, k_cache, v_cache, k_new, v_new, block_table, con
     _check(lib().pkv_paged_attn_decode_append(*common, _p(out), _p(lse_out), _p(workspace),
                                               ws_len, _stream()))
     return (out, lse_out) if return_lse else out
+
+
+def paged_attn_decode_append_noalloc(q, k_cache, v_cache, k_new, v_new, block_table,
+                                     context_lens, max_context_len: int, scale: float,
+                                     split_tokens: int = 0, out=None, lse_out=None,
+                                     return_lse: bool = False, k_scale: float = 1.0,
+                                     v_scale: float = 1.0, window: int = 0, sink: int = 0):
+    """pkv_paged_attn_decode_append_noalloc: paged_attn_decode_append with its
+    split partials in the library's static device array instead of a
+    workspace.  out and lse_out are the caller's (allocated here only when
+    not given)."""
+    desc, batch, hq, opts, common = _append_common(
+        q, k_cache, v_cache, k_new, v_new, block_table, context_lens, max_context_len, scale,
+        split_tokens, k_scale, v_scale, window, sink)
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse_out is None:
+        lse_out = torch.empty((batch, hq), dtype=torch.float32, device=q.device)
+    _check(lib().pkv_paged_attn_decode_append_noalloc(*common, _p(out), _p(lse_out), _stream()))
+    return (out, lse_out) if return_lse else out
+
+
+def noalloc_scratch_bytes() -> int:
+    """Size of the static scratch array of paged_attn_decode_append_noalloc."""
+    return int(lib().pkv_noalloc_scratch_bytes())
 
 
 def paged_attn_decode_append_partials(q, k_cache, v_cache, k_new, v_new, block_table,

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <unordered_set>
 #include <vector>
@@ -679,6 +680,70 @@ int pkv_paged_attn_decode_append_partials(
   return partials_impl(desc, k_cache, v_cache, q, batch, num_q_heads, block_table,
                        block_table_stride, context_lens, max_context_len, scale, split_tokens,
                        opts, workspace, workspace_bytes, stream, k_new, v_new, true);
+}
+
+// ---- the decode step without a caller workspace (pkv_paged_attn_decode_append_noalloc)
+//
+// Its split-KV partials go to a file-scope device array, one copy per GPU,
+// held for the life of the process.  In host code `scratch` names a host-side
+// stand-in, not the device array: its device address is looked up once per
+// device (hipGetSymbolAddress, with that device current) and only that
+// address is passed to kernels.
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array (looked up on first use).
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(PKV_ERR_HIP, "no current HIP device for the scratch array (device %d)", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(PKV_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
+}  // namespace
+
+size_t pkv_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int pkv_paged_attn_decode_append_noalloc(const pkv_cache_desc* desc, void* k_cache,
+                                         void* v_cache, const void* k_new, const void* v_new,
+                                         const void* q, int32_t batch, int32_t num_q_heads,
+                                         const int32_t* block_table, int32_t block_table_stride,
+                                         const int32_t* context_lens, int32_t max_context_len,
+                                         float scale, int32_t split_tokens,
+                                         const pkv_decode_opts* opts, void* out, float* lse_out,
+                                         void* stream) {
+  DecodeCommon dc;
+  if (int rc = check_decode(desc, k_cache, v_cache, q, batch, num_q_heads, block_table,
+                            block_table_stride, context_lens, max_context_len, scale,
+                            split_tokens, opts, &dc))
+    return rc;
+  if (dc.plan.n_split > 1 && dc.plan.ws_bytes > kScratchBytes)
+    return fail(PKV_ERR_WORKSPACE,
+                "the split plan needs %zu bytes of partials, over the %zu-byte static scratch "
+                "(fewer splits: a larger split_tokens)",
+                dc.plan.ws_bytes, kScratchBytes);
+  void* ws = nullptr;
+  if (batch > 0 && dc.plan.n_split > 1)
+    if (int rc = scratch_address(&ws)) return rc;
+  return decode_impl(desc, k_cache, v_cache, q, batch, num_q_heads, block_table,
+                     block_table_stride, context_lens, max_context_len, scale, split_tokens,
+                     opts, out, lse_out, ws, ws ? kScratchBytes : 0, stream, k_new, v_new, true);
 }
 
 int pkv_kv_append_quant(const pkv_cache_desc* desc, void* k_cache, void* v_cache,

@@ -89,6 +89,28 @@ def test_decode_workspace_required_when_split(L):
     assert _decode(L, d, max_len=128, split=32, ws=None, ws_bytes=0) == -3
 
 
+def test_noalloc_args(L):
+    """The decode step on the static scratch array: argument checks as the
+    workspace form, and a split plan larger than the array is refused before
+    any HIP call."""
+    assert L.pkv_noalloc_scratch_bytes() == 16 << 20
+    d = desc(hkv=8)
+
+    def call(batch=64, hq=32, stride=256, max_len=4096, split=0, q=FAKE, out=FAKE):
+        return L.pkv_paged_attn_decode_append_noalloc(
+            C.byref(d), FAKE, FAKE, FAKE, FAKE, q, batch, hq, FAKE, stride, FAKE, max_len,
+            0.125, split, None, out, None, None)
+
+    # 64 x 32 rows x 256 splits x 129 floats: 270 MB of partials
+    assert call(split=16) == -3 and "static scratch" in err(L)
+    assert call(batch=0) == 0
+    assert call(hq=12) == -1
+    assert call(split=24) == -1
+    assert call(max_len=256 * 16 + 1) == -1
+    assert call(q=None) == -1
+    assert call(out=None) == -1
+
+
 @pytest.mark.parametrize("name,batch,hq,hkv,max_len,want_split", [
     ("llama70b_128k", 8, 16, 2, 131072, 16),       # G 8: matrix-core kernel, 256 workgroups
     ("llama70b_128k, G 4", 8, 8, 2, 131072, 16),   # G 4, 16-bit: matrix cores too, 256
