@@ -526,6 +526,39 @@ int pkv_validate_tables(const pkv_cache_desc* desc, const int32_t* block_table_h
                         int32_t block_table_stride, const int32_t* lens_host, int32_t batch,
                         const int32_t* slots_host, int32_t n_slots);
 
+/*
+ * Measurement aids -- not part of the attention path.  They give the
+ * measured ceilings the rooflines of the kernels above are read against
+ * (the nominal peaks being the chip's published figures).
+ *
+ * probe_read -- read every byte of buf once with 16-byte streaming loads.
+ *   block_order == NULL: sequentially, grid workgroups of 256 threads
+ *   stepping over the buffer.  Otherwise buf is bytes / block_bytes blocks
+ *   (block_bytes a multiple of 4096) read whole in the order block_order
+ *   (device int32 [bytes / block_bytes]) gives -- the decode's pattern of
+ *   randomly placed 4 KiB (page, KV head) blocks when it is a permutation;
+ *   ids outside the range are skipped.  Bytes read per launch: bytes.
+ *   sink: device uint32 [1]; written only when the loaded data's XOR hits a
+ *   fixed value, which keeps the loads live.  16-byte aligned buf; bytes a
+ *   positive multiple of 16 (and of block_bytes).
+ *
+ * probe_mfma -- grid workgroups of 8 waves (two per SIMD), each wave running
+ *   iters rounds of 4 independent v_mfma_f32_32x32x16_bf16 on operands read
+ *   from `operands` (device, 256 x 16 bytes of bf16, e.g. random values; the
+ *   matrix cores draw more power, and the clock drops further, on random
+ *   data than on zeros).  vector_work 1 adds, per MFMA, the vector work the
+ *   prefill kernel does per MFMA (an FMA, an exp2 and an add per score, a
+ *   bf16 pair conversion every second MFMA).  Flops per launch:
+ *   grid * 8 * iters * 4 * 32768.  clocks: device int64 [2], the shader-clock
+ *   and the 100 MHz constant-clock cycles of wave 0 of workgroup 0 (their
+ *   ratio times 100 MHz is the shader clock under this load).  sink as above.
+ */
+int pkv_probe_read(const void* buf, size_t bytes, const int32_t* block_order,
+                   int32_t block_bytes, int32_t grid, uint32_t* sink, void* stream);
+
+int pkv_probe_mfma(const void* operands, int32_t iters, int32_t vector_work, int32_t grid,
+                   uint32_t* sink, int64_t* clocks, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -98,6 +98,8 @@ def lib():
                                                            vp, vp]
         L.pkv_noalloc_scratch_bytes.restype = sz
         L.pkv_noalloc_scratch_bytes.argtypes = []
+        L.pkv_probe_read.argtypes = [vp, sz, vp, i32, i32, vp, vp]
+        L.pkv_probe_mfma.argtypes = [vp, i32, i32, i32, vp, vp, vp]
         for name in ("pkv_kv_append", "pkv_gather_kv", "pkv_decode_plan", "pkv_paged_attn_decode",
                      "pkv_paged_attn_decode_partials", "pkv_merge_states",
                      "pkv_paged_attn_prefill_chunk", "pkv_validate_tables",
@@ -107,7 +109,8 @@ def lib():
                      "pkv_paged_attn_prefill_chunk_ex", "pkv_paged_attn_mixed_ex",
                      "pkv_decode_shared_prefix_plan", "pkv_paged_attn_decode_shared_prefix",
                      "pkv_paged_attn_decode_append", "pkv_paged_attn_decode_append_partials",
-                     "pkv_paged_attn_decode_append_noalloc"):
+                     "pkv_paged_attn_decode_append_noalloc", "pkv_probe_read",
+                     "pkv_probe_mfma"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -649,6 +652,24 @@ def prepare_decode_append_partials(q, k_cache, v_cache, k_new, v_new, block_tabl
                          context_lens, workspace))
 
 
+def prepare_decode_append(q, k_cache, v_cache, k_new, v_new, block_table, context_lens,
+                          max_context_len: int, scale: float, split_tokens: int, out,
+                          lse_out=None, workspace=None, k_scale: float = 1.0,
+                          v_scale: float = 1.0, window: int = 0,
+                          sink: int = 0) -> PreparedCall:
+    """pkv_paged_attn_decode_append with its arguments marshalled once (a
+    single launch when the plan has one split)."""
+    desc, _, _, opts, common = _append_common(
+        q, k_cache, v_cache, k_new, v_new, block_table, context_lens, max_context_len, scale,
+        split_tokens, k_scale, v_scale, window, sink)
+    _dev(out, "out", q.dtype)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return PreparedCall(lib().pkv_paged_attn_decode_append,
+                        common + (_p(out), _p(lse_out), _p(workspace), ws_len, _stream()),
+                        (desc, opts, q, k_cache, v_cache, k_new, v_new, block_table,
+                         context_lens, out, lse_out, workspace))
+
+
 def prepare_kv_append_quant(k_cache, v_cache, k_new, v_new, slots, k_scale: float,
                             v_scale: float) -> PreparedCall:
     desc = _check_pools(k_cache, v_cache)
@@ -672,3 +693,33 @@ def prepare_merge_states(o_parts, lse_parts, out, lse_out=None) -> PreparedCall:
     args = (_p(o_parts), _p(lse_parts), rows, n, d, _TORCH_TO_CODE[out.dtype], _p(out),
             _p(lse_out), _stream())
     return PreparedCall(lib().pkv_merge_states, args, (o_parts, lse_parts, out, lse_out))
+
+
+# ---- measurement aids (not the attention path): the ceilings the rooflines
+# are read against
+
+def probe_read(buf: torch.Tensor, order: Optional[torch.Tensor] = None, block_bytes: int = 0,
+               grid: int = 8192, sink: Optional[torch.Tensor] = None) -> None:
+    """pkv_probe_read over the bytes of buf: sequential, or whole blocks of
+    block_bytes in the order of `order` (int32 device tensor)."""
+    _dev(buf, "buf")
+    if sink is None:
+        sink = torch.zeros(4, dtype=torch.int32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    if order is not None:
+        _dev(order, "order", torch.int32)
+    _check(lib().pkv_probe_read(_p(buf), nbytes, _p(order), int(block_bytes), int(grid),
+                                _p(sink), _stream()))
+
+
+def probe_mfma(operands: torch.Tensor, iters: int, vector_work: bool, grid: int,
+               clocks: torch.Tensor, sink: Optional[torch.Tensor] = None) -> None:
+    """pkv_probe_mfma: operands 4 KiB of bf16 on the device, clocks int64 [2]."""
+    _dev(operands, "operands")
+    _dev(clocks, "clocks", torch.int64)
+    if operands.numel() * operands.element_size() < 4096:
+        raise ValueError("operands must hold 256 16-byte vectors")
+    if sink is None:
+        sink = torch.zeros(4, dtype=torch.int32, device=operands.device)
+    _check(lib().pkv_probe_mfma(_p(operands), int(iters), 1 if vector_work else 0, int(grid),
+                                _p(sink), _p(clocks), _stream()))

@@ -1151,6 +1151,36 @@ int pkv_paged_attn_decode_shared_prefix(
                     "merge launch");
 }
 
+int pkv_probe_read(const void* buf, size_t bytes, const int32_t* block_order,
+                   int32_t block_bytes, int32_t grid, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return fail(PKV_ERR_INVALID, "NULL pointer");
+  if (!aligned16(buf)) return fail(PKV_ERR_INVALID, "buf must be 16-byte aligned");
+  if (bytes == 0 || bytes % 16 != 0) return fail(PKV_ERR_INVALID, "bytes must be a positive multiple of 16");
+  if (grid <= 0) return fail(PKV_ERR_INVALID, "grid %d <= 0", grid);
+  if (block_order) {
+    if (block_bytes <= 0 || block_bytes % 4096 != 0)
+      return fail(PKV_ERR_INVALID, "block_bytes %d is not a positive multiple of 4096",
+                  block_bytes);
+    if (bytes % (size_t)block_bytes != 0 || bytes / 4096 > 0x7fffffff)
+      return fail(PKV_ERR_INVALID, "bytes is not a whole number of blocks (or over 8 TiB)");
+  }
+  return hip_status(pkv::launch_read_probe(buf, bytes, block_order, block_bytes, 0x9e3779b9u,
+                                           sink, grid, (hipStream_t)stream),
+                    "read probe launch");
+}
+
+int pkv_probe_mfma(const void* operands, int32_t iters, int32_t vector_work, int32_t grid,
+                   uint32_t* sink, int64_t* clocks, void* stream) {
+  if (!operands || !sink || !clocks) return fail(PKV_ERR_INVALID, "NULL pointer");
+  if (!aligned16(operands)) return fail(PKV_ERR_INVALID, "operands must be 16-byte aligned");
+  if (iters <= 0 || grid <= 0) return fail(PKV_ERR_INVALID, "iters and grid must be > 0");
+  if (vector_work != 0 && vector_work != 1)
+    return fail(PKV_ERR_INVALID, "vector_work must be 0 or 1");
+  return hip_status(pkv::launch_mfma_probe(operands, iters, vector_work, grid, 0x9e3779b9u,
+                                           sink, clocks, (hipStream_t)stream),
+                    "mfma probe launch");
+}
+
 int pkv_validate_tables(const pkv_cache_desc* desc, const int32_t* block_table_host,
                         int32_t stride, const int32_t* lens_host, int32_t batch,
                         const int32_t* slots_host, int32_t n_slots) {

@@ -140,6 +140,14 @@ hipError_t launch_merge(int out_dtype, int head_dim, const float* o_parts,
 hipError_t launch_prefill(int kv_dtype, int q_dtype, int head_dim, int group,
                           const PrefillArgs& a, hipStream_t stream);
 
+// Measurement probes (probe.hip).
+hipError_t launch_read_probe(const void* buf, size_t bytes, const int32_t* order,
+                             int32_t block_bytes, uint32_t never, uint32_t* sink, int grid,
+                             hipStream_t stream);
+hipError_t launch_mfma_probe(const void* ops, int32_t iters, int32_t vec, int grid,
+                             uint32_t never, uint32_t* sink, int64_t* clocks,
+                             hipStream_t stream);
+
 // Rows of query positions one prefill workgroup covers (per KV head group).
 int prefill_rows_per_tile(int group);
 
