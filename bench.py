@@ -20,14 +20,24 @@ time measured with HIP events on the stream it runs on.  `cpu_baseline` is
 the CPU oracle timed on this host's cores on a bounded sample of the same
 workload.
 
+`measured_ceilings` holds what the library's probe kernels measure on the
+same GPU (1 GiB read sequentially and as randomly placed 4 KiB blocks; bf16
+MFMAs on random operands, alone and with the prefill kernel's vector work);
+each roofline carries the matching one as `measured_peak` beside the nominal
+peak.  `system` records the ROCm and runtime versions and amd-smi's clocks.
+
 Extra objects (--extras, all by default) measure the other rows of the hot
 path on their own workloads, each with the roofline of its dominant kernel
-and a parity check of sampled rows against the oracle:
-  prefill_chunk  chunked prefill on the matrix cores (MFMA TFLOP/s)
+and a parity check against the oracle (every row, except where noted):
+  llama8b_decode the Llama-3-8B decode step (64 sequences, 513..4097 keys)
+  tiny_decode    the tiny fp32 decode: latency (p10/p50/p90)
+  prefill_chunk  chunked prefill on the matrix cores (MFMA TFLOP/s); parity
+                 on one whole (sequence, KV head) pair and rows of the rest
   fp8_prefill    the same prefill over fp8 (e5m2) pools (MFMA TFLOP/s)
   fp8_decode     the 128K decode over fp8 (e4m3) pools (HBM GB/s)
   window_decode  the 128K decode with a 4096-key window and a 128-key sink
   mixed_batch    an 8192-token batch of decode rows and prefill chunks
+                 (parity on the decode rows and sampled chunk rows)
   shared_prefix  256 sequences sharing 2048 tokens of pages: the one-pass decode
                  and the shared-prefix (cascade) decode, on logical and unique bytes
 """
@@ -96,9 +106,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="lower bound on the CPU oracle sample's wall time")
-    ap.add_argument("--extras", default="prefill,fp8prefill,fp8,window,mixed,prefix",
-                    help="comma-separated extra rows to measure: prefill, fp8prefill, fp8, "
-                         "window, mixed, prefix ('' or 'none' for none)")
+    ap.add_argument("--extras", default="llama8b,tiny,prefill,fp8prefill,fp8,window,mixed,prefix",
+                    help="comma-separated extra rows to measure: llama8b, tiny, prefill, "
+                         "fp8prefill, fp8, window, mixed, prefix ('' or 'none' for none)")
     ap.add_argument("--prefill", action="store_true", help="same as --extras prefill")
     ap.add_argument("--separate-append", action="store_true",
                     help="store the new tokens with their own kv_append launch")
@@ -163,14 +173,22 @@ def main():
     fused = has_append and not args.separate_append
     call_append = (pkv.binding.prepare_kv_append(kc, vc, k_new, v_new, slots)
                    if has_append and not fused else None)
-    if fused:
+    # a plan of one split needs no partials and no merge: the decode launch
+    # writes the output itself (one launch per step)
+    direct = fused and n_split == 1
+    if direct:
+        call_partials = pkv.binding.prepare_decode_append(
+            q, kc, vc, k_new, v_new, bt, cl, w.max_context_len, w.scale, args.split_tokens,
+            out, lse)
+    elif fused:
         call_partials = pkv.binding.prepare_decode_append_partials(
             q, kc, vc, k_new, v_new, bt, cl, w.max_context_len, w.scale, args.split_tokens,
             workspace)
     else:
         call_partials = pkv.binding.prepare_decode_partials(*dargs, args.split_tokens,
                                                             workspace)
-    call_merge = pkv.binding.prepare_merge_states(o_parts, l_parts, out, lse)
+    call_merge = (None if direct else
+                  pkv.binding.prepare_merge_states(o_parts, l_parts, out, lse))
 
     def step(ev=None):
         if call_append is not None:
@@ -180,11 +198,13 @@ def main():
         call_partials()
         if ev is not None:
             ev[1].record()
-        call_merge()
+        if call_merge is not None:
+            call_merge()
 
     progress(f"timing {args.steps} steps after {args.warmup} warm-up steps")
     for _ in range(args.warmup):
         step()
+    _warm(step)          # and at least 40 ms of them: clocks at their steady state
     torch.cuda.synchronize()
 
     t_begin = torch.cuda.Event(enable_timing=True)
@@ -211,6 +231,11 @@ def main():
     if args.graph:
         # the same three calls per step, replayed as one HIP graph: no launch gaps
         def issue_step():
+            if direct:
+                pkv.binding.prepare_decode_append(
+                    q, kc, vc, k_new, v_new, bt, cl, w.max_context_len, w.scale,
+                    args.split_tokens, out, lse)()
+                return
             if fused:
                 pkv.binding.prepare_decode_append_partials(
                     q, kc, vc, k_new, v_new, bt, cl, w.max_context_len, w.scale,
@@ -225,6 +250,7 @@ def main():
         wall = time.perf_counter() - t0
     kern_us = [e0.elapsed_time(e1) * 1e3 for e0, e1 in events]
     step_kern_us = float(np.mean(kern_us))
+    kern_spread = _spread(kern_us)
     # the kernel's own duration: back-to-back launches between one event pair
     # on its stream, so that the per-call event overhead does not count
     kern_avg_us = _back_to_back_us(call_partials, args.steps)
@@ -232,6 +258,10 @@ def main():
     # the same launch timed warm by its own event pair
     cold_us = _cold_event_us(call_partials, 10)
     _, warm_event_us = _event_times(call_partials, 10)
+
+    system = system_info()
+    progress("measured ceilings (read and matrix-core probes)")
+    ceilings = measure_ceilings(dev)
 
     kv_bytes = A.decode_kv_bytes(w.context_lens.tolist(), w.num_kv_heads, w.head_dim, w.dtype)
     # the fused launch also reads the new rows and stores them in the pools
@@ -311,14 +341,20 @@ def main():
                      "frac": round(achieved / A.HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": kern_bytes,
                      "kernel_avg_us": round(kern_avg_us, 2),
-                     "in_step_event_us": round(step_kern_us, 2)},
-        "step_launches": (2 if fused or not has_append else 3),
+                     "in_step_event_us": round(step_kern_us, 2),
+                     "event_us_spread": kern_spread,
+                     "measured_peak": ceilings["random_4k_block_read"]["gbps"],
+                     "frac_of_measured": round(achieved / ceilings["random_4k_block_read"]["gbps"],
+                                               4)},
+        "step_launches": (1 if direct else 2 if fused or not has_append else 3),
         "cold_cache": {"event_us": round(cold_us, 2), "warm_event_us": round(warm_event_us, 2),
                        "achieved_gbps": round(kern_bytes / (cold_us * 1e-6) / 1e9, 1)},
         "cpu_baseline": cpu,
         "parity": parity,
         "host_wall_s": round(wall, 4),
         "gen_s": round(gen_s, 1),
+        "measured_ceilings": ceilings,
+        "system": system,
     }
 
     extras = [e for e in args.extras.split(",") if e and e != "none"]
@@ -331,10 +367,14 @@ def main():
         line["window_decode"] = bench_window(args, dev, sample, reuse)
     del kc, vc, workspace
     torch.cuda.empty_cache()
+    if "llama8b" in extras:
+        line["llama8b_decode"] = bench_llama8b(args, dev, sample, ceilings)
+    if "tiny" in extras:
+        line["tiny_decode"] = bench_tiny(args, dev, sample)
     if "prefill" in extras:
-        line["prefill_chunk"] = bench_prefill(args, dev, sample)
+        line["prefill_chunk"] = bench_prefill(args, dev, sample, ceilings=ceilings)
     if "fp8prefill" in extras:
-        line["fp8_prefill"] = bench_prefill(args, dev, sample, "prefill_fp8")
+        line["fp8_prefill"] = bench_prefill(args, dev, sample, "prefill_fp8", ceilings)
     if "fp8" in extras:
         line["fp8_decode"] = bench_fp8(args, dev, sample)
     if "mixed" in extras:
@@ -370,8 +410,7 @@ def _back_to_back_us(fn, n):
     """Mean microseconds per call of n back-to-back calls of fn() bracketed by
     one pair of HIP events on the current stream."""
     import torch
-    fn()
-    torch.cuda.synchronize()
+    _warm(fn)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -431,7 +470,7 @@ def _event_times(fn, n, warmup=3):
     import torch
     for _ in range(warmup):
         fn()
-    torch.cuda.synchronize()
+    _warm(fn)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n)]
     for e0, e1 in ev:
@@ -441,6 +480,251 @@ def _event_times(fn, n, warmup=3):
     torch.cuda.synchronize()
     us = [e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]
     return float(np.mean(us)), float(np.median(us))
+
+
+def _warm(fn, ms: float = 40.0):
+    """Call fn() until at least `ms` of GPU-busy wall time has passed: the
+    chip raises its clocks over the first ~25 ms of sustained work (a
+    prefill launch settles from 1.1-1.3 ms to ~0.95-1.0 ms), so every row is
+    timed at its steady state."""
+    import time
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t0) * 1e3 >= ms:
+                return
+
+
+def _spread(us):
+    """Mean and the 10th, 50th and 90th percentiles of per-launch times (us)."""
+    import numpy as np
+    a = np.asarray(us, dtype=np.float64)
+    return {"mean": round(float(a.mean()), 2), "p10": round(float(np.percentile(a, 10)), 2),
+            "p50": round(float(np.percentile(a, 50)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2), "n": int(a.size)}
+
+
+def _event_list(fn, n, warmup=3):
+    """Per-call microseconds of n calls of fn(), each between its own pair of
+    HIP events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    _warm(fn)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for e0, e1 in ev:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]
+
+
+def system_info():
+    """ROCm and runtime versions, the device, and the clocks amd-smi reports
+    (sampled after the timed steps; the maxima are the chip's limits)."""
+    import subprocess
+    import torch
+    info = {"torch": torch.__version__, "hip_runtime": torch.version.hip}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        info["rocm"] = None
+    p = torch.cuda.get_device_properties(0)
+    info["device"] = {"arch": p.gcnArchName, "compute_units": p.multi_processor_count,
+                      "memory_gib": round(p.total_memory / 2 ** 30, 1),
+                      "l2_bytes_per_xcd": getattr(p, "L2_cache_size", None)}
+    try:
+        r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True,
+                           text=True, timeout=30)
+        data = json.loads(r.stdout)
+        gpu = data["gpu_data"][0] if isinstance(data, dict) else data[0]
+        clk = gpu["clock"]
+    except Exception:
+        clk = None
+    if isinstance(clk, dict):
+        gfx = [v for k, v in sorted(clk.items()) if k.startswith("gfx_") and isinstance(v, dict)]
+        mem = next((v for k, v in sorted(clk.items())
+                    if k.startswith("mem") and isinstance(v, dict)), None)
+        def mhz(d, key):
+            try:
+                return d[key]["value"]
+            except Exception:
+                return None
+        info["amd_smi_clock_mhz"] = {
+            "gfx_current_per_xcd": [mhz(g, "clk") for g in gfx],
+            "gfx_max": mhz(gfx[0], "max_clk") if gfx else None,
+            "mem_current": mhz(mem, "clk") if isinstance(mem, dict) else None,
+            "sampled": "after the timed steps (idle)"}
+    else:
+        info["amd_smi_clock_mhz"] = None
+    return info
+
+
+def measure_ceilings(dev):
+    """Measured ceilings on this GPU with the library's probe kernels: 1 GiB
+    read sequentially and as randomly placed 4 KiB blocks (the decode's
+    pattern), best of a few grid sizes; 32x32x16 bf16 MFMAs on random
+    operands alone and with the prefill kernel's vector work per MFMA, with
+    the shader clock under that load."""
+    import torch
+
+    import paged_kv_cache_04_amd as pkv
+    nbytes = 1 << 30
+    buf = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=dev)
+    res = {}
+    best = None
+    for grid in (4096, 8192, 16384):
+        us = _back_to_back_us(lambda: pkv.binding.probe_read(buf, grid=grid), 10)
+        best = us if best is None else min(best, us)
+    res["sequential_read"] = {"gbps": round(nbytes / (best * 1e-6) / 1e9, 1),
+                              "us_per_gib": round(best, 2)}
+    gen = torch.Generator(device="cpu").manual_seed(11)
+    order = torch.randperm(nbytes // 4096, generator=gen).to(torch.int32).to(dev)
+    best = None
+    for grid in (8192, 16384):
+        us = _back_to_back_us(lambda: pkv.binding.probe_read(buf, order, 4096, grid=grid), 10)
+        best = us if best is None else min(best, us)
+    res["random_4k_block_read"] = {"gbps": round(nbytes / (best * 1e-6) / 1e9, 1),
+                                   "us_per_gib": round(best, 2)}
+    del buf, order
+    ops = torch.randn(2048, generator=gen).to(torch.bfloat16).to(dev)
+    clocks = torch.zeros(2, dtype=torch.int64, device=dev)
+    iters, grid = 4000, 256
+    flops = grid * 8 * iters * 4 * 32768
+    for key, vec in (("mfma_bf16_random", False), ("mfma_bf16_random_with_prefill_vector_work", True)):
+        us = _back_to_back_us(lambda: pkv.binding.probe_mfma(ops, iters, vec, grid, clocks), 5)
+        c = clocks.tolist()
+        res[key] = {"tflops": round(flops / (us * 1e-6) / 1e12, 1),
+                    "shader_clock_ghz": round(c[0] / max(c[1], 1) * 0.1, 3)}
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_llama8b(args, dev, sample, ceilings):
+    """The Llama-3-8B decode step (64 sequences of 513..4097 keys, GQA 4):
+    the new token stored by the decode launch, split by the batch's lengths
+    as a scheduler that holds them would (pkv_decode_split_for_lens), then
+    the merge; the automatic plan (one split, a single launch writing the
+    output) beside it."""
+    progress("llama8b_decode")
+    import torch
+
+    import paged_kv_cache_04_amd as pkv
+    from paged_kv_cache_04_amd import accounting as A
+    from paged_kv_cache_04_amd import workloads as W
+
+    w = W.make("llama8b")
+    kc, vc = w.k_cache.to(dev), w.v_cache.to(dev)
+    q, bt, cl = w.q.to(dev), w.block_table.to(dev), w.context_lens.to(dev)
+    k_new, v_new = w.k_new.to(dev), w.v_new.to(dev)
+    desc = pkv.cache_desc(kc)
+    lens = w.context_lens.tolist()
+    split = pkv.decode_split_for_lens(desc, w.num_q_heads, lens)
+    n_split, _ = pkv.decode_plan(desc, w.batch, w.num_q_heads, w.max_context_len, split)
+    _, total = pkv.binding.partials_bytes(w.batch, w.num_q_heads, n_split, w.head_dim)
+    ws = torch.empty(total, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=dev)
+    o_parts, l_parts, _ = pkv.paged_attn_decode_partials(
+        q, kc, vc, bt, cl, w.max_context_len, w.scale, split_tokens=split, workspace=ws)
+    c_part = pkv.binding.prepare_decode_append_partials(q, kc, vc, k_new, v_new, bt, cl,
+                                                        w.max_context_len, w.scale, split, ws)
+    c_merge = pkv.binding.prepare_merge_states(o_parts, l_parts, out, lse)
+
+    def step():
+        c_part()
+        c_merge()
+
+    for _ in range(10):
+        step()
+    step_us = _back_to_back_us(step, 50)
+    part_us = _back_to_back_us(c_part, 50)
+    part_ev = _spread(_event_list(c_part, 50))
+    cold_us = _cold_event_us(c_part, 10)
+    out1 = torch.empty_like(q)
+    c_direct = pkv.binding.prepare_decode_append(q, kc, vc, k_new, v_new, bt, cl,
+                                                 w.max_context_len, w.scale, 0, out1)
+    direct_us = _back_to_back_us(c_direct, 50)
+    kv_bytes = A.decode_kv_bytes(lens, w.num_kv_heads, w.head_dim, w.dtype)
+    kern_bytes = kv_bytes + A.append_bytes(w.batch, w.num_kv_heads, w.head_dim, w.dtype)
+    roof = _hbm_roofline("decode_mfma_kernel (split-KV partials, storing the new tokens)",
+                         kern_bytes, part_us)
+    meas = ceilings["random_4k_block_read"]["gbps"]
+    roof["measured_peak"] = meas
+    roof["frac_of_measured"] = round(roof["achieved"] / meas, 4)
+    roof["event_us_spread"] = part_ev
+    res = {"workload": WORKLOAD_TEXT["llama8b"],
+           "kv_bytes": int(kv_bytes), "split_tokens": split, "n_split": n_split,
+           "tokens_per_s": round(w.batch / (step_us * 1e-6), 1),
+           "step_us": round(step_us, 2), "step_launches": 2,
+           "kv_gbps_per_step": round(kv_bytes / (step_us * 1e-6) / 1e9, 1),
+           "roofline": roof,
+           "cold_cache": {"kernel_us": round(cold_us, 2),
+                          "achieved_gbps": round(kern_bytes / (cold_us * 1e-6) / 1e9, 1)},
+           "automatic_plan_one_launch": {
+               "n_split": 1, "call_us": round(direct_us, 2),
+               "tokens_per_s": round(w.batch / (direct_us * 1e-6), 1),
+               "achieved_gbps": round(kern_bytes / (direct_us * 1e-6) / 1e9, 1)}}
+    if sample:
+        from oracle import pkvref
+        torch.cuda.synchronize()
+        pkvref.kv_append(w.dtype, w.k_cache, w.v_cache, w.k_new, w.v_new, w.slots)
+        ref, ref_lse = pkvref.decode(w.dtype, w.k_cache, w.v_cache, w.q, w.block_table,
+                                     w.context_lens, w.scale, n_threads=host_cores())
+        got = out.float().cpu().double().numpy().reshape(ref.shape)
+        res["parity"] = _parity(got, ref, w.dtype)
+        res["parity"]["lse_max_abs_err"] = float(abs(lse.cpu().double().numpy().reshape(-1)
+                                                     - ref_lse).max())
+        got1 = out1.float().cpu().double().numpy().reshape(ref.shape)
+        res["automatic_plan_one_launch"]["parity"] = _parity(got1, ref, w.dtype)
+    return res
+
+
+def bench_tiny(args, dev, sample):
+    """The tiny fp32 decode (4 sequences of 37..511 keys, head_dim 64): a
+    launch-bound call, reported as latency; parity of every row."""
+    progress("tiny_decode")
+    import torch
+
+    import paged_kv_cache_04_amd as pkv
+    from paged_kv_cache_04_amd import workloads as W
+
+    w = W.make("tiny")
+    kc, vc = w.k_cache.to(dev), w.v_cache.to(dev)
+    q, bt, cl = w.q.to(dev), w.block_table.to(dev), w.context_lens.to(dev)
+    n_split, ws_bytes = pkv.decode_plan(pkv.cache_desc(kc), w.batch, w.num_q_heads,
+                                        w.max_context_len, 0)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+
+    def call():
+        pkv.paged_attn_decode(q, kc, vc, bt, cl, w.max_context_len, w.scale, out=out,
+                              workspace=ws)
+
+    spread = _spread(_event_list(call, 50, warmup=10))
+    res = {"workload": WORKLOAD_TEXT["tiny"], "n_split": n_split,
+           "launches": 1 if n_split == 1 else 2,
+           "call_event_us": spread,
+           "back_to_back_us": round(_back_to_back_us(call, 50), 2),
+           "tokens_per_s": round(w.batch / (spread["p50"] * 1e-6), 1),
+           "note": "3.6 MB of K/V, cache resident: latency, no roofline claim"}
+    if sample:
+        from oracle import pkvref
+        torch.cuda.synchronize()
+        ref, _ = pkvref.decode(w.dtype, w.k_cache, w.v_cache, w.q, w.block_table,
+                               w.context_lens, w.scale, n_threads=host_cores())
+        got = out.double().cpu().numpy().reshape(ref.shape)
+        res["parity"] = _parity(got, ref, w.dtype)
+    return res
 
 
 def _parity(got, ref, dtype):
@@ -468,7 +752,7 @@ def _mfma_roofline(kernel, flops, us, dtype):
             "algorithmic_flops_per_launch": int(flops), "kernel_avg_us": round(us, 2)}
 
 
-def bench_prefill(args, dev, sample, config="prefill"):
+def bench_prefill(args, dev, sample, config="prefill", ceilings=None):
     fp8 = config == "prefill_fp8"
     progress("fp8_prefill" if fp8 else "prefill_chunk")
     import numpy as np
@@ -494,7 +778,7 @@ def bench_prefill(args, dev, sample, config="prefill"):
         pkv.paged_attn_prefill_chunk(q, kc, vc, qi, bt, kl, max(chunk), w.max_context_len,
                                      w.scale, out=out, **sc)
 
-    us, us_med = _event_times(run, 10)
+    us, us_med = _event_times(run, 30)
     flops = A.prefill_flops(w.context_lens.tolist(), chunk, w.num_q_heads, w.head_dim)
     text = ("batch 4, 32768-token paged history + 512-row causal chunk, 32 q / 8 kv heads, "
             "head_dim 128, bf16")
@@ -506,11 +790,23 @@ def bench_prefill(args, dev, sample, config="prefill"):
            "query_tokens_per_s": round(sum(chunk) / (us * 1e-6), 1),
            "roofline": _mfma_roofline("prefill_kernel" + ("<bf16 q, fp8 e5m2 cache>" if fp8 else ""),
                                       flops, us, "bf16")}
+    res["kernel_event_us_spread"] = _spread(_event_list(run, 20))
+    if ceilings is not None:
+        # the matrix cores' measured rate on random operands with the vector
+        # work this kernel does per MFMA (no memory traffic, no barriers)
+        meas = ceilings["mfma_bf16_random_with_prefill_vector_work"]["tflops"]
+        res["roofline"]["measured_peak"] = meas
+        res["roofline"]["frac_of_measured"] = round(res["roofline"]["achieved"] / meas, 4)
     if sample:
         from oracle import pkvref
         hq = w.num_q_heads
-        toks = [int(w.q_indptr[b]) + i for b in range(w.batch) for i in (0, 255, 511)]
-        rows = [t * hq + h for t in toks for h in (0, 13, 31)]
+        g_size = hq // w.num_kv_heads
+        # one whole (sequence, KV head) pair -- sequence 0, KV head 0: every
+        # chunk row of its query heads -- plus rows of the other sequences
+        q0, q1 = int(w.q_indptr[0]), int(w.q_indptr[1])
+        rows = [t * hq + h for t in range(q0, q1) for h in range(g_size)]
+        toks = [int(w.q_indptr[b]) + i for b in range(1, w.batch) for i in (0, 255, 511)]
+        rows += [t * hq + h for t in toks for h in (5, 13, 31)]
         if fp8:
             f8 = W.DTYPES[w.kv_dtype]
             kq = torch.from_numpy(pkvref.quant_fp8(w.kv_dtype, w.dtype, w.k_new, w.k_scale))
@@ -610,7 +906,7 @@ def bench_fp8(args, dev, sample):
         vq = torch.from_numpy(pkvref.quant_fp8(w.kv_dtype, w.dtype, w.v_new, w.v_scale))
         pkvref.kv_append(w.kv_dtype, w.k_cache, w.v_cache, kq.view(W.DTYPES[w.kv_dtype]),
                          vq.view(W.DTYPES[w.kv_dtype]), w.slots)
-        rows = [b * w.num_q_heads + h for b in range(w.batch) for h in (0, 9)]
+        rows = list(range(w.batch * w.num_q_heads))      # every row
         ref, _ = pkvref.decode_ex(w.dtype, w.kv_dtype, w.k_cache, w.v_cache, w.q, w.block_table,
                                   w.context_lens, w.scale, k_scale=w.k_scale,
                                   v_scale=w.v_scale, rows=rows, n_threads=host_cores())
@@ -699,7 +995,7 @@ def bench_window(args, dev, sample, reuse=None):
                           "achieved_gbps": round(kv_bytes / (cold_us * 1e-6) / 1e9, 1)}}
     if sample:
         from oracle import pkvref
-        rows = [b * w.num_q_heads + h for b in range(w.batch) for h in (0, 15)]
+        rows = list(range(w.batch * w.num_q_heads))      # every row
         ref, _ = pkvref.decode_ex(w.dtype, w.dtype, w.k_cache, w.v_cache, w.q, w.block_table,
                                   w.context_lens, w.scale, window=window, sink=sink, rows=rows,
                                   n_threads=host_cores())
@@ -767,7 +1063,7 @@ def bench_shared_prefix(args, dev, sample):
     if sample:
         from oracle import pkvref
         torch.cuda.synchronize()
-        rows = [b * w.num_q_heads + h for b in range(0, w.batch, 16) for h in (0, 31)]
+        rows = list(range(w.batch * w.num_q_heads))      # every row
         ref, _ = pkvref.decode(w.dtype, w.k_cache, w.v_cache, w.q, w.block_table,
                                w.context_lens, w.scale, rows=rows, n_threads=host_cores())
         got = out.float().cpu().double().numpy().reshape(-1, w.head_dim)[rows]

@@ -133,19 +133,17 @@ def test_fp8_decode_shapes(fp8, qd, hq, hkv):
         check_ex(w, split_tokens=split, what=f"{fp8} {qd} G{hq // hkv} split {split}")
 
 
-def test_fp8_decode_128k_sampled_rows():
+def test_fp8_decode_128k_every_row():
     """Full size: 8 x 131072 keys over e4m3 pools, GQA 8, split-KV + merge;
-    rows sampled over every sequence and head."""
+    every one of the 128 query rows against the oracle."""
     w = W.make("llama70b_128k_fp8")
     print("[fp8 parity] llama70b_128k_fp8 full size", flush=True)
     d = to_dev(w, DEV)
     out, lse = ex_decode(w, d)
-    rows = [b * w.num_q_heads + h for b in range(w.batch) for h in (0, 5, 7, 8, 15)]
-    ref, ref_lse = oracle_ex(w, rows=rows)
+    ref, ref_lse = oracle_ex(w)
     assert torch.equal(bits(d["k_cache"]), bits(w.k_cache)), "k pool after the append"
-    idx = torch.tensor(rows, device=DEV)
-    assert_close(out.reshape(-1, w.head_dim)[idx], ref, w.dtype, "fp8 128K")
-    assert_lse_close(lse.reshape(-1)[idx], ref_lse, w.dtype, "fp8 128K")
+    assert_close(out.reshape(ref.shape), ref, w.dtype, "fp8 128K")
+    assert_lse_close(lse.reshape(-1), ref_lse, w.dtype, "fp8 128K")
 
 
 # -------------------------------------------------------------- sliding window
@@ -210,18 +208,16 @@ def test_window_of_one_key_bit_exact():
                     assert torch.equal(bits(out[b, h]), bits(want)), (dtype, split, b, h)
 
 
-def test_window_128k_sampled_rows():
+def test_window_128k_every_row():
     """Full 128K pools with a 4096-key window and a 128-key sink: only the
-    visited pages count, rows sampled against the oracle."""
+    visited pages count; every query row against the oracle."""
     w = W.make("llama70b_128k")
     print("[window parity] llama70b_128k, window 4096, sink 128", flush=True)
     d = to_dev(w, DEV)
     out, lse = ex_decode(w, d, window=4096, sink=128)
-    rows = [b * w.num_q_heads + h for b in range(w.batch) for h in (0, 7, 8, 15)]
-    ref, ref_lse = oracle_ex(w, rows=rows, window=4096, sink=128)
-    idx = torch.tensor(rows, device=DEV)
-    assert_close(out.reshape(-1, w.head_dim)[idx], ref, w.dtype, "window 128K")
-    assert_lse_close(lse.reshape(-1)[idx], ref_lse, w.dtype, "window 128K")
+    ref, ref_lse = oracle_ex(w, window=4096, sink=128)
+    assert_close(out.reshape(ref.shape), ref, w.dtype, "window 128K")
+    assert_lse_close(lse.reshape(-1), ref_lse, w.dtype, "window 128K")
 
 
 # ------------------------------------------------------------ ragged mixed batch

@@ -62,6 +62,19 @@ def test_prefill_config_sampled_rows():
     check_prefill(w, rows)
 
 
+def test_prefill_config_whole_pair():
+    """Full size, every row of one (sequence, KV head) pair: the 512 chunk
+    rows of query heads 4..7 of sequence 2 (KV head 1), 2048 rows, each
+    against 32769..33280 keys."""
+    w = W.make("prefill")
+    print("[prefill parity] batch 4, 32768 + 512, sequence 2 x KV head 1, all rows", flush=True)
+    hq, g = w.num_q_heads, w.num_q_heads // w.num_kv_heads
+    q0, q1 = int(w.q_indptr[2]), int(w.q_indptr[3])
+    rows = [t * hq + h for t in range(q0, q1) for h in range(g, 2 * g)]
+    assert len(rows) == 2048
+    check_prefill(w, rows, "prefill pair (2, 1)")
+
+
 @pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (8, 2), (16, 2), (32, 2)])
