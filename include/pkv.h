@@ -155,7 +155,14 @@ int pkv_gather_kv(const pkv_cache_desc* desc, const void* k_cache, const void* v
                   void* stream);
 
 /*
- * decode_plan -- how the decode call splits each sequence's keys.
+ * decode_plan -- how the decode call splits each sequence's keys.  The keys
+ * of a sequence are cut into blocks that are reduced one at a time (page 2,
+ * "FlashAttention + PageAttention joint tuning", section 2.2: the tiling of
+ * K and V, and the online-softmax recursion that joins the blocks); a split
+ * is such a block run by its own workgroup, and the workspace holds each
+ * split's partial result until the merge applies that recursion across the
+ * splits.  (This call also answers "how many workspace bytes": it reports
+ * them beside the split count.)
  * split_tokens > 0 (a multiple of P) fixes the keys per split; 0 lets the
  * library choose from batch, H_kv and max_context_len (a fixed rule aimed at
  * filling a 256-CU device, so the result does not depend on the device).
@@ -353,7 +360,11 @@ int pkv_kv_append_quant(const pkv_cache_desc* desc, void* k_cache, void* v_cache
                         void* stream);
 
 /*
- * merge_states -- combine n_parts partial attention states per row:
+ * merge_states -- combine n_parts partial attention states per row.  Each
+ * part is the softmax-weighted V sum of one block of keys with its
+ * log-sum-exp; joining them is the online-softmax recursion of page 2,
+ * "FlashAttention + PageAttention joint tuning", section 2.2 (the running
+ * maximum and the rescaled sums), applied once across the blocks:
  *     M = max_k lse_k,  w_k = exp(lse_k - M),
  *     out = sum_k w_k o_k / sum_k w_k,  lse = M + log(sum_k w_k),
  * in ascending k order.  Parts with lse_k = -inf are skipped; all skipped
@@ -516,7 +527,10 @@ int pkv_paged_attn_decode_shared_prefix(
 
 /*
  * validate_tables -- host-side check of host copies of the tables (no HIP
- * call): every entry a sequence uses (the first ceil(lens[b]/P) of its row)
+ * call), the consistency checker that page 3, "Flash Attention and Paged KV
+ * Cache in practice", section 6.2 recommends against scrambled attention
+ * after page replacement (every page within its size, every page id valid):
+ * every entry a sequence uses (the first ceil(lens[b]/P) of its row)
  * is in [0, num_pages); 0 <= lens[b] <= stride * P; every slot is < 0 or in
  * [0, num_pages * P) and no slot >= 0 repeats.  slots may be NULL (n = 0).
  * Returns PKV_OK or PKV_ERR_INVALID with the first offence in

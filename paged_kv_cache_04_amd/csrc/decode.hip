@@ -99,7 +99,10 @@ struct DecodeCfg {
   // workgroups per CU the registers are sized for
   static constexpr bool OCC3 = !FP8 && ES == 2 && G <= 4;
   static constexpr int NB = FP8 ? 5 : ((ES == 4 || OCC3) ? 2 : 3);
-  static constexpr int OCC = OCC3 ? 3 : 2;
+  // f32 at head_dim 128 with G >= 4 holds 16 G registers of q per lane: one
+  // workgroup per CU (a wave per SIMD, 512 registers) instead of spilling
+  static constexpr bool OCC1 = ES == 4 && D == 128 && G >= 4;
+  static constexpr int OCC = OCC3 ? 3 : (OCC1 ? 1 : 2);
   static_assert(KV >= 1 && KV * KL * VEC == D, "head_dim / vector mismatch");
   static_assert(QW >= 1, "q vector layout");
   static_assert(TG >= 1 && VT * TG == P, "V layout mismatch");

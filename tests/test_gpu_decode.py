@@ -62,6 +62,7 @@ def test_decode_llama70b_128k_parity():
 
 @pytest.mark.parametrize("dtype,d,hq,hkv", [
     ("f32", 64, 2, 2), ("f32", 128, 8, 1), ("f32", 64, 8, 1), ("f32", 128, 4, 2),
+    ("f32", 128, 8, 2),                      # f32 at head_dim 128, G 4 and 8: a wave per SIMD
     ("f16", 64, 4, 2), ("f16", 128, 2, 1), ("f16", 64, 8, 1), ("f16", 128, 1, 1),
     ("bf16", 64, 16, 2), ("bf16", 128, 6, 3), ("bf16", 64, 1, 1), ("bf16", 128, 16, 16),
     ("bf16", 64, 8, 2),                      # G = 4 at head_dim 64: the vector kernel
