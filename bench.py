@@ -114,6 +114,10 @@ def parse():
                     help="store the new tokens with their own kv_append launch")
     ap.add_argument("--graph", action="store_true",
                     help="time the steps as HIP graph replays instead of eager launches")
+    ap.add_argument("--no-smi", action="store_true",
+                    help="do not query amd-smi for clocks (for runs under a profiler that "
+                         "initialises the GPU before this process starts: a child process "
+                         "cannot be started then)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain copy of this many MiB first (counter calibration)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -259,7 +263,7 @@ def main():
     cold_us = _cold_event_us(call_partials, 10)
     _, warm_event_us = _event_times(call_partials, 10)
 
-    system = system_info()
+    system = system_info(query_smi=not args.no_smi)
     progress("measured ceilings (read and matrix-core probes)")
     ceilings = measure_ceilings(dev)
 
@@ -527,7 +531,7 @@ def _event_list(fn, n, warmup=3):
     return [e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]
 
 
-def system_info():
+def system_info(query_smi: bool = True):
     """ROCm and runtime versions, the device, and the clocks amd-smi reports
     (sampled after the timed steps; the maxima are the chip's limits)."""
     import subprocess
@@ -543,6 +547,8 @@ def system_info():
                       "memory_gib": round(p.total_memory / 2 ** 30, 1),
                       "l2_bytes_per_xcd": getattr(p, "L2_cache_size", None)}
     try:
+        if not query_smi:
+            raise RuntimeError("amd-smi not queried (--no-smi)")
         r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True,
                            text=True, timeout=30)
         data = json.loads(r.stdout)

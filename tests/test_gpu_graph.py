@@ -120,3 +120,37 @@ def test_prefill_and_mixed_graph():
     replay_matches(gm, (mout,), eager_m,
                    lambda: pkv.paged_attn_mixed(*margs, split_tokens=0,
                                                 out=torch.empty_like(mout)))
+
+
+def test_shared_prefix_graph():
+    """The shared-prefix decode (three launches: the shared pages on the
+    matrix cores, the own pages on the split-KV decode, the merge), captured
+    on torch's capture stream: every replay gives the eager result bit for
+    bit."""
+    prefix, suffix = 512, [3, 200, 1000, 64]
+    w = W.make_decode("grs", seed=113, batch=len(suffix), hq=32, hkv=8, d=128, dtype="bf16",
+                      hist_lens=[prefix + s for s in suffix], append=False, pool_slack=0.1,
+                      shared_prefix=prefix)
+    d = to_dev(w, DEV)
+    pp = prefix // 16
+    prefix_table = d["block_table"][0, :pp].contiguous()
+    own = d["block_table"][:, pp:].contiguous()
+    suffix_lens = (d["context_lens"] - prefix).contiguous()
+    max_suffix = int(suffix_lens.max().item())
+    n_parts, ws_bytes = pkv.shared_prefix_plan(pkv.cache_desc(d["k_cache"]), w.batch,
+                                               w.num_q_heads, prefix, max_suffix)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(d["q"])
+    lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=DEV)
+    args = (d["q"], d["k_cache"], d["v_cache"], prefix_table, prefix, own, suffix_lens,
+            max_suffix, w.scale)
+    pkv.paged_attn_decode_shared_prefix(*args, out=out, lse_out=lse, workspace=ws)
+    torch.cuda.synchronize()
+    eager = (out.clone(), lse.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pkv.paged_attn_decode_shared_prefix(*args, out=out, lse_out=lse, workspace=ws)
+    ws2 = torch.empty_like(ws)
+    replay_matches(g, (out, lse), eager,
+                   lambda: pkv.paged_attn_decode_shared_prefix(*args, out=torch.empty_like(out),
+                                                               workspace=ws2))

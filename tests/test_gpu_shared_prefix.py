@@ -156,3 +156,38 @@ def test_prefix_workload_every_row():
     ref, ref_lse = oracle(w)
     assert_close(out.reshape(ref.shape), ref, w.dtype, "prefix workload")
     assert_lse_close(lse.reshape(-1), ref_lse, w.dtype, "prefix workload")
+
+
+def test_shared_prefix_from_two_host_threads():
+    """Two host threads, each on its own torch stream, call the cascade at the
+    same time, 20 times each: the host layer keeps no state between calls
+    (only a per-thread error string), so each call sees only its own inputs."""
+    import threading
+    ws_list, outs, refs, inputs = [], [], [], []
+    for k, (prefix, suffix) in enumerate(((256, [5, 300, 40]), (512, [100, 7, 900, 33]))):
+        w = build("bf16", 32, 8, prefix, suffix, append=False, seed=200 + k)
+        d = to_dev(w, DEV)
+        inputs.append((w, d, prefix))
+        refs.append(oracle(w))
+    errors = []
+
+    def worker(i):
+        try:
+            w, d, prefix = inputs[i]
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                for _ in range(20):
+                    out, _ = cascade(w, d, prefix)
+            outs.append((i, out))
+        except Exception as e:   # surfaced by the main thread
+            errors.append(e)
+
+    ts = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not errors, errors
+    for i, out in outs:
+        ref, _ = refs[i]
+        assert_close(out.reshape(ref.shape), ref, "bf16", f"thread {i}")
