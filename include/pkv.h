@@ -20,8 +20,9 @@
  * Conventions for every entry point:
  *   - Pointers named "device" are HIP device pointers; "host" ones are CPU
  *     memory.  The caller owns every buffer.  The library allocates no device
- *     memory, keeps no pointer after returning, and never synchronises
- *     (outside the PKV_CHECK debug mode below).
+ *     memory (the one static device array of the allocation-free decode step
+ *     comes with the loaded library), keeps no pointer after returning, and
+ *     never synchronises (outside the PKV_CHECK debug mode below).
  *   - stream: a hipStream_t passed as void*; NULL is the null stream.  All
  *     device work is enqueued on it asynchronously.
  *   - Base pointers of device buffers must be 16-byte aligned.
