@@ -341,7 +341,9 @@ int check_decode(const pkv_cache_desc* desc, const void* k_cache, const void* v_
                          plan_len(max_context_len, dc->opts, desc->page_size), split_tokens,
                          dc->opts.q_dtype, &dc->plan))
     return rc;
-  const int64_t blocks = (int64_t)batch * desc->num_kv_heads * dc->plan.n_split;
+  // the split-major grid pads the units to a multiple of 8 (pkv::decode_grid)
+  const int64_t units = (int64_t)batch * desc->num_kv_heads;
+  const int64_t blocks = (units + 7) / 8 * 8 * dc->plan.n_split;
   if (blocks > 0x7fffffff) return fail(PKV_ERR_INVALID, "grid too large (%lld)", (long long)blocks);
   return PKV_OK;
 }
