@@ -288,18 +288,19 @@ def test_mixed_batch_degenerate(layout):
 
 def test_mixed_batch_full_size_sampled():
     """The 8192-token batch: 6 decode rows at 8K..128K keys and two 4093-row
-    chunks (history 0 and 65536); every decode row and sampled chunk rows."""
+    chunks (history 0 and 65536); the decode tokens' rows of every head, and
+    sampled chunk rows."""
     w = W.make("mixed")
     print("[mixed parity] 6 decode rows + 2 x 4093-row chunks", flush=True)
     d = to_dev(w, DEV)
     out, lse = mixed_run(w, d)
     hq = w.num_q_heads
     ind = w.q_indptr.tolist()
-    toks = list(range(6))
+    rows = list(range(6 * hq))                    # the decode tokens, all heads
     for b in (6, 7):
         base = ind[b]
-        toks += [base + i for i in (0, 1, 15, 16, 17, 2047, 4091, 4092)]
-    rows = [t * hq + h for t in toks for h in (0, 5, 8, 15)]
+        rows += [(base + i) * hq + h for i in (0, 1, 15, 16, 17, 2047, 4091, 4092)
+                 for h in (0, 5, 8, 15)]
     ref, ref_lse = oracle_mixed(w, rows=rows)
     idx = torch.tensor(rows, device=DEV)
     assert_close(out.reshape(-1, w.head_dim)[idx], ref, w.dtype, "mixed full size")

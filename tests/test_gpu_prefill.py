@@ -62,17 +62,18 @@ def test_prefill_config_sampled_rows():
     check_prefill(w, rows)
 
 
-def test_prefill_config_whole_pair():
-    """Full size, every row of one (sequence, KV head) pair: the 512 chunk
-    rows of query heads 4..7 of sequence 2 (KV head 1), 2048 rows, each
-    against 32769..33280 keys."""
+@pytest.mark.parametrize("seq", [0, 1, 2, 3])
+def test_prefill_config_every_row(seq):
+    """Full size, every row: the 512 chunk rows of all 32 query heads of
+    sequence `seq` (16384 rows, each against 32769..33280 keys); the four
+    cases together cover all 65536 rows of the workload."""
     w = W.make("prefill")
-    print("[prefill parity] batch 4, 32768 + 512, sequence 2 x KV head 1, all rows", flush=True)
-    hq, g = w.num_q_heads, w.num_q_heads // w.num_kv_heads
-    q0, q1 = int(w.q_indptr[2]), int(w.q_indptr[3])
-    rows = [t * hq + h for t in range(q0, q1) for h in range(g, 2 * g)]
-    assert len(rows) == 2048
-    check_prefill(w, rows, "prefill pair (2, 1)")
+    print(f"[prefill parity] batch 4, 32768 + 512, sequence {seq}, all rows", flush=True)
+    hq = w.num_q_heads
+    q0, q1 = int(w.q_indptr[seq]), int(w.q_indptr[seq + 1])
+    rows = list(range(q0 * hq, q1 * hq))
+    assert len(rows) == 512 * 32
+    check_prefill(w, rows, f"prefill sequence {seq}")
 
 
 @pytest.mark.parametrize("d", [128, 64])
