@@ -166,7 +166,8 @@ int pkv_gather_kv(const pkv_cache_desc* desc, const void* k_cache, const void* v
  * them beside the split count.)
  * split_tokens > 0 (a multiple of P) fixes the keys per split; 0 lets the
  * library choose from batch, H_kv and max_context_len (a fixed rule aimed at
- * filling a 256-CU device, so the result does not depend on the device).
+ * filling a 256-CU device, so the result does not depend on the device; a
+ * max_context_len of at most 32 pages is not split).
  * Writes *n_split (splits per sequence; 1 means no workspace and no merge
  * pass) and *workspace_bytes (0 when n_split == 1).  Host-only; no HIP call.
  */

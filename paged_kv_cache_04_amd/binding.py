@@ -614,6 +614,30 @@ def prepare_kv_append(k_cache, v_cache, k_new, v_new, slots) -> PreparedCall:
     return PreparedCall(lib().pkv_kv_append, args, (desc, k_cache, v_cache, k_new, v_new, slots))
 
 
+def prepare_decode(q, k_cache, v_cache, block_table, context_lens, max_context_len: int,
+                   scale: float, split_tokens: int, out, lse_out=None, workspace=None,
+                   k_scale: float = 1.0, v_scale: float = 1.0, window: int = 0,
+                   sink: int = 0) -> PreparedCall:
+    """pkv_paged_attn_decode (its _ex form with options) with its arguments
+    marshalled once: one launch when the plan has one split, partials and
+    merge otherwise (the workspace from decode_plan)."""
+    desc, batch, hq = _decode_common(q, k_cache, v_cache, block_table, context_lens,
+                                     max_context_len)
+    opts = decode_opts(q.dtype, k_cache.dtype, k_scale, v_scale, window, sink)
+    _dev(out, "out", q.dtype)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    common = (C.byref(desc), _p(k_cache), _p(v_cache), _p(q), batch, hq, _p(block_table),
+              int(block_table.shape[1]), _p(context_lens), int(max_context_len), float(scale),
+              int(split_tokens))
+    tail = (_p(out), _p(lse_out), _p(workspace), ws_len, _stream())
+    if opts is None:
+        fn, args = lib().pkv_paged_attn_decode, common + tail
+    else:
+        fn, args = lib().pkv_paged_attn_decode_ex, common + (C.byref(opts),) + tail
+    return PreparedCall(fn, args, (desc, opts, q, k_cache, v_cache, block_table, context_lens,
+                                   out, lse_out, workspace))
+
+
 def prepare_decode_partials(q, k_cache, v_cache, block_table, context_lens,
                             max_context_len: int, scale: float, split_tokens: int,
                             workspace, k_scale: float = 1.0, v_scale: float = 1.0,

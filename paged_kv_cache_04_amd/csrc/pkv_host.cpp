@@ -213,7 +213,8 @@ int debug_check_slots(const pkv_cache_desc* d, const int32_t* slots, int32_t n, 
 // Decode split plan.  Auto rule: aim for about 512 workgroups (two per CU
 // on a 256-CU device, one round of residency) for the vector decode kernel,
 // 256 (one per CU) for the matrix-core kernel, whose workgroups each keep more
-// bytes in flight; never less than 16 pages (256 keys) per split.
+// bytes in flight; never less than 16 pages (256 keys) per split, and no
+// split at all for contexts of at most 32 pages.
 struct Plan {
   int32_t n_split;
   int32_t pages_per_split;
@@ -225,6 +226,10 @@ constexpr int64_t kTargetWorkgroups = 512;
 constexpr int64_t kTargetWorkgroupsMfma = 256;
 constexpr int32_t kXcdSplitTiles = 64;    // prefill: query tiles per (b, kv head)
 constexpr int32_t kMinSplitPages = 16;
+// Contexts of at most this many pages are not split: the merge launch costs
+// more than the shorter workgroups save (the tiny batch, 4 x 8 units of up to
+// 32 pages: 13.9 us in one launch against 16.5 us split in two plus the merge).
+constexpr int64_t kNoSplitPages = 32;
 // Splits for batches of unequal lengths (pkv_decode_split_for_lens): small
 // enough that about 1024 workgroups (four per CU) carry the batch, so that the
 // hardware balances the uneven tails, and at least 32 pages each.
@@ -250,6 +255,7 @@ int make_plan(const pkv_cache_desc* d, int32_t batch, int32_t num_q_heads,
     int64_t want = units > 0 ? (target + units - 1) / units : 1;
     const int64_t cap = (max_pages + kMinSplitPages - 1) / kMinSplitPages;
     if (want > cap) want = cap;
+    if (max_pages <= kNoSplitPages) want = 1;
     if (want < 1) want = 1;
     pps = (max_pages + want - 1) / want;
     if (pps < 1) pps = 1;

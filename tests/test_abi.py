@@ -115,7 +115,8 @@ def test_noalloc_args(L):
     ("llama70b_128k", 8, 16, 2, 131072, 16),       # G 8: matrix-core kernel, 256 workgroups
     ("llama70b_128k, G 4", 8, 8, 2, 131072, 16),   # G 4, 16-bit: matrix cores too, 256
     ("llama70b_128k, G 2", 8, 4, 2, 131072, 32),   # G 2: vector kernel, 512
-    ("tiny", 4, 8, 8, 511, 2),
+    ("tiny", 4, 8, 8, 511, 1),                     # at most 32 pages: no split
+    ("33 pages", 4, 8, 8, 513, 3),
     ("prefix", 256, 32, 8, 2560, 1),
 ])
 def test_auto_plan(L, name, batch, hq, hkv, max_len, want_split):

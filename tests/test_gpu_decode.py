@@ -314,3 +314,28 @@ def test_prepared_calls_match_regular_calls():
             c()
     torch.cuda.synchronize()
     assert torch.equal(bits(out), bits(ref_out)) and torch.equal(bits(lse), bits(ref_lse))
+
+
+@pytest.mark.parametrize("split,window", [(0, 0), (256, 0), (0, 300)])
+def test_prepared_decode_same_bits(split, window):
+    """The decode call marshalled once (binding.prepare_decode) gives the bits
+    of the plain call, one launch or partials + merge, with options or not;
+    the tiny batch (at most 32 pages) is not split by the automatic plan."""
+    w = W.make("tiny")
+    d = to_dev(w, DEV)
+    args = (d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["context_lens"],
+            w.max_context_len, w.scale)
+    n_split, ws_bytes = pkv.decode_plan(pkv.cache_desc(d["k_cache"]), w.batch, w.num_q_heads,
+                                        w.max_context_len, split)
+    assert (n_split == 1) == (split == 0)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=DEV)
+    want = pkv.paged_attn_decode(*args, split_tokens=split, window=window, sink=4 if window else 0)
+    out = torch.empty_like(d["q"])
+    pkv.binding.prepare_decode(*args, split, out, workspace=ws, window=window,
+                               sink=4 if window else 0)()
+    torch.cuda.synchronize()
+    assert torch.equal(bits(out), bits(want))
+    ref, _ = pkvref.decode_ex(w.dtype, w.dtype, w.k_cache, w.v_cache, w.q, w.block_table,
+                              w.context_lens, w.scale, window=window, sink=4 if window else 0,
+                              n_threads=host_threads())
+    assert_close(out.reshape(ref.shape), ref, w.dtype, f"prepared split {split} window {window}")
