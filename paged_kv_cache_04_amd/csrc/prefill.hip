@@ -46,7 +46,7 @@
 // bf16; page 4, section 3.1 prefills in chunks over an e5m2 cache): a page
 // block is 2 KiB.  The wave that copies a page brings it into a staging
 // buffer of its own and, halfway through the iteration (after its weights,
-// before its PV step), waits for its own copy and widens the page exactly to
+// before its PV step), waits for its own copies and widens the page exactly to
 // the query type into the same swizzled tile the 16-bit pools use (every fp8
 // value is exact in f16 and in bf16); from there the tile loop is the same.
 // Each element is widened once per workgroup, not once per wave that reads
@@ -292,8 +292,8 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
 
   if (tid == 0) bad_flag = bad ? 1 : 0;
 
-  // ---- staging: waves 0-3 copy the K pages and waves 4-7 the V pages of a
-  // tile, wave w page w % 4 (key rows 16(w%4) .. +15), as four 1-KiB LDS
+  // ---- staging: waves 0-3 copy the K and the V pages of a tile, wave w
+  // page w of each (key rows 16w .. +15), as four 1-KiB LDS
   // chunks of four rows; lane i of a chunk fills row 4j + i/16, physical
   // chunk i%16 with logical chunk (i%16) ^ swz(row).  The page, its
   // descriptor and the LDS destination are the same for the whole wave
@@ -303,8 +303,14 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   const int64_t head_block = (int64_t)PAGEB;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int wp = wu & 3;          // page of the tile this wave copies
-  const bool kwave = wu < 4;      // waves 0-3 copy K pages, waves 4-7 V pages
-  constexpr int NDMA = F8 ? 1 : PAGEB / 1024;   // 1-KiB copies per page (16-bit pools)
+  // Waves 0-3 copy the tile's pages, K and V (wave w: page w of the tile);
+  // waves 4-7 copy nothing.  The two waves on a SIMD (w and w + 4) share its
+  // issue slots and the older one (w) gets ahead: with the copies split
+  // between them (w: K, w + 4: V) the older one waited ~1100 of a tile's
+  // ~3500 cycles at the barrier while the other, its copies included,
+  // finished the tile.
+  const bool kwave = wu < 4;
+  constexpr int NDMA = PAGEB / 1024;             // 1-KiB copies per page (16-bit pools)
   constexpr int RPC = 1024 / ROWB;               // tile rows per 1-KiB copy
   uint32_t dma_off[NDMA];
 #pragma unroll
@@ -326,13 +332,17 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
     if (pi < seq_pages && out) my_bad = true;
     return out ? 0 : pid;
   };
-  lds_u8* my_stg = (lds_u8*)(stg + (F8 ? wu * PAGEB : 0));
-  auto copy_page = [&](const void* pool, int pid, lds_u8* dst) {
+  // fp8: a copying wave stages its K page in slot wp and its V page in slot
+  // wp + 4 of stg (a constant offset from the K slot, folded into the LDS
+  // instructions)
+  lds_u8* stg_k = (lds_u8*)(stg + (F8 ? wp * PAGEB : 0));
+  constexpr int STG_V = F8 ? 4 * PAGEB : 0;
+  auto copy_page = [&](const void* pool, int pid, lds_u8* dst, lds_u8* staging) {
     const __amdgpu_buffer_rsrc_t r =
         page_rsrc((const char*)pool + ((int64_t)pid * a.num_kv_heads + g) * head_block, PAGEB);
     if constexpr (F8) {
 #pragma unroll
-      for (int j = 0; j < PAGEB / 1024; ++j) dma16(r, (uint32_t)(j * 1024 + 16 * lane), my_stg + j * 1024);
+      for (int j = 0; j < PAGEB / 1024; ++j) dma16(r, (uint32_t)(j * 1024 + 16 * lane), staging + j * 1024);
     } else {
 #pragma unroll
       for (int j = 0; j < NDMA; ++j) dma16(r, dma_off[j], dst + (16 * wp + RPC * j) * ROWB);
@@ -342,13 +352,13 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   // rows 16wp .. 16wp+15 of tile dst: lane i takes the 8-element chunks
   // i, i+64, i+128, i+192 of the page (row = chunk / 16, logical chunk =
   // chunk % 16) and stores each at its swizzled place.
-  auto widen_page = [&](lds_u8* dst) {
+  auto widen_page = [&](lds_u8* dst, const lds_u8* staging) {
     if constexpr (F8) {
 #pragma unroll 1
       for (int i = 0; i < P * NCH / 64; ++i) {
         const int ch = lane + 64 * i, r = ch / NCH, lc = ch % NCH;
         const u32x2_t x = *reinterpret_cast<const u32x2_t __attribute__((address_space(3)))*>(
-            my_stg + r * (D * CT::bytes) + lc * 8);
+            staging + r * (D * CT::bytes) + lc * 8);
         u32x4_t y;
         y[0] = CT::template cvt2<TT, false>(x[0]);
         y[1] = CT::template cvt2<TT, true>(x[0]);
@@ -493,16 +503,19 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   // into another.
   const float wmax = __builtin_ldexpf(1.f, kLazyLog2 + (int)M::POFF);
   int pid_f = 0;      // block-table entry of the page this wave copies next
+  int pid_v = 0;      // checked page id of the V page this wave copies next
   auto iteration = [&](int j, lds_u8* kd, const lds_u8* kc, uint8_t* vc_raw, lds_u8* vd,
                        f32x16_t (&s_cur)[2], f32x16_t (&s_nxt)[2], auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const lds_u8* vc = (const lds_u8*)vc_raw;
+    // V(j+1) first (read sooner), from the id checked when K(j+1) was copied
     if (kwave) {
-      if (j + 2 < n_tiles) copy_page(a.k_cache, check_pid(j + 2, pid_f), kd);
+      if (j + 1 < n_tiles) copy_page(a.v_cache, pid_v, vd, stg_k + STG_V);
+      if (j + 2 < n_tiles) {
+        pid_v = check_pid(j + 2, pid_f);
+        copy_page(a.k_cache, pid_v, kd, stg_k);
+      }
       pid_f = load_pid(j + 3);
-    } else {
-      if (j + 1 < n_tiles) copy_page(a.v_cache, check_pid(j + 1, pid_f), vd);
-      pid_f = load_pid(j + 2);
     }
     if constexpr (MASKED) mask_tile(j, s_cur);
     fence();
@@ -548,14 +561,15 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
       for (int g = 0; g < 4; ++g) weights(s_cur, g, mc2, pk[g], ls);
     }
     fence();
-    // fp8: widen the page this wave copied above, if any, once its copy has
-    // landed.  Its destination (K(j), read in iteration j-1, or V(j-1), read
-    // in that iteration's PV) is free since the last barrier, and it is read
+    // fp8: widen the pages this wave copied above, once its copies have
+    // landed.  Their destinations (K(j), read in iteration j-1, and V(j-1),
+    // read in that iteration's PV) are free since the last barrier and read
     // only after the next one; widening here overlaps the other waves' PV.
     if constexpr (F8) {
-      if (kwave ? (j + 2 < n_tiles) : (j + 1 < n_tiles)) {
+      if (kwave && j + 1 < n_tiles) {
         __builtin_amdgcn_s_waitcnt(0);
-        widen_page(kwave ? kd : vd);
+        widen_page(vd, stg_k + STG_V);
+        if (j + 2 < n_tiles) widen_page(kd, stg_k);
       }
     }
     if (MASKED && (tile0 + j) * BK + BK > kvl) {
@@ -589,26 +603,22 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   {
     const int pid0 = check_pid(0, load_pid(0));
     if (kwave) {
-      copy_page(a.k_cache, pid0, kb0);
+      copy_page(a.k_cache, pid0, kb0, stg_k);
+      copy_page(a.v_cache, pid0, vb0, stg_k + STG_V);
       if constexpr (F8) {
         __builtin_amdgcn_s_waitcnt(0);
-        widen_page(kb0);
+        widen_page(kb0, stg_k);
+        widen_page(vb0, stg_k + STG_V);
       }
       if (n_tiles > 1) {
-        copy_page(a.k_cache, check_pid(1, load_pid(1)), kb1);
+        pid_v = check_pid(1, load_pid(1));
+        copy_page(a.k_cache, pid_v, kb1, stg_k);
         if constexpr (F8) {
           __builtin_amdgcn_s_waitcnt(0);
-          widen_page(kb1);
+          widen_page(kb1, stg_k);
         }
       }
       pid_f = load_pid(2);
-    } else {
-      copy_page(a.v_cache, pid0, vb0);
-      if constexpr (F8) {
-        __builtin_amdgcn_s_waitcnt(0);
-        widen_page(vb0);
-      }
-      pid_f = load_pid(1);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
