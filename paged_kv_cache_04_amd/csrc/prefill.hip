@@ -305,10 +305,10 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   const int wp = wu & 3;          // page of the tile this wave copies
   // Waves 0-3 copy the tile's pages, K and V (wave w: page w of the tile);
   // waves 4-7 copy nothing.  The two waves on a SIMD (w and w + 4) share its
-  // issue slots and the older one (w) gets ahead: with the copies split
-  // between them (w: K, w + 4: V) the older one waited ~1100 of a tile's
-  // ~3500 cycles at the barrier while the other, its copies included,
-  // finished the tile.
+  // issue slots and the older one (w) gets ahead, so the younger one ends
+  // each tile; with the copies split between them (w: K, w + 4: V), w waited
+  // ~1100 of a tile's ~3500 cycles at the barrier while w + 4 finished its
+  // copies and its products.  All copies on w took ~450 cycles off the tile.
   const bool kwave = wu < 4;
   constexpr int NDMA = PAGEB / 1024;             // 1-KiB copies per page (16-bit pools)
   constexpr int RPC = 1024 / ROWB;               // tile rows per 1-KiB copy
