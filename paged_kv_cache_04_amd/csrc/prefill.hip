@@ -484,9 +484,9 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
 
   // ---- software pipeline over key tiles.  Iteration j holds S(j) in
   // registers, K(j+1) and V(j) in LDS, and:
-  //   copies K(j+2) into the buffer K(j) used (waves 0-3) and V(j+1) into the
-  //   other V buffer (waves 4-7); every wave finished with both buffers
-  //   before the last barrier;
+  //   copies (waves 0-3) V(j+1) into the other V buffer and K(j+2) into the
+  //   buffer K(j) used; every wave finished with both buffers before the
+  //   last barrier;
   //   computes S(j+1) on the matrix cores while the vector units form the
   //   weights of S(j) against the current reference (the stream is fenced
   //   into regions of four MFMAs, each with its K operand reads and the
