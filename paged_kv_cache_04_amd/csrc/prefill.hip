@@ -508,7 +508,8 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
                        f32x16_t (&s_cur)[2], f32x16_t (&s_nxt)[2], auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const lds_u8* vc = (const lds_u8*)vc_raw;
-    // V(j+1) first (read sooner), from the id checked when K(j+1) was copied
+    // V(j+1), from the id checked when K(j+1) was copied, and K(j+2); both
+    // land before this iteration's closing barrier
     if (kwave) {
       if (j + 1 < n_tiles) copy_page(a.v_cache, pid_v, vd, stg_k + STG_V);
       if (j + 2 < n_tiles) {
