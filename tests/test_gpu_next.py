@@ -286,21 +286,23 @@ def test_mixed_batch_degenerate(layout):
     assert_lse_close(lse.reshape(-1), ref_lse, "bf16", layout)
 
 
-def test_mixed_batch_full_size_sampled():
+def test_mixed_batch_full_size_rows():
     """The 8192-token batch: 6 decode rows at 8K..128K keys and two 4093-row
-    chunks (history 0 and 65536); the decode tokens' rows of every head, and
-    sampled chunk rows."""
+    chunks (history 0 and 65536).  Every decode row (all 16 heads), every
+    position of the first chunk and every 32nd position (and the last) of
+    the second, for one query head of each KV head (0 and 8): 8540 rows
+    against the oracle, every row tile and key tile edge of the first chunk
+    among them."""
     w = W.make("mixed")
     print("[mixed parity] 6 decode rows + 2 x 4093-row chunks", flush=True)
     d = to_dev(w, DEV)
     out, lse = mixed_run(w, d)
     hq = w.num_q_heads
     ind = w.q_indptr.tolist()
-    rows = list(range(6 * hq))                    # the decode tokens, all heads
-    for b in (6, 7):
-        base = ind[b]
-        rows += [(base + i) * hq + h for i in (0, 1, 15, 16, 17, 2047, 4091, 4092)
-                 for h in (0, 5, 8, 15)]
+    rows = list(range(ind[6] * hq))                   # the decode tokens, all heads
+    rows += [t * hq + h for t in range(ind[6], ind[7]) for h in (0, 8)]
+    tail = list(range(ind[7], ind[8], 32)) + [ind[8] - 1]
+    rows += [t * hq + h for t in tail for h in (0, 8)]
     ref, ref_lse = oracle_mixed(w, rows=rows)
     idx = torch.tensor(rows, device=DEV)
     assert_close(out.reshape(-1, w.head_dim)[idx], ref, w.dtype, "mixed full size")
