@@ -72,6 +72,7 @@ constexpr int BK = 64;           // keys per tile (4 pages)
 constexpr int NWP = 8;           // waves per workgroup
 constexpr int ROWS = 256;        // query rows per workgroup
 constexpr int kLazyLog2 = 8;     // weights stay below 2^(8 + POFF)
+constexpr int kRankMax = 256;    // longest-first sequence order up to this batch
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -203,15 +204,42 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
   // XCD (mt + pair) % 8: a pair's tiles on one XCD still read the same keys
   // (all start at key 0), every XCD gets light and heavy causal tiles alike,
   // and the first tile of the pairs -- all a one-row chunk has -- lands on a
-  // different XCD for each pair.  Each XCD walks the pairs one after another
-  // (pair-major), so that a long pair's workgroups start together instead of
-  // queueing behind chains of short workgroups on the same CUs.
+  // different XCD for each pair.
+  // Longest first: a workgroup of a causal chunk sees more keys the higher its
+  // tile, so each mapping hands out the heavy tiles first, and with xcd_split
+  // each XCD walks the sequences by decreasing key count (their KV heads
+  // interleaved, so that a long sequence's workgroups start together).  When
+  // there are more workgroups than CUs, the CU that frees first (lightest
+  // work so far) then takes the heaviest of the workgroups still waiting: the
+  // two 4093-row chunks of an 8192-token batch (histories 0 and 65536) with
+  // the short one first had put its heaviest tiles before the long chunk's
+  // heaviest on the same CUs.
   const int nbg = a.batch * a.num_kv_heads;
   int bg, mt, ks = 0;
-  if (a.xcd_split) {
+  if (!PFX && a.xcd_split) {
     const int x = blockIdx.x % 8, j = blockIdx.x / 8;
-    bg = j / a.m_tiles_x;
-    mt = 8 * (j % a.m_tiles_x) + ((x + 8 - (bg & 7)) & 7);
+    const int hk = a.num_kv_heads;
+    const int jt = j / hk;
+    const int r = jt / a.m_tiles_x;            // rank of the sequence
+    const int k = jt % a.m_tiles_x;            // k-th heaviest tile of its pairs here
+    // the sequence of rank r by (kv_len descending, index ascending); batches
+    // above kRankMax keep their index order
+    __shared__ int seq_of_rank;
+    if (a.batch <= kRankMax) {
+      for (int s = tid; s < a.batch; s += NWP * 64) {
+        const int ws = a.kv_lens[s];
+        int rk = 0;
+        for (int o = 0; o < a.batch; ++o) {
+          const int wo = a.kv_lens[o];
+          rk += (wo > ws || (wo == ws && o < s)) ? 1 : 0;
+        }
+        if (rk == r) seq_of_rank = s;
+      }
+      __syncthreads();
+    }
+    const int bq = a.batch <= kRankMax ? seq_of_rank : r;
+    bg = bq * hk + j % hk;
+    mt = 8 * (a.m_tiles_x - 1 - k) + ((x + 8 - (bg & 7)) & 7);
     if (mt >= a.m_tiles) return;     // padding past the last tile
   } else if constexpr (PFX) {        // key split next, so a split's row tiles share L2
     bg = blockIdx.x % nbg;
@@ -220,7 +248,7 @@ __global__ __launch_bounds__(NWP * 64, 1) void prefill_kernel(PrefillArgs a) {
     mt = id / a.n_ksplit;
   } else {
     bg = blockIdx.x % nbg;
-    mt = blockIdx.x / nbg;
+    mt = a.m_tiles - 1 - blockIdx.x / nbg;
   }
   const int b = bg / a.num_kv_heads;
   const int g = bg % a.num_kv_heads;
