@@ -22,9 +22,10 @@ workload.
 
 `measured_ceilings` holds what the library's probe kernels measure on the
 same GPU (1 GiB read sequentially and as randomly placed 4 KiB blocks; bf16
-MFMAs on random operands, alone and with the prefill kernel's vector work);
-each roofline carries the matching one as `measured_peak` beside the nominal
-peak.  `system` records the ROCm and runtime versions and amd-smi's clocks.
+MFMAs on random operands, alone and with the prefill kernel's vector work;
+the prefill kernel's tile loop with its LDS operand reads, with and without
+that vector work); each roofline carries the matching one as `measured_peak`
+beside the nominal peak, and the prefill's also its tile loop's rate.  `system` records the ROCm and runtime versions and amd-smi's clocks.
 
 Extra objects (--extras, all by default) measure the other rows of the hot
 path on their own workloads, each with the roofline of its dominant kernel
@@ -611,6 +612,21 @@ def measure_ceilings(dev):
         c = clocks.tolist()
         res[key] = {"tflops": round(flops / (us * 1e-6) / 1e12, 1),
                     "shader_clock_ghz": round(c[0] / max(c[1], 1) * 0.1, 3)}
+    # the prefill kernel's tile loop alone (its MFMAs, LDS operand reads and,
+    # second, its vector work; no copies or barriers), after ~50 ms of load so
+    # that the clock has settled as it has for the kernel
+    iters, grid = 1000, 256
+    flops = grid * 8 * iters * 2 * 32 * 32768
+    for key, vec in (("prefill_tile_loop_lds_operands", False),
+                     ("prefill_tile_loop_lds_operands_with_vector_work", True)):
+        def run():
+            pkv.binding.probe_prefill_loop(ops, iters, vec, grid, clocks)
+        for _ in range(15):
+            run()
+        us = _back_to_back_us(run, 5)
+        c = clocks.tolist()
+        res[key] = {"tflops": round(flops / (us * 1e-6) / 1e12, 1),
+                    "shader_clock_ghz": round(c[0] / max(c[1], 1) * 0.1, 3)}
     torch.cuda.empty_cache()
     return res
 
@@ -808,6 +824,11 @@ def bench_prefill(args, dev, sample, config="prefill", ceilings=None):
         meas = ceilings["mfma_bf16_random_with_prefill_vector_work"]["tflops"]
         res["roofline"]["measured_peak"] = meas
         res["roofline"]["frac_of_measured"] = round(res["roofline"]["achieved"] / meas, 4)
+        # and this kernel's own tile loop, LDS operand reads included, without
+        # the page copies and barriers around it
+        loop = ceilings["prefill_tile_loop_lds_operands_with_vector_work"]["tflops"]
+        res["roofline"]["tile_loop_tflops"] = loop
+        res["roofline"]["frac_of_tile_loop"] = round(res["roofline"]["achieved"] / loop, 4)
     if sample:
         from oracle import pkvref
         hq = w.num_q_heads

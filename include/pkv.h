@@ -568,12 +568,27 @@ int pkv_validate_tables(const pkv_cache_desc* desc, const int32_t* block_table_h
  *   grid * 8 * iters * 4 * 32768.  clocks: device int64 [2], the shader-clock
  *   and the 100 MHz constant-clock cycles of wave 0 of workgroup 0 (their
  *   ratio times 100 MHz is the shader clock under this load).  sink as above.
+ *
+ * probe_prefill_loop -- the chunked-prefill kernel's tile loop on its own:
+ *   grid workgroups of 8 waves, each wave running iters rounds of two 64-key
+ *   tiles at bf16, head_dim 128, 32 query rows: per tile 16 QK MFMAs whose K
+ *   operands are read from an LDS tile in that kernel's layout, then 16 PV
+ *   MFMAs whose V^T operands come from transposing LDS reads (the tiles are
+ *   filled once from `operands`, 256 x 16 bytes of bf16).  vector_work 1
+ *   forms the weights of each tile's scores beside the next tile's QK MFMAs
+ *   (an FMA, an exp2 and an add per score, a bf16 pair conversion per two),
+ *   as that kernel does; 0 leaves them out.  No page copies, barriers, masks
+ *   or rescaling.  Flops per launch: grid * 8 * iters * 2 * 32 * 32768.
+ *   clocks and sink as for probe_mfma.
  */
 int pkv_probe_read(const void* buf, size_t bytes, const int32_t* block_order,
                    int32_t block_bytes, int32_t grid, uint32_t* sink, void* stream);
 
 int pkv_probe_mfma(const void* operands, int32_t iters, int32_t vector_work, int32_t grid,
                    uint32_t* sink, int64_t* clocks, void* stream);
+
+int pkv_probe_prefill_loop(const void* operands, int32_t iters, int32_t vector_work,
+                           int32_t grid, uint32_t* sink, int64_t* clocks, void* stream);
 
 #ifdef __cplusplus
 }

@@ -100,6 +100,7 @@ def lib():
         L.pkv_noalloc_scratch_bytes.argtypes = []
         L.pkv_probe_read.argtypes = [vp, sz, vp, i32, i32, vp, vp]
         L.pkv_probe_mfma.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+        L.pkv_probe_prefill_loop.argtypes = [vp, i32, i32, i32, vp, vp, vp]
         for name in ("pkv_kv_append", "pkv_gather_kv", "pkv_decode_plan", "pkv_paged_attn_decode",
                      "pkv_paged_attn_decode_partials", "pkv_merge_states",
                      "pkv_paged_attn_prefill_chunk", "pkv_validate_tables",
@@ -110,7 +111,7 @@ def lib():
                      "pkv_decode_shared_prefix_plan", "pkv_paged_attn_decode_shared_prefix",
                      "pkv_paged_attn_decode_append", "pkv_paged_attn_decode_append_partials",
                      "pkv_paged_attn_decode_append_noalloc", "pkv_probe_read",
-                     "pkv_probe_mfma"):
+                     "pkv_probe_mfma", "pkv_probe_prefill_loop"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -747,3 +748,16 @@ def probe_mfma(operands: torch.Tensor, iters: int, vector_work: bool, grid: int,
         sink = torch.zeros(4, dtype=torch.int32, device=operands.device)
     _check(lib().pkv_probe_mfma(_p(operands), int(iters), 1 if vector_work else 0, int(grid),
                                 _p(sink), _p(clocks), _stream()))
+
+
+def probe_prefill_loop(operands: torch.Tensor, iters: int, vector_work: bool, grid: int,
+                       clocks: torch.Tensor, sink: Optional[torch.Tensor] = None) -> None:
+    """pkv_probe_prefill_loop: operands 4 KiB of bf16 on the device, clocks int64 [2]."""
+    _dev(operands, "operands")
+    _dev(clocks, "clocks", torch.int64)
+    if operands.numel() * operands.element_size() < 4096:
+        raise ValueError("operands must hold 256 16-byte vectors")
+    if sink is None:
+        sink = torch.zeros(4, dtype=torch.int32, device=operands.device)
+    _check(lib().pkv_probe_prefill_loop(_p(operands), int(iters), 1 if vector_work else 0,
+                                        int(grid), _p(sink), _p(clocks), _stream()))

@@ -1189,6 +1189,19 @@ int pkv_probe_mfma(const void* operands, int32_t iters, int32_t vector_work, int
                     "mfma probe launch");
 }
 
+int pkv_probe_prefill_loop(const void* operands, int32_t iters, int32_t vector_work,
+                           int32_t grid, uint32_t* sink, int64_t* clocks, void* stream) {
+  if (!operands || !sink || !clocks) return fail(PKV_ERR_INVALID, "NULL pointer");
+  if (!aligned16(operands)) return fail(PKV_ERR_INVALID, "operands must be 16-byte aligned");
+  if (iters <= 0 || grid <= 0) return fail(PKV_ERR_INVALID, "iters and grid must be > 0");
+  if (vector_work != 0 && vector_work != 1)
+    return fail(PKV_ERR_INVALID, "vector_work must be 0 or 1");
+  return hip_status(pkv::launch_prefill_loop_probe(operands, iters, vector_work, grid,
+                                                   0x9e3779b9u, sink, clocks,
+                                                   (hipStream_t)stream),
+                    "prefill loop probe launch");
+}
+
 int pkv_validate_tables(const pkv_cache_desc* desc, const int32_t* block_table_host,
                         int32_t stride, const int32_t* lens_host, int32_t batch,
                         const int32_t* slots_host, int32_t n_slots) {

@@ -147,6 +147,9 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, const int32_t* order
 hipError_t launch_mfma_probe(const void* ops, int32_t iters, int32_t vec, int grid,
                              uint32_t never, uint32_t* sink, int64_t* clocks,
                              hipStream_t stream);
+hipError_t launch_prefill_loop_probe(const void* ops, int32_t iters, int32_t vec, int grid,
+                                     uint32_t never, uint32_t* sink, int64_t* clocks,
+                                     hipStream_t stream);
 
 // Rows of query positions one prefill workgroup covers (per KV head group).
 int prefill_rows_per_tile(int group);

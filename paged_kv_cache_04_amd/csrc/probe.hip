@@ -9,7 +9,10 @@
 //   - a matrix-core probe: a register-only loop of 32x32x16 bf16 MFMAs on
 //     random operands, alone or with the vector work the prefill kernel
 //     does per MFMA, timed in shader clocks and in the 100 MHz constant
-//     clock so that the clock under that load comes out too.
+//     clock so that the clock under that load comes out too;
+//   - the prefill kernel's tile loop on its own: the same MFMAs, LDS operand
+//     reads and vector work per 64-key tile and wave, without the page
+//     copies, barriers, masks or rescaling around them.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -21,6 +24,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef uint8_t __attribute__((address_space(3))) lds_t;
 
 constexpr int kReadThreads = 256;
 constexpr int kReadUnroll = 4;          // 16-byte loads in flight per thread
@@ -141,6 +146,134 @@ __global__ __launch_bounds__(512) void mfma_loop_kernel(const uint4* ops, int32_
   }
 }
 
+// The prefill kernel's per-wave work on one 64-key tile at bf16, head_dim
+// 128, 32 query rows per wave, two waves per SIMD: K and V tiles in LDS in
+// that kernel's layout (256-byte key rows, 16-byte chunk c of row r at
+// c ^ swz(r)), filled once from `ops`; Q^T in registers.  Per tile: 16 QK
+// MFMAs (two 32-key blocks x 8 k-steps of 16 head dims, K operands read from
+// LDS) and, with VEC, the weights of the previous tile's scores beside them
+// (an FMA, an exp2 and an add per score, a bf16 pair conversion per two);
+// then 16 PV MFMAs (4 k-steps of 16 keys x 4 blocks of 32 head dims) with
+// V^T operands from transposing LDS reads.  Without VEC the PV steps take
+// fixed B operands and the scores accumulate across tiles, so that no MFMA
+// is dead code.  Each iteration runs two tiles.
+__device__ __forceinline__ int tile_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+template <bool VEC>
+__global__ __launch_bounds__(512, 1) void prefill_loop_kernel(const uint4* ops, int32_t iters,
+                                                              uint32_t never, uint32_t* sink,
+                                                              int64_t* clocks) {
+  constexpr int ROWB = 256;
+  __shared__ __align__(1024) uint8_t kt[64 * ROWB];
+  __shared__ __align__(1024) uint8_t vt[64 * ROWB];
+  const int t = threadIdx.x, lane = t & 63, n = lane & 31, half = lane >> 5;
+  for (int i = t; i < 64 * ROWB / 16; i += 512) {
+    reinterpret_cast<uint4*>(kt)[i] = ops[(i * 3 + 1) & 255];
+    reinterpret_cast<uint4*>(vt)[i] = ops[(i * 5 + 2) & 255];
+  }
+  bf16x8_t qr[8], pfix[4];
+  for (int i = 0; i < 8; ++i) qr[i] = __builtin_bit_cast(bf16x8_t, ops[(t * 3 + 7 + 17 * i) & 255]);
+  for (int i = 0; i < 4; ++i) pfix[i] = __builtin_bit_cast(bf16x8_t, ops[(t * 5 + 1 + 13 * i) & 255]);
+  __syncthreads();
+  // per-lane LDS byte offsets: K operand of k-step ks; V^T operand of block db
+  // (key slots 0..3 and 4..7 at k-step 0; k-step ks adds 16 rows)
+  int k_off[8], va_off[4], vb_off[4];
+  for (int ks = 0; ks < 8; ++ks) k_off[ks] = n * ROWB + (((2 * ks + half) ^ tile_swz(n)) * 16);
+  const int q16 = lane >> 4, li = lane & 15, kk = li >> 2, jj = li & 3;
+  const int key0 = 4 * (q16 >> 1) + kk;
+  for (int db = 0; db < 4; ++db) {
+    const int dcol = 32 * db + 16 * (q16 & 1) + 4 * jj;
+    const int lc = dcol >> 3, sub8 = (dcol & 7) * 2;
+    va_off[db] = key0 * ROWB + ((lc ^ tile_swz(key0)) * 16) + sub8;
+    vb_off[db] = (key0 + 8) * ROWB + ((lc ^ tile_swz(key0 + 8)) * 16) + sub8;
+  }
+  const lds_t* kl = (const lds_t*)kt;
+  const lds_t* vl = (const lds_t*)vt;
+  const float c = 0.1f + (t & 7) * 1e-3f;
+  const float mc = 0.25f;
+  f32x16_t s0[2] = {}, s1[2] = {}, o[4] = {};
+  float l = 0.f;
+  const f32x16_t zero16 = {};
+
+  auto tile = [&](f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
+    __asm__ volatile("" ::: "memory");   // operands are read from LDS every tile
+    bf16x8_t pk[4];
+    float ls = 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if constexpr (VEC) {
+        const int kb = g >> 1, sub = g & 1;
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * sub + e], c, -mc));
+          ls += p[e];
+        }
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f32x2_t v = {p[2 * e], p[2 * e + 1]};
+          w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+        }
+        pk[g] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+      } else {
+        pk[g] = pfix[g];
+      }
+      bf16x8_t ka[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        ka[x] = *reinterpret_cast<const bf16x8_t __attribute__((address_space(3)))*>(
+            kl + (x & 1) * 32 * ROWB + k_off[2 * g + (x >> 1)]);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int ks = 2 * g + (x >> 1), kb = x & 1;
+        sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[x], qr[ks],
+                                                         (VEC && ks == 0) ? zero16 : sn[kb], 0,
+                                                         0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8_t va[4];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (i16x4_t __attribute__((address_space(3)))*)(vl + ks * 16 * ROWB + va_off[db]));
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (i16x4_t __attribute__((address_space(3)))*)(vl + ks * 16 * ROWB + vb_off[db]));
+        const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+        va[db] = __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y));
+      }
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], pk[ks], o[db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l += ls;
+  };
+
+  const int64_t t0 = clock64();
+  const int64_t r0 = wall_clock64();
+  for (int it = 0; it < iters; ++it) {
+    tile(s0, s1);
+    tile(s1, s0);
+  }
+  const int64_t t1 = clock64();
+  const int64_t r1 = wall_clock64();
+  float s = l;
+  for (int i = 0; i < 16; ++i) {
+    s += s0[0][i] + s0[1][i] + s1[0][i] + s1[1][i];
+    for (int db = 0; db < 4; ++db) s += o[db][i];
+  }
+  const uint32_t h = __builtin_bit_cast(uint32_t, s);
+  if (h == never) sink[0] = h;
+  if (blockIdx.x == 0 && t == 0) {
+    clocks[0] = t1 - t0;
+    clocks[1] = r1 - r0;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_read_probe(const void* buf, size_t bytes, const int32_t* order,
@@ -165,6 +298,18 @@ hipError_t launch_mfma_probe(const void* ops, int32_t iters, int32_t vec, int gr
                        (const uint4*)ops, iters, never, sink, clocks);
   else
     hipLaunchKernelGGL(mfma_loop_kernel<false>, dim3(grid), dim3(512), 0, stream,
+                       (const uint4*)ops, iters, never, sink, clocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_loop_probe(const void* ops, int32_t iters, int32_t vec, int grid,
+                                     uint32_t never, uint32_t* sink, int64_t* clocks,
+                                     hipStream_t stream) {
+  if (vec)
+    hipLaunchKernelGGL(prefill_loop_kernel<true>, dim3(grid), dim3(512), 0, stream,
+                       (const uint4*)ops, iters, never, sink, clocks);
+  else
+    hipLaunchKernelGGL(prefill_loop_kernel<false>, dim3(grid), dim3(512), 0, stream,
                        (const uint4*)ops, iters, never, sink, clocks);
   return hipGetLastError();
 }

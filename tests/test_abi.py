@@ -420,3 +420,18 @@ def test_decode_append_args(L):
     assert _decode_append(L, d, max_len=128, split=32) == -3
     assert _decode_append(L, d, partials=True) == -3
 
+
+
+@pytest.mark.parametrize("name", ["pkv_probe_mfma", "pkv_probe_prefill_loop"])
+def test_matrix_probe_args(L, name):
+    """The measurement probes reject bad arguments before any HIP call."""
+    f = getattr(L, name)
+    assert f(None, 10, 0, 1, FAKE, FAKE, None) == -1                     # operands
+    assert f(FAKE, 10, 0, 1, None, FAKE, None) == -1                     # sink
+    assert f(FAKE, 10, 0, 1, FAKE, None, None) == -1                     # clocks
+    assert f(C.c_void_p((1 << 20) + 4), 10, 0, 1, FAKE, FAKE, None) == -1
+    assert "aligned" in err(L)
+    assert f(FAKE, 0, 0, 1, FAKE, FAKE, None) == -1                      # iters
+    assert f(FAKE, 10, 0, 0, FAKE, FAKE, None) == -1                     # grid
+    assert f(FAKE, 10, 2, 1, FAKE, FAKE, None) == -1                     # vector_work
+    assert "vector_work" in err(L)
