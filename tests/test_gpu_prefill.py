@@ -137,3 +137,56 @@ def test_prefill_bad_page_poisons_its_rows_only():
     out, _ = gpu_prefill(w, d)
     assert torch.isfinite(out[:40].float()).all()
     assert torch.isnan(out[40:].float()).all()
+
+
+def _run_all_rows_written(w):
+    """Append, then prefill into NaN-filled outputs; every row must be written."""
+    d = to_dev(w, DEV)
+    pkv.kv_append(d["k_cache"], d["v_cache"], d["k_new"], d["v_new"], d["slots"])
+    out = torch.full_like(d["q"], float("nan"))
+    lse = torch.full((d["q"].shape[0], w.num_q_heads), float("nan"), device=DEV)
+    pkv.paged_attn_prefill_chunk(d["q"], d["k_cache"], d["v_cache"], d["q_indptr"],
+                                 d["block_table"], d["context_lens"], max(w.meta["chunk_lens"]),
+                                 w.max_context_len, w.scale, out=out, lse_out=lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    return out, lse
+
+
+def _check_rows(w, out, lse, rows, what):
+    ref, ref_lse = oracle_prefill(w, rows)
+    idx = torch.tensor(rows, dtype=torch.long, device=DEV)
+    assert_close(out.reshape(-1, w.head_dim)[idx], ref, w.dtype, what)
+    assert_lse_close(lse.reshape(-1)[idx], ref_lse, w.dtype, what)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64)])
+def test_prefill_long_chunks_longest_first(dtype, d):
+    """Chunks of 1024 or more positions at G = 16 (64 or more row tiles per
+    (sequence, KV head)): every workgroup ranks the sequences by key count --
+    here 1024, 4030, 1600, 4030 (a tie, broken by index) and 1500 -- and the
+    tiles go out heaviest first.  Every row is written; every position of
+    query heads 0 and 15 is checked against the oracle."""
+    hist = [0, 3000, 500, 2994, 37]
+    chunk = [1024, 1030, 1100, 1036, 1463]
+    w = W.make_prefill("longest", seed=31, batch=5, hq=16, hkv=1, d=d, dtype=dtype, hist=hist,
+                       chunk=chunk, pool_slack=0.1)
+    print(f"[prefill parity] longest-first order, {dtype} D{d}", flush=True)
+    out, lse = _run_all_rows_written(w)
+    rows = [t * 16 + h for t in range(sum(chunk)) for h in (0, 15)]
+    _check_rows(w, out, lse, rows, f"longest first {dtype} D{d}")
+
+
+def test_prefill_long_chunks_large_batch_index_order():
+    """257 sequences of 1024-position chunks at G = 16: one more sequence than
+    the workgroups rank, so the tiles keep the batch's index order.  Every row
+    is written; all positions of query heads 0 and 15 of sequences 0, 128 and
+    256 are checked against the oracle."""
+    batch = 257
+    hist = [(b * 37) % 300 for b in range(batch)]
+    w = W.make_prefill("wide", seed=32, batch=batch, hq=16, hkv=1, d=64, dtype="bf16",
+                       hist=hist, chunk=[1024] * batch)
+    print("[prefill parity] 257 long chunks, index order", flush=True)
+    out, lse = _run_all_rows_written(w)
+    rows = [(b * 1024 + i) * 16 + h for b in (0, 128, 256) for i in range(1024) for h in (0, 15)]
+    _check_rows(w, out, lse, rows, "257 long chunks")
